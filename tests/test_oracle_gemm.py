@@ -1,0 +1,185 @@
+"""Pins of the oracle's scaled-GEMM results: exact rational arithmetic on tiny
+shapes (Python fractions over decoded codes), permutation identities, the
+block/tensor-mode equivalence, the FP32-accumulation error bound and the
+a-priori bound against the unquantised fp64 GEMM."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from fp8_mixed_precision_linear_amd import datagen
+
+FMAX = {0: 448.0, 1: 57344.0}
+
+
+def rand_codes(rng, shape, fmt):
+    """Random finite FP8 codes (no NaN/Inf)."""
+    c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    mag = c & 0x7F
+    if fmt == 0:
+        c[mag == 0x7F] &= 0xFE
+    else:
+        c[mag >= 0x7C] = (c[mag >= 0x7C] & 0x80) | 0x7B
+    return c
+
+
+def frac_decode(code, fmt):
+    """Exact value of an FP8 code as a Fraction, from its fields."""
+    s = code >> 7
+    eb, mb, bias = (4, 3, 7) if fmt == 0 else (5, 2, 15)
+    e = (code >> mb) & ((1 << eb) - 1)
+    m = code & ((1 << mb) - 1)
+    if e == 0:
+        v = Fraction(m, 1 << mb) * Fraction(2) ** (1 - bias)
+    else:
+        v = (1 + Fraction(m, 1 << mb)) * Fraction(2) ** (e - bias)
+    return -v if s else v
+
+
+def scale_of(s, scaling, rows, row, kb):
+    if scaling == 0:
+        return s.reshape(-1)[0]
+    if scaling == 1:
+        return s[kb, row]
+    return s[kb, row // 128]
+
+
+def exact_gemm(A, af, asc, sa, B, bf, bsc, sb):
+    M, K = A.shape
+    N = B.shape[0]
+    out = np.empty((M, N), dtype=object)
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for k in range(K):
+                kb = k // 128
+                tot += (frac_decode(int(A[m, k]), af) * Fraction(float(scale_of(sa, asc, M, m, kb)))
+                        * frac_decode(int(B[n, k]), bf) * Fraction(float(scale_of(sb, bsc, N, n, kb))))
+            out[m, n] = tot
+    return out
+
+
+def scales_for(rng, scaling, rows, K):
+    nkb = (K + 127) // 128
+    if scaling == 0:
+        return np.array([rng.uniform(0.01, 3.0)], np.float32)
+    if scaling == 1:
+        return rng.uniform(0.001, 2.0, (nkb, rows)).astype(np.float32)
+    return rng.uniform(0.001, 2.0, (nkb, (rows + 127) // 128)).astype(np.float32)
+
+
+@pytest.mark.parametrize("af,bf", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("asc,bsc", [(0, 0), (1, 2), (1, 1)])
+def test_exact_matches_fractions(O, af, bf, asc, bsc):
+    rng = np.random.default_rng(100 + 10 * af + bf + 3 * asc + bsc)
+    M, N, K = 3, 4, 384
+    A = rand_codes(rng, (M, K), af)
+    B = rand_codes(rng, (N, K), bf)
+    sa = scales_for(rng, asc, M, K)
+    sb = scales_for(rng, bsc, N, K)
+    got = O.gemm(A, af, asc, sa, B, bf, bsc, sb)
+    ref = exact_gemm(A, af, asc, sa, B, bf, bsc, sb)
+    for m in range(M):
+        for n in range(N):
+            r = float(ref[m, n])
+            assert abs(got["E"][m, n] - r) <= 2.0 ** -52 * abs(r) + 1e-300
+            D = sum(abs(frac_decode(int(A[m, k]), af) * frac_decode(int(B[n, k]), bf))
+                    * Fraction(float(scale_of(sa, asc, M, m, k // 128)))
+                    * Fraction(float(scale_of(sb, bsc, N, n, k // 128))) for k in range(K))
+            assert abs(got["D"][m, n] - float(D)) <= 1e-12 * float(D)
+
+
+def test_permutation_identity_exact(O):
+    rng = np.random.default_rng(9)
+    M, K = 16, 256
+    A = rand_codes(rng, (M, K), 0)
+    perm = rng.permutation(K)
+    B = np.zeros((K, K), np.uint8)          # B[n][k] = 1.0 where k = perm[n]
+    B[np.arange(K), perm] = 0x38            # 0x38 = 1.0 in E4M3
+    one = np.array([1.0], np.float32)
+    got = O.gemm(A, 0, 0, one, B, 0, 0, one)
+    want = O.decode(A[:, perm], 0)
+    assert np.array_equal(got["E"], want)
+    assert np.array_equal(got["F"].astype(np.float64), want)
+
+
+def test_block_with_equal_scales_equals_tensor(O):
+    rng = np.random.default_rng(12)
+    M, N, K = 40, 50, 512
+    A = rand_codes(rng, (M, K), 0)
+    B = rand_codes(rng, (N, K), 1)
+    sa, sb = np.float32(0.125), np.float32(0.5)   # powers of two: products exact
+    t = O.gemm(A, 0, 0, np.array([sa]), B, 1, 0, np.array([sb]))
+    b = O.gemm(A, 0, 1, np.full((4, M), sa, np.float32), B, 1, 2, np.full((4, 1), sb, np.float32))
+    assert np.array_equal(t["E"], b["E"])
+    assert np.array_equal(t["F"], b["F"])
+
+
+@pytest.mark.parametrize("asc,bsc", [(0, 0), (1, 2), (1, 1)])
+def test_f32_accumulation_within_bound(O, asc, bsc):
+    rng = np.random.default_rng(21)
+    M, N, K = 24, 40, 2048
+    A = rand_codes(rng, (M, K), 0)
+    B = rand_codes(rng, (N, K), 1)
+    sa = scales_for(rng, asc, M, K)
+    sb = scales_for(rng, bsc, N, K)
+    g = O.gemm(A, 0, asc, sa, B, 1, bsc, sb)
+    nkb = K // 128
+    gam = (nkb + 3) * 2.0 ** -24 / (1 - (nkb + 3) * 2.0 ** -24)
+    err = np.abs(g["F"].astype(np.float64) - g["E"])
+    assert np.all(err <= gam * g["D"])
+    assert np.any(err > 0)  # the FP32 partner is not the exact result
+
+
+def _quantise_operands(O, a16, b16, mode, af, bf):
+    """Quantise bf16 operands a [M][K], b [N][K] the way the layer does."""
+    if mode == "tensor":
+        sa, sai, _ = O.compute_scale(O.amax(a16), af)
+        sb, sbi, _ = O.compute_scale(O.amax(b16), bf)
+        return (O.cast(a16, sa, af), 0, np.array([sai], np.float32),
+                O.cast(b16, sb, bf), 0, np.array([sbi], np.float32))
+    if mode == "delayed":  # stale scales: the tensors overflow the range
+        sa, sai, _ = O.compute_scale(O.amax(a16) / 4, af)
+        sb, sbi, _ = O.compute_scale(O.amax(b16) / 2, bf)
+        return (O.cast(a16, sa, af), 0, np.array([sai], np.float32),
+                O.cast(b16, sb, bf), 0, np.array([sbi], np.float32))
+    ga = O.cast_block(a16, af, O.S1x128)
+    gb = O.cast_block(b16, bf, O.S128x128 if mode == "block" else O.S1x128)
+    return (ga["y"], 1, ga["sinv"], gb["y"], 2 if mode == "block" else 1, gb["sinv"])
+
+
+@pytest.mark.parametrize("mode", ["tensor", "delayed", "block", "block_rowcol"])
+def test_reference_bound_holds(O, mode):
+    rng = np.random.default_rng(31)
+    M, N, K = 96, 130, 640
+    a16 = datagen.student_t3(rng, (M, K), 1.0)
+    b16 = datagen.normal(rng, (N, K), 0.02)
+    A, asc, sa, B, bsc, sb = _quantise_operands(O, a16, b16, mode, 0, 1)
+    g = O.gemm(A, 0, asc, sa, B, 1, bsc, sb)
+    R, Bd = O.gemm_ref_bound(A, 0, asc, sa, B, 1, bsc, sb, a16, b16)
+    assert np.all(np.abs(g["E"] - R) <= Bd)
+    assert np.all(np.abs(g["F"] - R) <= Bd)
+    # the bound is first order in the unit roundoffs: a fraction of sum|a b|
+    # (E4M3 x E5M2: u_a + u_b = 3/16), not a multiple of it
+    # (saturation under stale delayed scales adds its own, larger term)
+    if mode != "delayed":
+        assert np.max(Bd / g["D"]) < 0.25
+
+
+def test_reference_bound_catches_a_wrong_operand(O):
+    """A transposed/shifted operand must violate the bound somewhere."""
+    rng = np.random.default_rng(33)
+    M, N, K = 32, 32, 256
+    a16 = datagen.normal(rng, (M, K), 1.0)
+    b16 = datagen.normal(rng, (N, K), 1.0)
+    A, asc, sa, B, bsc, sb = _quantise_operands(O, a16, b16, "tensor", 0, 0)
+    bad = O.gemm(A, 0, asc, sa, np.roll(B, 1, axis=1), 0, bsc, sb)
+    R, Bd = O.gemm_ref_bound(A, 0, asc, sa, B, 0, bsc, sb, a16, b16)
+    assert np.any(np.abs(bad["E"] - R) > Bd)
+
+
+def test_bf16_output_rounding(O):
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20, -2.5, np.inf], np.float32)
+    bits = O.f32_to_bf16(x)
+    assert list(bits) == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020, 0x7F80]
+    assert np.array_equal(bits, datagen.bf16_bits(x))

@@ -1,0 +1,256 @@
+"""Pins of the oracle's amax, scale, history and cast functions: closed forms,
+invariants, hand-computed sequences and an independent library conversion
+(torch's float8 dtypes after an explicit clip)."""
+import numpy as np
+import pytest
+import torch
+
+from fp8_mixed_precision_linear_amd import datagen
+
+TORCH_DT = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2}
+FMAX = {0: 448.0, 1: 57344.0}
+
+
+def lib_cast(x_bf16, s, fmt):
+    """Library route: binary32 multiply, clip to +-max (saturation), torch RNE."""
+    with np.errstate(over="ignore", invalid="ignore"):
+        v = datagen.bf16_to_f32(x_bf16) * np.float32(s)
+    v = np.clip(v, -FMAX[fmt], FMAX[fmt]).astype(np.float32)
+    return torch.from_numpy(np.ascontiguousarray(v)).to(TORCH_DT[fmt]).view(torch.uint8).numpy()
+
+
+# ------------------------------------------------------------------ amax ---
+def test_amax_matches_numpy_and_invariants(O):
+    rng = np.random.default_rng(3)
+    x = datagen.normal(rng, (257, 333), 2.0)
+    ref = np.max(np.abs(datagen.bf16_to_f32(x)))
+    assert O.amax(x) == ref
+    perm = rng.permutation(x.size)
+    assert O.amax(x.reshape(-1)[perm]) == ref
+    chunks = np.array_split(x.reshape(-1), 7)
+    assert max(O.amax(c) for c in chunks) == ref
+    assert O.amax_parallel(x) == ref
+
+
+def test_amax_special_cases(O):
+    z = np.zeros((64, 64), np.uint16)
+    assert O.amax(z) == 0.0
+    z[5, 7] = datagen.bf16_bits(np.array([-37.5], np.float32))[0]
+    assert O.amax(z) == np.float32(37.5)
+    z[1, 1] = 0xFF80  # -inf
+    assert np.isinf(O.amax(z))
+    z[2, 2] = 0x7FC1  # NaN
+    assert np.isnan(O.amax(z))
+    assert O.amax(np.zeros(0, np.uint16)) == 0.0
+
+
+# ----------------------------------------------------------------- scale ---
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_scale_closed_forms(O, fmt):
+    fmax = FMAX[fmt]
+    s, si, ok = O.compute_scale(fmax, fmt)
+    assert ok and s == 1.0 and si == 1.0
+    for k in range(-20, 21):
+        s, si, ok = O.compute_scale(2.0 ** k, fmt)
+        assert s == np.float32(fmax * 2.0 ** -k)
+        s, si, ok = O.compute_scale(fmax * 2.0 ** k, fmt)
+        assert s == np.float32(2.0 ** -k) and si == np.float32(2.0 ** k)
+    s, si, ok = O.compute_scale(fmax, fmt, margin=2)
+    assert s == 0.25 and si == 4.0
+
+
+def test_scale_matches_ieee_division(O):
+    rng = np.random.default_rng(11)
+    a = np.exp2(rng.uniform(-30, 30, 20000)).astype(np.float32)
+    for fmt in (0, 1):
+        for v in a[:2000]:
+            s, si, ok = O.compute_scale(v, fmt)
+            assert s == np.float32(FMAX[fmt]) / v
+            assert si == np.float32(1.0) / s
+
+
+def test_scale_edge_rules(O):
+    for bad in [0.0, np.inf, np.nan]:
+        s, si, ok = O.compute_scale(bad, 0, fallback=3.0)
+        assert not ok and s == 3.0 and si == np.float32(1.0) / np.float32(3.0)
+    tiny = np.float32(1e-40)  # 448 / tiny overflows binary32
+    s, si, ok = O.compute_scale(tiny, 0)
+    assert ok and s == np.finfo(np.float32).max and si > 0
+
+
+# --------------------------------------------------------------- history ---
+def _run_history(O, amaxes, algo=0, fmt=0, ln=16):
+    h = np.zeros((1, ln), np.float32)
+    s = np.ones(1, np.float32)
+    si = np.ones(1, np.float32)
+    out = []
+    for a in amaxes:
+        O.history_update(h, np.array([a], np.float32), fmt, 0, algo, s, si)
+        out.append((h.copy(), s[0], si[0]))
+    return out
+
+
+def test_history_increasing_sequence(O):
+    seq = [float(t + 1) for t in range(20)]
+    res = _run_history(O, seq)
+    for t, (h, s, si) in enumerate(res):
+        want = [float(t + 1 - j) if t - j >= 0 else 0.0 for j in range(16)]
+        assert list(h[0]) == want
+        assert s == np.float32(448.0) / np.float32(t + 1)
+
+
+def test_history_window_drops_after_16(O):
+    seq = [100.0 - t for t in range(40)]
+    res = _run_history(O, seq)
+    for t, (h, s, si) in enumerate(res):
+        eff = 100.0 - max(0, t - 15)
+        assert s == np.float32(448.0) / np.float32(eff)
+
+
+def test_history_spike_persists_exactly_16(O):
+    seq = [1.0] * 40
+    seq[3] = 10.0
+    res = _run_history(O, seq)
+    for t, (h, s, si) in enumerate(res):
+        want = 448.0 / 10.0 if 3 <= t <= 18 else 448.0
+        assert s == np.float32(want), t
+
+
+def test_history_constant_and_zero(O):
+    res = _run_history(O, [0.0, 0.0, 2.0, 2.0, 2.0])
+    assert res[0][1] == 1.0 and res[1][1] == 1.0   # all-zero: keep the previous scale
+    assert all(r[1] == np.float32(224.0) for r in res[2:])
+    res = _run_history(O, [4.0, np.nan, 4.0])
+    assert res[0][1] == 112.0 and res[1][1] == 112.0 and res[2][1] == 112.0  # NaN in window
+
+
+def test_history_most_recent_and_len32(O):
+    res = _run_history(O, [8.0, 2.0, 4.0], algo=1)
+    assert [r[1] for r in res] == [56.0, 224.0, 112.0]
+    seq = [1.0] * 40
+    seq[0] = 7.0
+    res = _run_history(O, seq, ln=32)
+    assert res[31][1] == np.float32(64.0) and res[32][1] == 448.0
+
+
+def test_history_checkpoint_restore_bitexact(O):
+    """Failure pattern 7 (checkpoint-restore divergence): state copied mid-run
+    continues bit-exactly."""
+    rng = np.random.default_rng(5)
+    am = np.abs(rng.standard_normal((16, 3))).astype(np.float32) * 10
+    h = np.zeros((3, 16), np.float32); s = np.ones(3, np.float32); si = np.ones(3, np.float32)
+    fmts = [0, 0, 1]
+    def step(h, s, si, a):
+        for i, f in enumerate(fmts):
+            hh, ss, sii = h[i:i + 1].copy(), s[i:i + 1].copy(), si[i:i + 1].copy()
+            O.history_update(hh, a[i:i + 1], f, 0, 0, ss, sii)
+            h[i], s[i], si[i] = hh[0], ss[0], sii[0]
+    for t in range(8):
+        step(h, s, si, am[t])
+    ck = (h.copy(), s.copy(), si.copy())
+    for t in range(8, 16):
+        step(h, s, si, am[t])
+    h2, s2, si2 = ck
+    for t in range(8, 16):
+        step(h2, s2, si2, am[t])
+    assert np.array_equal(h.view(np.uint32), h2.view(np.uint32))
+    assert np.array_equal(s.view(np.uint32), s2.view(np.uint32))
+
+
+# ------------------------------------------------------------------ cast ---
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_cast_all_bf16_patterns_vs_library(O, fmt):
+    x = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    xf = datagen.bf16_to_f32(x)
+    keep = ~np.isnan(xf)
+    rng = np.random.default_rng(1)
+    scales = [1.0] + [2.0 ** k for k in range(-20, 21, 3)]
+    scales += list(np.float32(FMAX[fmt]) / np.exp2(rng.uniform(-10, 10, 12)).astype(np.float32))
+    scales += [np.float32(1.0 + 2.0 ** -23), np.float32(3.0), np.float32(0.7)]
+    for s in scales:
+        ours = O.cast(x, s, fmt)
+        assert np.array_equal(ours[keep], lib_cast(x[keep], s, fmt)), s
+        assert np.all((ours[~keep] & 0x7F) == 0x7F)
+
+
+def test_cast_transpose_is_transpose(O):
+    rng = np.random.default_rng(2)
+    x = datagen.normal(rng, (67, 131), 3.0)
+    y, yt = O.cast_transpose_plain(x, 17.0, 0)
+    assert np.array_equal(yt, y.T)
+    y2, yt2 = O.cast_transpose(x, 17.0, 0)
+    assert np.array_equal(y2, y) and np.array_equal(yt2, yt)
+
+
+# ------------------------------------------------------------ block cast ---
+def _tile_amax_rows(xf, rows, cols):
+    ncb = (cols + 127) // 128
+    am = np.zeros((ncb, rows), np.float32)
+    for cb in range(ncb):
+        am[cb] = np.max(np.abs(xf[:, cb * 128:(cb + 1) * 128]), axis=1)
+    return am
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("shape", [(256, 384), (200, 300), (1, 130), (129, 1)])
+def test_block_1x128_vs_library(O, fmt, shape):
+    rng = np.random.default_rng(4)
+    x = datagen.student_t3(rng, shape, 1.0)
+    rows, cols = shape
+    xf = datagen.bf16_to_f32(x)
+    got = O.cast_block(x, fmt, O.S1x128, want_y=True, want_t=True)
+    plain = O.cast_block(x, fmt, O.S1x128, want_y=True, want_t=True, plain=True)
+    for k in ("y", "sinv", "y_t", "sinv_t"):
+        assert np.array_equal(got[k], plain[k])
+    am = _tile_amax_rows(xf, rows, cols)
+    s = np.float32(FMAX[fmt]) / am
+    assert np.array_equal(got["sinv"], np.float32(1.0) / s)
+    for cb in range(am.shape[0]):
+        sl = slice(cb * 128, (cb + 1) * 128)
+        for r in range(rows):
+            assert np.array_equal(got["y"][r, sl], lib_cast(x[r, sl], s[cb, r], fmt))
+    # transposed copy: tiles along the row (token) axis, from bf16
+    amt = _tile_amax_rows(xf.T.copy(), cols, rows)
+    st = np.float32(FMAX[fmt]) / amt
+    assert np.array_equal(got["sinv_t"], np.float32(1.0) / st)
+    xt = np.ascontiguousarray(x.T)
+    for rb in range(amt.shape[0]):
+        sl = slice(rb * 128, (rb + 1) * 128)
+        for c in range(cols):
+            assert np.array_equal(got["y_t"][c, sl], lib_cast(xt[c, sl], st[rb, c], fmt))
+
+
+@pytest.mark.parametrize("shape", [(256, 384), (300, 200)])
+def test_block_128x128_vs_library(O, shape):
+    rng = np.random.default_rng(6)
+    x = datagen.normal(rng, shape, 0.02)
+    rows, cols = shape
+    xf = datagen.bf16_to_f32(x)
+    got = O.cast_block(x, 0, O.S128x128, want_y=True, want_t=True)
+    assert np.array_equal(got["y_t"], got["y"].T)
+    assert np.array_equal(got["sinv_t"], got["sinv"].T)
+    for rb in range((rows + 127) // 128):
+        for cb in range((cols + 127) // 128):
+            blk = (slice(rb * 128, (rb + 1) * 128), slice(cb * 128, (cb + 1) * 128))
+            s = np.float32(448.0) / np.max(np.abs(xf[blk]))
+            assert got["sinv"][cb, rb] == np.float32(1.0) / s
+            assert np.array_equal(got["y"][blk], lib_cast(x[blk], s, 0))
+
+
+def test_block_constant_and_zero_tiles(O):
+    x = np.full((128, 256), datagen.bf16_bits(np.array([-3.0], np.float32))[0], np.uint16)
+    x[:, 128:] = 0
+    got = O.cast_block(x, 0, O.S1x128, want_y=True, want_t=True)
+    assert np.all(got["y"][:, :128] == 0xFE) and np.all(got["y"][:, 128:] == 0)
+    assert np.all(got["sinv"][0] == np.float32(1.0) / (np.float32(448.0) / np.float32(3.0)))
+    assert np.all(got["sinv"][1] == 1.0)   # all-zero tile: scale 1
+    g2 = O.cast_block(x, 1, O.S128x128)
+    assert np.all(g2["y"][:, :128] == 0xFB) and g2["sinv"][1, 0] == 1.0
+    # a tile copied to every tile gives identical bytes and scales
+    rng = np.random.default_rng(8)
+    t = datagen.normal(rng, (1, 128), 1.0)
+    xx = np.tile(t, (4, 3))
+    g3 = O.cast_block(xx, 0, O.S1x128)
+    assert np.all(g3["sinv"] == g3["sinv"][0, 0])
+    assert all(np.array_equal(g3["y"][r, cb * 128:(cb + 1) * 128], g3["y"][0, :128])
+               for r in range(4) for cb in range(3))
