@@ -1,0 +1,239 @@
+// cast_kernels.hip -- per-tensor saturating RNE cast to FP8 on gfx950, with
+// optional fused transpose (LDS-staged) and fused amax of the input.
+//
+// [MPG] = "Mixed Precision LLM Training: The Complete Guide",
+//   "Transformer Engine internals > Per-tensor scaling": multiply by the
+//   tensor's scale, then quantise.
+// [TALK] = PyData Amsterdam 2026 "FP8 for pretraining", outline 05:00-15:00:
+//   E4M3 for forward activations and weights, E5M2 for gradients.
+//
+// Memory-bound kernels: every byte is read or written once, with 16-byte
+// accesses.  The transposed copy goes through LDS as dwords that each hold
+// 4 codes of one column (a 4x4 byte transpose in registers), with a 16-byte
+// XOR swizzle so that the writes and the 16-byte reads are conflict free.
+#include "fp8_device.h"
+#include "launch.h"
+
+namespace fp8lin {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ void block_amax_to(float* out, uint32_t v) {
+  __shared__ uint32_t part[kThreads / 64];
+  v = wave_max_u32(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t w = part[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) w = w > part[i] ? w : part[i];
+    if (w != 0u) atomic_max_bits(out, w);
+  }
+}
+
+// ---------------------------------------------------------------------
+// Flat cast (no transpose): 16 elements per thread per step (two 16-byte
+// loads, one 16-byte store).  Any n; the last n % 16 values are handled by
+// the first threads of block 0.
+// ---------------------------------------------------------------------
+template <int FMT, bool AMAX>
+__global__ void __launch_bounds__(kThreads)
+    k_cast_flat(const uint16_t* __restrict__ x, int64_t n, const float* __restrict__ scale,
+                uint8_t* __restrict__ y, float* __restrict__ amax) {
+  const float s = *scale;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint4* yv = reinterpret_cast<uint4*>(y);
+  const int64_t nu = n >> 4;  // units of 16 elements
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint32_t m = 0;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nu; u += stride) {
+    uint4 a = ld_nt16(xv + 2 * u);
+    uint4 b = ld_nt16(xv + 2 * u + 1);
+    if (AMAX) {
+      m = absmax_pk(m, a.x); m = absmax_pk(m, a.y); m = absmax_pk(m, a.z); m = absmax_pk(m, a.w);
+      m = absmax_pk(m, b.x); m = absmax_pk(m, b.y); m = absmax_pk(m, b.z); m = absmax_pk(m, b.w);
+    }
+    uint2 qa = cvt8_bf16<FMT>(a, s);
+    uint2 qb = cvt8_bf16<FMT>(b, s);
+    st_nt16(make_uint4(qa.x, qa.y, qb.x, qb.y), yv + u);
+  }
+  uint32_t mb = AMAX ? absmax_fold(m) : 0u;
+  if (blockIdx.x == 0 && threadIdx.x < (n & 15)) {
+    int64_t i = (nu << 4) + threadIdx.x;
+    uint16_t h = x[i];
+    float v = __uint_as_float((uint32_t)h << 16) * s;
+    y[i] = (uint8_t)(cvt4<FMT>(v, 0.f, 0.f, 0.f) & 0xFFu);
+    if (AMAX) {
+      uint32_t t = (uint32_t)(h & 0x7FFFu) << 16;
+      mb = mb > t ? mb : t;
+    }
+  }
+  if (AMAX) block_amax_to(amax, mb);
+}
+
+// ---------------------------------------------------------------------
+// Cast + transpose, tile 128 x 128, 256 threads.  Requires rows % 16 == 0
+// and cols % 16 == 0 (16-byte rows in both orientations); tiles at the
+// right / bottom edge may be partial in steps of 16.
+// Thread t owns rows 4*(t/8) .. +3 and columns 16*(t%8) .. +15 of the tile.
+// LDS holds the transposed tile: line c (a column of x, 128 bytes = 8
+// chunks of 16 rows); chunk ch of line c sits at physical chunk
+// ch ^ ((c/16) & 7).
+// ---------------------------------------------------------------------
+__device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                             uint32_t& t0, uint32_t& t1, uint32_t& t2,
+                                             uint32_t& t3) {
+  // wK holds bytes [r=K][c=0..3]; tJ gets bytes [r=0..3][c=J].
+  // __builtin_amdgcn_perm(hi, lo, sel): selector bytes 0-3 pick lo, 4-7 hi.
+  uint32_t a01_lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // r0c0 r1c0 r0c1 r1c1
+  uint32_t a01_hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // r0c2 r1c2 r0c3 r1c3
+  uint32_t a23_lo = __builtin_amdgcn_perm(w3, w2, 0x05010400u);  // r2c0 r3c0 r2c1 r3c1
+  uint32_t a23_hi = __builtin_amdgcn_perm(w3, w2, 0x07030602u);  // r2c2 r3c2 r2c3 r3c3
+  t0 = __builtin_amdgcn_perm(a23_lo, a01_lo, 0x05040100u);       // r0c0 r1c0 r2c0 r3c0
+  t1 = __builtin_amdgcn_perm(a23_lo, a01_lo, 0x07060302u);       // c1
+  t2 = __builtin_amdgcn_perm(a23_hi, a01_hi, 0x05040100u);       // c2
+  t3 = __builtin_amdgcn_perm(a23_hi, a01_hi, 0x07060302u);       // c3
+}
+
+template <int FMT, bool AMAX, bool WANT_Y>
+__global__ void __launch_bounds__(kThreads)
+    k_cast_transpose(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                     const float* __restrict__ scale, uint8_t* __restrict__ y,
+                     uint8_t* __restrict__ yt, float* __restrict__ amax) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[128 * 128];
+  const float s = *scale;
+  const int t = threadIdx.x;
+  const int cg = t & 7, rg = t >> 3;
+  const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
+  const int64_t cbase = c0 + 16 * cg;
+  const bool col_ok = cbase < cols;  // cols % 16 == 0: whole 16-col group in or out
+  uint32_t w[4][4];                  // [row i][dword j]: codes of cols 4j..4j+3
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + 4 * rg + i;
+    uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+    if (col_ok && r < rows) {
+      const uint4* p = reinterpret_cast<const uint4*>(x + r * cols + cbase);
+      a = ld_nt16(p);
+      b = ld_nt16(p + 1);
+    }
+    if (AMAX) {
+      m = absmax_pk(m, a.x); m = absmax_pk(m, a.y); m = absmax_pk(m, a.z); m = absmax_pk(m, a.w);
+      m = absmax_pk(m, b.x); m = absmax_pk(m, b.y); m = absmax_pk(m, b.z); m = absmax_pk(m, b.w);
+    }
+    uint2 qa = cvt8_bf16<FMT>(a, s);
+    uint2 qb = cvt8_bf16<FMT>(b, s);
+    w[i][0] = qa.x; w[i][1] = qa.y; w[i][2] = qb.x; w[i][3] = qb.y;
+    if (WANT_Y && col_ok && r < rows)
+      st_nt16(make_uint4(qa.x, qa.y, qb.x, qb.y),
+                                  reinterpret_cast<uint4*>(y + r * cols + cbase));
+  }
+  // transposed dwords into LDS: column c = 16*cg + 4*j + k, rows 4*rg..+3
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t t0, t1, t2, t3;
+    transpose4x4(w[0][j], w[1][j], w[2][j], w[3][j], t0, t1, t2, t3);
+    const uint32_t tv[4] = {t0, t1, t2, t3};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = 16 * cg + 4 * j + k;
+      const int ch = rg >> 2, within = rg & 3;
+      const int phys = ch ^ ((c >> 4) & 7);
+      *reinterpret_cast<uint32_t*>(lds + c * 128 + phys * 16 + within * 4) = tv[k];
+    }
+  }
+  __syncthreads();
+  // y_t rows: tile column c -> y_t row c0 + c, 16 bytes = rows 16*ch..+15
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = it * kThreads + t;  // 0..1023
+    const int c = idx >> 3, ch = idx & 7;
+    const int phys = ch ^ ((c >> 4) & 7);
+    const int64_t gc = c0 + c, gr = r0 + 16 * ch;
+    if (gc < cols && gr < rows) {
+      uint4 v = *reinterpret_cast<const uint4*>(lds + c * 128 + phys * 16);
+      st_nt16(v, (yt + gc * rows + gr));
+    }
+  }
+  if (AMAX) block_amax_to(amax, absmax_fold(m));
+}
+
+// ---------------------------------------------------------------------
+// Generic cast for shapes the tiled kernels do not take (rows or cols not
+// multiples of 16): one element per thread, same arithmetic.
+// ---------------------------------------------------------------------
+template <int FMT, bool AMAX>
+__global__ void __launch_bounds__(kThreads)
+    k_cast_generic(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                   const float* __restrict__ scale, uint8_t* __restrict__ y,
+                   uint8_t* __restrict__ yt, float* __restrict__ amax) {
+  const float s = *scale;
+  const int64_t n = rows * cols;
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint16_t h = x[i];
+    const uint8_t q = (uint8_t)(cvt4<FMT>(__uint_as_float((uint32_t)h << 16) * s, 0.f, 0.f, 0.f) &
+                                0xFFu);
+    const int64_t r = i / cols, c = i - r * cols;
+    if (y) y[i] = q;
+    if (yt) yt[c * rows + r] = q;
+    if (AMAX) {
+      uint32_t t = (uint32_t)(h & 0x7FFFu) << 16;
+      m = m > t ? m : t;
+    }
+  }
+  if (AMAX) block_amax_to(amax, m);
+}
+
+template <int FMT, bool AMAX>
+hipError_t launch_cast_t(const uint16_t* x, int64_t rows, int64_t cols, const float* scale,
+                         uint8_t* y, uint8_t* yt, float* amax, hipStream_t s) {
+  const int64_t n = rows * cols;
+  if (yt == nullptr) {
+    int64_t nu = n >> 4;
+    int64_t blocks = (nu + kThreads - 1) / kThreads;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL((k_cast_flat<FMT, AMAX>), dim3((unsigned)blocks), dim3(kThreads), 0, s, x,
+                       n, scale, y, amax);
+    return hipGetLastError();
+  }
+  if (rows % 16 == 0 && cols % 16 == 0) {
+    dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
+    if (y)
+      hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, true>), grid, dim3(kThreads), 0, s, x, rows,
+                         cols, scale, y, yt, amax);
+    else
+      hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, false>), grid, dim3(kThreads), 0, s, x, rows,
+                         cols, scale, y, yt, amax);
+    return hipGetLastError();
+  }
+  int64_t blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL((k_cast_generic<FMT, AMAX>), dim3((unsigned)blocks), dim3(kThreads), 0, s, x,
+                     rows, cols, scale, y, yt, amax);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, const float* scale, int fmt,
+                       uint8_t* y, uint8_t* y_t, float* amax, hipStream_t s) {
+  if (amax) {
+    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 1, 0u, s);
+    if (e != hipSuccess) return e;
+  }
+  if (rows == 0 || cols == 0) return hipSuccess;
+  if (fmt == 0)
+    return amax ? launch_cast_t<0, true>(x, rows, cols, scale, y, y_t, amax, s)
+                : launch_cast_t<0, false>(x, rows, cols, scale, y, y_t, amax, s);
+  return amax ? launch_cast_t<1, true>(x, rows, cols, scale, y, y_t, amax, s)
+              : launch_cast_t<1, false>(x, rows, cols, scale, y, y_t, amax, s);
+}
+
+}  // namespace fp8lin

@@ -1,0 +1,130 @@
+// fp8_device.h -- device-side helpers of the FP8 scaled linear layer (gfx950).
+//
+// FP8 codes are the OCP encodings that gfx950's conversion and matrix
+// instructions use natively: E4M3 (max 448, no Inf) and E5M2 (max 57344).
+// Sources, cited by page title and section:
+//   [MPG] "Mixed Precision LLM Training: The Complete Guide":
+//         "The precision formats", "FP8 E4M3", "FP8 E5M2",
+//         "Transformer Engine internals > Per-tensor scaling".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8lin {
+
+constexpr float kMaxE4M3 = 448.0f;
+constexpr float kMaxE5M2 = 57344.0f;
+constexpr float kFltMax = 3.402823466e+38f;
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<0> {
+  static constexpr float max = kMaxE4M3;
+};
+template <>
+struct Fmt<1> {
+  static constexpr float max = kMaxE5M2;
+};
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming (non-temporal) global load / store.
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+  u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt16(uint4 v, void* p) {
+  u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Saturation before the hardware conversion: finite values beyond the
+// format's largest magnitude and +-Inf become +-max; NaN passes through so
+// the conversion emits a NaN code.  Values between max and the rounding
+// midpoint above it round to max anyway, so clamping first and rounding
+// second equals rounding first and saturating second.
+template <int FMT>
+__device__ __forceinline__ float sat(float v) {
+  float c = __builtin_amdgcn_fmed3f(v, -Fmt<FMT>::max, Fmt<FMT>::max);
+  return __builtin_isnan(v) ? v : c;
+}
+
+// Four binary32 values -> four FP8 codes packed little-endian in a dword
+// (a in byte 0 ... d in byte 3), round to nearest even.
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  int w;
+  if constexpr (FMT == 0) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat<0>(a), sat<0>(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat<0>(c), sat<0>(d), w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(sat<1>(a), sat<1>(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(sat<1>(c), sat<1>(d), w, true);
+  }
+  return (uint32_t)w;
+}
+
+// Eight bf16 (one 16-byte load, as 4 dwords) times s -> 8 codes (2 dwords).
+template <int FMT>
+__device__ __forceinline__ uint2 cvt8_bf16(uint4 v, float s) {
+  uint2 r;
+  r.x = cvt4<FMT>(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
+  r.y = cvt4<FMT>(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
+  return r;
+}
+
+// max |x| over the bf16 halves of a dword, as a packed pair of 15-bit
+// magnitudes: clearing the sign bits leaves patterns whose unsigned order
+// is the order of |x| (NaN above Inf), so a packed u16 max is exact.
+__device__ __forceinline__ uint32_t absmax_pk(uint32_t acc, uint32_t w) {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  us2 a = __builtin_bit_cast(us2, acc);
+  us2 b = __builtin_bit_cast(us2, w & 0x7FFF7FFFu);
+  us2 m = __builtin_elementwise_max(a, b);
+  return __builtin_bit_cast(uint32_t, m);
+}
+
+// Fold a packed pair into the binary32 bit pattern of the larger |x|.
+__device__ __forceinline__ uint32_t absmax_fold(uint32_t pk) {
+  uint32_t lo = pk & 0xFFFFu, hi = pk >> 16;
+  return (lo > hi ? lo : hi) << 16;
+}
+
+// Maximum over the 64 lanes of a wavefront (unsigned).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+// Scale from an amax: s = fl32(fmax / amax) * 2^-margin, s_inv = fl32(1/s)
+// (both divisions correctly rounded); returns false (and leaves s, s_inv
+// untouched) for amax == 0 or non-finite.  A quotient that overflows
+// binary32 is clamped to FLT_MAX.  [MPG] "Per-tensor scaling"; the recipe's
+// `margin` read as a division by 2^margin.
+__device__ __forceinline__ bool scale_from_amax(float amax, float fmax, int margin, float& s,
+                                                float& s_inv) {
+  if (!(amax > 0.0f) || __builtin_isinf(amax)) return false;   // also rejects NaN
+  float q = __fdiv_rn(fmax, amax);
+  if (__builtin_isinf(q)) q = kFltMax;
+  if (margin != 0) q = __builtin_ldexpf(q, -margin);
+  s = q;
+  s_inv = __fdiv_rn(1.0f, q);
+  return true;
+}
+
+// Device-scope atomic max on the bits of a non-negative binary32 value
+// (unsigned order = value order for patterns with the sign bit clear).
+__device__ __forceinline__ void atomic_max_bits(float* dst, uint32_t bits) {
+  atomicMax(reinterpret_cast<unsigned int*>(dst), bits);
+}
+
+}  // namespace fp8lin

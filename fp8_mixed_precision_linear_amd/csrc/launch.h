@@ -1,0 +1,49 @@
+// launch.h -- host-side launchers behind the C ABI (internal to the library).
+// Each launcher assumes its arguments were validated by the entry point in
+// abi.hip and returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8lin {
+
+// Fill n dwords at p with v (a kernel, so it is safe inside graph capture).
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+
+// amax over n bf16 values (x 16-byte aligned); writes the result to *amax.
+hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t s);
+
+hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, int margin, float* scale,
+                                float* scale_inv, hipStream_t s);
+
+hipError_t launch_history_update(float* history, int64_t n, int64_t len, const float* amax_new,
+                                 int fmt, int margin, int algo, float* scale, float* scale_inv,
+                                 hipStream_t s);
+
+// Per-tensor cast with optional transpose and amax (amax must be zeroed by
+// the caller first when given).
+hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, const float* scale, int fmt,
+                       uint8_t* y, uint8_t* y_t, float* amax, hipStream_t s);
+
+// Block-wise cast (tile: 1 = 1x128, 2 = 128x128).
+hipError_t launch_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int tile,
+                             uint8_t* y, float* sinv, uint8_t* y_t, float* sinv_t, hipStream_t s);
+
+struct GemmParams {
+  int64_t M, N, K, lda, ldb, ldd;
+  const uint8_t* A;
+  int a_fmt, a_scaling;
+  const float* a_sinv;
+  const uint8_t* B;
+  int b_fmt, b_scaling;
+  const float* b_sinv;
+  void* D;
+  int d_f32;
+  float* d_amax;  // zeroed by the caller first when given
+  int accumulate;
+};
+
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+
+}  // namespace fp8lin

@@ -1,0 +1,152 @@
+// scale_kernels.hip -- amax reduction, scale computation and amax-history
+// update for gfx950.
+//
+// [MPG] = "Mixed Precision LLM Training: The Complete Guide":
+//   "Transformer Engine internals > Per-tensor scaling" (amax -> scale),
+//   "Delayed scaling (the default recipe)", "History-based scaling",
+//   "Calibration deep dive > Dynamic calibration (delayed scaling)".
+#include "fp8_device.h"
+#include "launch.h"
+
+namespace fp8lin {
+
+namespace {
+
+constexpr int kAmaxThreads = 512;
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = v;
+}
+
+// Block-wide max of one value per thread, then one device atomic per block.
+__device__ __forceinline__ void block_max_to(float* out, uint32_t v) {
+  __shared__ uint32_t part[kAmaxThreads / 64];
+  v = wave_max_u32(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t w = lane < (int)(blockDim.x >> 6) ? part[lane] : 0u;
+    w = wave_max_u32(w);
+    if (lane == 0 && w != 0u) atomic_max_bits(out, w);
+  }
+}
+
+// max |x| over n bf16 values: 16-byte loads (8 values) on a grid-stride
+// loop, two loads in flight per thread, packed 16-bit max, then a
+// wavefront / block reduction and one atomic per block.
+__global__ void __launch_bounds__(kAmaxThreads) k_amax(const uint16_t* __restrict__ x, int64_t n,
+                                                       float* __restrict__ amax) {
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int64_t nv = n >> 3;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint32_t m0 = 0, m1 = 0;
+  for (; i + stride < nv; i += 2 * stride) {
+    uint4 a = ld_nt16(xv + i);
+    uint4 b = ld_nt16(xv + i + stride);
+    m0 = absmax_pk(m0, a.x); m0 = absmax_pk(m0, a.y);
+    m0 = absmax_pk(m0, a.z); m0 = absmax_pk(m0, a.w);
+    m1 = absmax_pk(m1, b.x); m1 = absmax_pk(m1, b.y);
+    m1 = absmax_pk(m1, b.z); m1 = absmax_pk(m1, b.w);
+  }
+  if (i < nv) {
+    uint4 a = ld_nt16(xv + i);
+    m0 = absmax_pk(m0, a.x); m0 = absmax_pk(m0, a.y);
+    m0 = absmax_pk(m0, a.z); m0 = absmax_pk(m0, a.w);
+  }
+  uint32_t m = absmax_fold(absmax_pk(m0, m1));
+  // tail: the last n % 8 values
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    uint32_t t = (uint32_t)(x[(nv << 3) + threadIdx.x] & 0x7FFFu) << 16;
+    m = m > t ? m : t;
+  }
+  block_max_to(amax, m);
+}
+
+// Current scaling: one thread per tensor.
+__global__ void k_compute_scale(const float* __restrict__ amax, int64_t n, float fmax, int margin,
+                                float* __restrict__ scale, float* __restrict__ scale_inv) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = 1.0f, si = 1.0f;
+  scale_from_amax(amax[i], fmax, margin, s, si);
+  scale[i] = s;
+  scale_inv[i] = si;
+}
+
+// Delayed scaling: one thread per tensor shifts its history (newest first),
+// inserts the new amax, takes the window maximum (NaN propagates: compared
+// as bit patterns of non-negative values) or the newest entry, and updates
+// the scale only for a positive finite effective amax.
+__global__ void k_history_update(float* __restrict__ history, int64_t n, int64_t len,
+                                 const float* __restrict__ amax_new, float fmax, int margin,
+                                 int algo, float* __restrict__ scale,
+                                 float* __restrict__ scale_inv) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float* h = history + i * len;
+  const float a = amax_new[i];
+  uint32_t best = __float_as_uint(a);
+  for (int64_t j = len - 1; j >= 1; --j) {
+    float v = h[j - 1];
+    h[j] = v;
+    uint32_t b = __float_as_uint(v);
+    best = b > best ? b : best;
+  }
+  h[0] = a;
+  float eff = algo == 1 ? a : __uint_as_float(best);
+  float s, si;
+  if (scale_from_amax(eff, fmax, margin, s, si)) {
+    scale[i] = s;
+    scale_inv[i] = si;
+  }
+}
+
+inline float fmax_of(int fmt) { return fmt == 0 ? kMaxE4M3 : kMaxE5M2; }
+
+}  // namespace
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t s) {
+  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 1, 0u, s);
+  if (e != hipSuccess || n == 0) return e;
+  int64_t nv = n >> 3;
+  // enough blocks to keep every CU streaming: 2 blocks of 512 per CU on a
+  // 256-CU part, fewer for small tensors.
+  int64_t blocks = (nv + 2 * kAmaxThreads - 1) / (2 * kAmaxThreads);
+  if (blocks < 1) blocks = 1;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(k_amax, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, s, x, n, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, int margin, float* scale,
+                                float* scale_inv, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_compute_scale, dim3((unsigned)blocks), dim3(256), 0, s, amax, n,
+                     fmax_of(fmt), margin, scale, scale_inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_history_update(float* history, int64_t n, int64_t len, const float* amax_new,
+                                 int fmt, int margin, int algo, float* scale, float* scale_inv,
+                                 hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 63) / 64;
+  hipLaunchKernelGGL(k_history_update, dim3((unsigned)blocks), dim3(64), 0, s, history, n, len,
+                     amax_new, fmax_of(fmt), margin, algo, scale, scale_inv);
+  return hipGetLastError();
+}
+
+}  // namespace fp8lin

@@ -1,0 +1,181 @@
+"""Thin Python binding of libfp8lin (the C ABI in include/fp8lin.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Tensors are torch tensors on the GPU (PyTorch provides device
+memory and streams); each call passes their device pointers and sizes to the
+C function of the same name and raises Fp8Error on a non-OK status.  There
+is no fallback: if libfp8lin.so is missing or fails to load, importing this
+module raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
+
+E4M3, E5M2 = 0, 1
+SCALE_TENSOR, SCALE_1x128, SCALE_128x128 = 0, 1, 2
+OUT_BF16, OUT_F32 = 0, 1
+AMAX_MAX, AMAX_MOST_RECENT = 0, 1
+
+STATUS = {0: "FP8_OK", 1: "FP8_ERR_NULL", 2: "FP8_ERR_SHAPE", 3: "FP8_ERR_ALIGN",
+          4: "FP8_ERR_UNSUPPORTED", 5: "FP8_ERR_LAUNCH", 6: "FP8_ERR_ARG"}
+
+
+class Fp8Error(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+class GemmArgs(C.Structure):
+    _fields_ = [("M", C.c_int64), ("N", C.c_int64), ("K", C.c_int64),
+                ("lda", C.c_int64), ("ldb", C.c_int64), ("ldd", C.c_int64),
+                ("A", C.c_void_p), ("a_fmt", C.c_int), ("a_scaling", C.c_int),
+                ("a_scale_inv", C.c_void_p),
+                ("B", C.c_void_p), ("b_fmt", C.c_int), ("b_scaling", C.c_int),
+                ("b_scale_inv", C.c_void_p),
+                ("D", C.c_void_p), ("d_dtype", C.c_int), ("d_amax", C.c_void_p),
+                ("accumulate", C.c_int)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m fp8_mixed_precision_linear_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int
+    sig = {
+        "fp8_abi_version": (i32, []),
+        "fp8_status_string": (C.c_char_p, [i32]),
+        "fp8_amax": (i32, [vp, i64, i64, vp, vp]),
+        "fp8_compute_scale": (i32, [vp, i64, i32, i32, vp, vp, vp]),
+        "fp8_amax_history_update": (i32, [vp, i64, i64, vp, i32, i32, i32, vp, vp, vp]),
+        "fp8_cast_e4m3": (i32, [vp, i64, i64, vp, vp, vp, vp, vp]),
+        "fp8_cast_e5m2": (i32, [vp, i64, i64, vp, vp, vp, vp, vp]),
+        "fp8_cast_block": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
+        "fp8_scaled_gemm": (i32, [C.POINTER(GemmArgs), vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    return L
+
+
+_L = _load()
+
+
+def abi_version() -> int:
+    return _L.fp8_abi_version()
+
+
+def status_string(status: int) -> str:
+    return _L.fp8_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise Fp8Error(fn, status, status_string(status))
+
+
+def _ptr(t, dtypes=None, name="tensor"):
+    """Device pointer of a GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+_BF16 = (torch.bfloat16,)
+_F32 = (torch.float32,)
+_U8 = (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2)
+
+
+def _rc(x):
+    """(rows, cols) of a tensor viewed as [rows][cols] (1-D: one row)."""
+    if x.dim() == 0:
+        return 1, 1
+    if x.dim() == 1:
+        return 1, x.shape[0]
+    cols = 1
+    for d in x.shape[1:]:
+        cols *= d
+    return x.shape[0], cols
+
+
+def fp8_amax(x, amax, stream=None):
+    rows, cols = _rc(x)
+    _check("fp8_amax", _L.fp8_amax(_ptr(x, _BF16, "x"), rows, cols, _ptr(amax, _F32, "amax"),
+                                   _stream(stream)))
+
+
+def fp8_compute_scale(amax, fmt, margin, scale, scale_inv, stream=None):
+    _check("fp8_compute_scale",
+           _L.fp8_compute_scale(_ptr(amax, _F32, "amax"), amax.numel(), fmt, margin,
+                                _ptr(scale, _F32, "scale"), _ptr(scale_inv, _F32, "scale_inv"),
+                                _stream(stream)))
+
+
+def fp8_amax_history_update(history, amax_new, fmt, margin, algo, scale, scale_inv, stream=None):
+    n, ln = history.shape
+    _check("fp8_amax_history_update",
+           _L.fp8_amax_history_update(_ptr(history, _F32, "history"), n, ln,
+                                      _ptr(amax_new, _F32, "amax_new"), fmt, margin, algo,
+                                      _ptr(scale, _F32, "scale"), _ptr(scale_inv, _F32, "scale_inv"),
+                                      _stream(stream)))
+
+
+def _cast(fn, x, scale, y, y_t, amax_out, stream):
+    rows, cols = _rc(x)
+    _check(fn.__name__, fn(_ptr(x, _BF16, "x"), rows, cols, _ptr(scale, _F32, "scale"),
+                           _ptr(y, _U8, "y"), _ptr(y_t, _U8, "y_t"),
+                           _ptr(amax_out, _F32, "amax_out"), _stream(stream)))
+
+
+def fp8_cast_e4m3(x, scale, y=None, y_t=None, amax_out=None, stream=None):
+    _cast(_L.fp8_cast_e4m3, x, scale, y, y_t, amax_out, stream)
+
+
+def fp8_cast_e5m2(x, scale, y=None, y_t=None, amax_out=None, stream=None):
+    _cast(_L.fp8_cast_e5m2, x, scale, y, y_t, amax_out, stream)
+
+
+def fp8_cast_block(x, fmt, tile, y=None, scale_inv=None, y_t=None, scale_inv_t=None, stream=None):
+    rows, cols = _rc(x)
+    _check("fp8_cast_block",
+           _L.fp8_cast_block(_ptr(x, _BF16, "x"), rows, cols, fmt, tile, _ptr(y, _U8, "y"),
+                             _ptr(scale_inv, _F32, "scale_inv"), _ptr(y_t, _U8, "y_t"),
+                             _ptr(scale_inv_t, _F32, "scale_inv_t"), _stream(stream)))
+
+
+def fp8_scaled_gemm(A, a_fmt, a_scaling, a_scale_inv, B, b_fmt, b_scaling, b_scale_inv, D,
+                    d_amax=None, accumulate=False, stream=None):
+    """D [M][N] (bf16 or fp32 tensor) = A [M][K] . B [N][K]^T with FP8 codes."""
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(D.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, D {tuple(D.shape)}")
+    d_dtype = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[D.dtype]
+    g = GemmArgs(M, N, K, K, K, N,
+                 _ptr(A, _U8, "A"), a_fmt, a_scaling, _ptr(a_scale_inv, _F32, "a_scale_inv"),
+                 _ptr(B, _U8, "B"), b_fmt, b_scaling, _ptr(b_scale_inv, _F32, "b_scale_inv"),
+                 _ptr(D, None, "D"), d_dtype, _ptr(d_amax, _F32, "d_amax"), 1 if accumulate else 0)
+    _check("fp8_scaled_gemm", _L.fp8_scaled_gemm(C.byref(g), _stream(stream)))

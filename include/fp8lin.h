@@ -1,0 +1,227 @@
+/*
+ * fp8lin.h -- C ABI of the FP8 scaled linear layer for AMD gfx950 (CDNA4).
+ *
+ * The layer: an amax reduction, a scale (current per-tensor, delayed from an
+ * amax history, or block-wise), a saturating round-to-nearest-even cast to
+ * FP8 (E4M3 for activations and weights, E5M2 for gradients), and the
+ * forward / dgrad / wgrad GEMMs with FP32 accumulation and the inverse
+ * scales applied in the epilogue (per-tensor) or per 128-wide K block
+ * (block-wise).
+ *
+ * Sources, cited by page title and section:
+ *   [MPG]  "Mixed Precision LLM Training: The Complete Guide"
+ *   [TALK] PyData Amsterdam 2026, "FP8 for pretraining" (talk abstract)
+ *
+ * Conventions for every entry point:
+ *   - Pointers are caller-owned DEVICE memory on the current HIP device,
+ *     unless stated otherwise.  The library never allocates, frees or keeps
+ *     a pointer after the call returns.
+ *   - Every call only enqueues work on `stream` (0 = the null stream) and
+ *     returns; nothing is read back to the host, so a sequence of calls can
+ *     run without host synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error code other than FP8_ERR_LAUNCH nothing was enqueued.
+ *   - bf16 tensors are row-major [rows][cols] arrays of 16-bit patterns.
+ *   - Outputs named *amax* are overwritten (not max-accumulated).
+ *   - No global mutable state: calls on different streams may interleave.
+ *   - FP8 codes are OCP E4M3 (max 448, no Inf, NaN = 0x7F/0xFF) and OCP E5M2
+ *     (max 57344); the cast saturates finite overflow and +-Inf to +-max,
+ *     maps NaN to 0x7F|sign, keeps the sign of zero, and rounds to nearest
+ *     even after a binary32 multiply by the scale.
+ */
+#ifndef FP8LIN_H
+#define FP8LIN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8LIN_ABI_VERSION 1
+
+/* [MPG] "The precision formats", "FP8 E4M3", "FP8 E5M2": E4M3 = 4 exponent
+ * and 3 mantissa bits, range about 2^-9..448; E5M2 = 5 and 2, range about
+ * 2^-16..57344.  "The HYBRID recipe": E4M3 forward, E5M2 for gradients. */
+typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format;
+
+typedef enum {
+  FP8_OK = 0,
+  FP8_ERR_NULL = 1,         /* a required pointer is NULL */
+  FP8_ERR_SHAPE = 2,        /* negative size, or a shape rule is broken */
+  FP8_ERR_ALIGN = 3,        /* pointer or leading dimension misaligned */
+  FP8_ERR_UNSUPPORTED = 4,  /* valid request this build does not implement */
+  FP8_ERR_LAUNCH = 5,       /* the HIP runtime rejected a kernel launch */
+  FP8_ERR_ARG = 6           /* an enum or scalar argument is out of range */
+} fp8_status;
+
+/* [MPG] "Calibration deep dive > Dynamic calibration (delayed scaling)":
+ * amax_compute_algo "max" (over the history) or "most_recent". */
+typedef enum { FP8_AMAX_MAX = 0, FP8_AMAX_MOST_RECENT = 1 } fp8_amax_algo;
+
+/* [MPG] "Per-row vs per-tensor scaling" and "DeepSeek FP8 training recipe
+ * in detail > Block-wise scaling at 128 granularity": one scale per tensor,
+ * per 128-element segment of a row (1x128), or per 128x128 block. */
+typedef enum { FP8_SCALE_TENSOR = 0, FP8_SCALE_1x128 = 1, FP8_SCALE_128x128 = 2 } fp8_scaling;
+
+typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_F32 = 1 } fp8_out_dtype;
+
+/* ABI version (FP8LIN_ABI_VERSION of the built library). */
+int fp8_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fp8_status_string(fp8_status status);
+
+/* ------------------------------------------------------------------------
+ * fp8_amax -- amax = max |x| over a bf16 tensor.
+ * [MPG] "Transformer Engine internals > Per-tensor scaling": the scale is
+ * set from the tensor's maximum absolute value.
+ *   x_bf16  [rows][cols] bf16, 16-byte aligned.
+ *   amax    1 float, overwritten.  The maximum is exact (no rounding is
+ *           involved); a NaN element makes the result NaN; an empty tensor
+ *           gives 0.
+ * Errors: FP8_ERR_NULL (x with rows*cols > 0, or amax NULL), FP8_ERR_SHAPE
+ * (negative size), FP8_ERR_ALIGN (x not 16-byte aligned).
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, float* amax,
+                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_compute_scale -- current scaling: scale = fl32(fmax / amax) * 2^-margin,
+ * scale_inv = fl32(1 / scale), elementwise over n tensors.
+ * [MPG] "Per-tensor scaling" (the scale puts the amax at the top of the FP8
+ * range; the matmul result is multiplied by the inverse scale) and the
+ * DelayedScaling recipe's `margin` argument (formula not given; read as a
+ * division of the scale by 2^margin).
+ *   amax       [n] floats (device).
+ *   fmt        fmax = 448 (E4M3) or 57344 (E5M2).
+ *   margin     0..64.
+ *   scale, scale_inv  [n] floats, overwritten.
+ * amax == 0 or non-finite: scale = 1, scale_inv = 1 ([MPG] "torch.compile
+ * and FP8": no scale update for an all-zero tensor).  A quotient that
+ * overflows binary32 is clamped to FLT_MAX.  Divisions are correctly
+ * rounded.
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE (n < 0), FP8_ERR_ARG (fmt, margin).
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_compute_scale(const float* amax, int64_t n, fp8_format fmt, int margin,
+                             float* scale, float* scale_inv, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_amax_history_update -- delayed scaling from an amax history.
+ * [MPG] "Delayed scaling (the default recipe)" and "History-based scaling":
+ * the scale used at step t+1 comes from the maxima of the last `len` steps.
+ * For each tensor i < n:
+ *   history[i][len-1..1] = history[i][len-2..0]; history[i][0] = amax_new[i];
+ *   eff = max_j history[i][j] (FP8_AMAX_MAX; NaN propagates) or
+ *         history[i][0] (FP8_AMAX_MOST_RECENT);
+ *   if eff > 0 and finite: scale[i] = fl32(fmax/eff)*2^-margin,
+ *                          scale_inv[i] = fl32(1/scale[i]);
+ *   otherwise scale[i], scale_inv[i] keep their previous values.
+ *   history    [n][len] floats, newest first, updated in place (initialise
+ *              to 0 with scale = scale_inv = 1 before the first step).
+ *   amax_new   [n] floats (e.g. the fused amax of the step's casts).
+ * Stream order makes the update happen after the step's casts and GEMMs
+ * that read the old scale when all are enqueued on one stream.
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE (n < 0, len < 1 or > 1024),
+ * FP8_ERR_ARG (fmt, margin, algo).
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_amax_history_update(float* history, int64_t n, int64_t len,
+                                   const float* amax_new, fp8_format fmt, int margin,
+                                   fp8_amax_algo algo, float* scale, float* scale_inv,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_cast_e4m3 / fp8_cast_e5m2 -- per-tensor saturating RNE cast,
+ * q = encode(fl32(x * scale)), with optional fused transpose and amax.
+ * [MPG] "Per-tensor scaling" (multiply by the scale before quantising);
+ * [TALK] outline 05:00-15:00 (E4M3 for activations and weights, E5M2 for
+ * gradients).
+ *   x_bf16    [rows][cols] bf16, 16-byte aligned.
+ *   scale     1 float (device): the quantisation scale (not the inverse).
+ *   y         [rows][cols] FP8 codes, or NULL.
+ *   y_t       [cols][rows] FP8 codes (y_t[c][r] = y[r][c]), or NULL.
+ *   amax_out  1 float, overwritten with max |x| (as fp8_amax), or NULL.
+ *   y and y_t must not both be NULL; y, y_t 16-byte aligned.
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN.
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_cast_e4m3(const void* x_bf16, int64_t rows, int64_t cols, const float* scale,
+                         uint8_t* y, uint8_t* y_t, float* amax_out, hipStream_t stream);
+fp8_status fp8_cast_e5m2(const void* x_bf16, int64_t rows, int64_t cols, const float* scale,
+                         uint8_t* y, uint8_t* y_t, float* amax_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_cast_block -- block-wise cast with per-tile scales computed on the fly.
+ * [MPG] "DeepSeek FP8 training recipe in detail > Block-wise scaling at 128
+ * granularity": one scale per 128x128 weight block, one per 128-element
+ * activation segment, stored next to the data and applied in the matmul.
+ * Per tile: amax over the elements present, scale = fl32(fmax/amax)
+ * (1 for an all-zero or non-finite tile), scale_inv = fl32(1/scale), then
+ * the cast of fp8_cast_e4m3 with that scale.
+ *   x_bf16   [rows][cols] bf16, 16-byte aligned.
+ *   tile == FP8_SCALE_1x128:
+ *     y         [rows][cols], tiles of 128 consecutive columns in one row;
+ *     scale_inv [ceil(cols/128)][rows]  (kb-major);
+ *     y_t       [cols][rows], tiles of 128 consecutive ROWS in one column
+ *               (the token-axis tiles of the transposed operand), each
+ *               quantised from bf16 with its own scale;
+ *     scale_inv_t [ceil(rows/128)][cols].
+ *   tile == FP8_SCALE_128x128:
+ *     one scale per 128x128 block; y_t is the byte transpose of y;
+ *     scale_inv   [ceil(cols/128)][ceil(rows/128)];
+ *     scale_inv_t [ceil(rows/128)][ceil(cols/128)] (same values, transposed).
+ *   Each of (y, scale_inv) and (y_t, scale_inv_t) is either both given or
+ *   both NULL, and at least one pair is given.  y, y_t 16-byte aligned.
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_ARG.
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_cast_block(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                          fp8_scaling tile, uint8_t* y, float* scale_inv, uint8_t* y_t,
+                          float* scale_inv_t, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_scaled_gemm -- D[m][n] = sum_k A[m][k] * B[n][k] with FP8 operands,
+ * FP32 accumulation and dequantisation.
+ * [MPG] "Per-tensor scaling" (multiply the matmul result by the inverse
+ * scales), "Skipping the BAcc accumulator promotion" and "Mixed-precision
+ * accumulation" (partial products accumulate in FP32; the result is cast to
+ * BF16), "Block-wise scaling at 128 granularity" (block scales applied
+ * during the matmul).
+ * Both operands are K-contiguous ("TN"): A [M][lda], B [N][ldb] FP8 codes.
+ * The layer's three GEMMs are operand choices (weights stored [in][out]):
+ *   forward  Y  = X W      : A = X_q   [T][in],  B = W^T_q  [out][in]
+ *   dgrad    dX = dY W^T   : A = dY_q  [T][out], B = W_q    [in][out]
+ *   wgrad    dW = X^T dY   : A = X^T_q [in][T],  B = dY^T_q [out][T]
+ * Inverse-scale layouts (as produced by the casts):
+ *   FP8_SCALE_TENSOR  : 1 float;
+ *   FP8_SCALE_1x128   : [ceil(K/128)][rows]       (rows = M for A, N for B);
+ *   FP8_SCALE_128x128 : [ceil(K/128)][ceil(rows/128)].
+ * Result: tensor x tensor: D = (sum_k a b) * sa * sb; any block scaling:
+ * D = sum_kb (sum_{k in kb} a b) * sa(m,kb) * sb(n,kb), each 128-wide K
+ * block promoted into the FP32 accumulator.  D is [M][ldd], BF16 (round
+ * to nearest even) or FP32.  accumulate = 1 (FP32 output only) adds the
+ * result to the existing D.  d_amax (nullable, 1 float) is overwritten with
+ * max |D| of the stored output values.
+ * Shape rules: M, N, K >= 0; K % 16 == 0 (tensor x tensor) or K % 128 == 0
+ * (block modes); lda, ldb >= K and multiples of 16; ldd >= N; A, B 16-byte
+ * aligned; D 4-byte aligned.  K == 0 gives D = 0 (or D unchanged when
+ * accumulating).
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_ARG,
+ * FP8_ERR_UNSUPPORTED (accumulate with BF16 output).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t M, N, K;
+  int64_t lda, ldb, ldd;
+  const uint8_t* A; fp8_format a_fmt; fp8_scaling a_scaling; const float* a_scale_inv;
+  const uint8_t* B; fp8_format b_fmt; fp8_scaling b_scaling; const float* b_scale_inv;
+  void* D; fp8_out_dtype d_dtype;
+  float* d_amax;
+  int accumulate;
+} fp8_gemm_args;
+
+fp8_status fp8_scaled_gemm(const fp8_gemm_args* args, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8LIN_H */

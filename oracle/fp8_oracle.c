@@ -418,18 +418,22 @@ static void* gemm_worker(void* p) {
   int64_t nkb = (g->K + 127) / 128;
   int qa = g->a_fmt == O_E4M3 ? 9 : 16, qb = g->b_fmt == O_E4M3 ? 9 : 16;
   int64_t* arow = (int64_t*)malloc(sizeof(int64_t) * (size_t)g->K);
-  int64_t* bcol = (int64_t*)malloc(sizeof(int64_t) * (size_t)g->K);
+  int64_t lut_b[256];
+  int nan_b[256];
+  /* decode table of B's format: integer significand of every code */
+  for (int c = 0; c < 256; ++c) { nan_b[c] = 0; lut_b[c] = fp8_int((uint8_t)c, g->b_fmt, &nan_b[c]); }
   for (int64_t ii = jb->i0; ii < jb->i1; ++ii) {
     int64_t m = jb->ms[ii];
     int anan = 0;
     for (int64_t k = 0; k < g->K; ++k) arow[k] = fp8_int(g->A[m * g->lda + k], g->a_fmt, &anan);
     for (int64_t jj = 0; jj < jb->nn; ++jj) {
       int64_t n = jb->ns[jj];
+      const uint8_t* brow = g->B + n * g->ldb;
       int bnan = 0;
       long double e_sum = 0.0L;
       double dsum = 0.0;
       float acc = 0.0f;
-      for (int64_t k = 0; k < g->K; ++k) bcol[k] = fp8_int(g->B[n * g->ldb + k], g->b_fmt, &bnan);
+      for (int64_t k = 0; k < g->K; ++k) bnan |= nan_b[brow[k]];
       for (int64_t kb = 0; kb < nkb; ++kb) {
         int64_t k0 = kb * 128, k1 = k0 + 128 < g->K ? k0 + 128 : g->K;
         __int128 S = 0;
@@ -437,7 +441,7 @@ static void* gemm_worker(void* p) {
         float sa = scale_at(g->a_scaling, g->a_sinv, g->M, m, kb);
         float sb = scale_at(g->b_scaling, g->b_sinv, g->N, n, kb);
         for (int64_t k = k0; k < k1; ++k) {
-          __int128 p = (__int128)arow[k] * (__int128)bcol[k];
+          __int128 p = (__int128)arow[k] * (__int128)lut_b[brow[k]];
           S += p;
           Sabs += (unsigned __int128)(p < 0 ? -p : p);
         }
@@ -473,7 +477,7 @@ static void* gemm_worker(void* p) {
       if (jb->Dm) jb->Dm[ii * jb->nn + jj] = dsum;
     }
   }
-  free(arow); free(bcol);
+  free(arow);
   return NULL;
 }
 

@@ -1,0 +1,71 @@
+"""Helpers for the GPU parity tests: host<->device copies of bf16 bit
+patterns, guarded output buffers (canary bytes around every output catch
+out-of-bounds writes) and the GEMM acceptance gates."""
+import sys
+
+import numpy as np
+import torch
+
+CANARY = 0xA5
+PAD = 256  # bytes of guard on each side (keeps 16-byte alignment)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(a_u16: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a_u16, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_u16(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+class Guarded:
+    """An output tensor with canary bytes before and after it."""
+
+    def __init__(self, shape, dtype):
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        n = int(np.prod(self.shape)) if len(self.shape) else 1
+        esz = torch.tensor([], dtype=dtype).element_size()
+        self.nbytes = n * esz
+        self.buf = torch.full((self.nbytes + 2 * PAD,), CANARY, dtype=torch.uint8, device="cuda")
+        self.t = self.buf[PAD:PAD + self.nbytes].view(dtype).view(self.shape)
+
+    def check(self):
+        b = self.buf.cpu().numpy()
+        assert np.all(b[:PAD] == CANARY), "write before the start of an output buffer"
+        assert np.all(b[PAD + self.nbytes:] == CANARY), "write past the end of an output buffer"
+
+    def np(self):
+        return self.t.cpu().numpy()
+
+
+def bf16_half_ulp(f: np.ndarray) -> np.ndarray:
+    """Half an ulp of bf16 at the magnitude of f (binary32 values)."""
+    a = np.abs(f.astype(np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.exp2(e - 8)
+
+
+def gemm_gate(G: np.ndarray, F: np.ndarray, D: np.ndarray, bf16: bool, tol: float = 1e-3):
+    """GPU result G against the oracle's FP32-accumulated F with magnitude D:
+    rel = |G - F| / max(|F|, D/64) <= tol (plus half a bf16 ulp of F for BF16
+    outputs).  Returns (ok, max_rel, n_floored)."""
+    G = G.astype(np.float64)
+    Fd = F.astype(np.float64)
+    floor = np.maximum(np.abs(Fd), D / 64.0)
+    err = np.abs(G - Fd)
+    if bf16:
+        err = np.maximum(err - bf16_half_ulp(F), 0.0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(floor > 0, err / floor, np.where(err == 0, 0.0, np.inf))
+    return bool(np.all(rel <= tol)), float(np.max(rel)) if rel.size else 0.0, int(np.sum(np.abs(Fd) < D / 64.0))
