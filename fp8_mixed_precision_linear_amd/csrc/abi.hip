@@ -19,8 +19,9 @@ inline fp8_status launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8
 fp8_status cast_common(const void* x, int64_t rows, int64_t cols, const float* scale, uint8_t* y,
                        uint8_t* y_t, float* amax_out, int fmt, hipStream_t stream) {
   if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
-  if (scale == nullptr || (y == nullptr && y_t == nullptr)) return FP8_ERR_NULL;
-  if (rows > 0 && cols > 0 && x == nullptr) return FP8_ERR_NULL;
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty && (x == nullptr || scale == nullptr || (y == nullptr && y_t == nullptr)))
+    return FP8_ERR_NULL;
   if (!aligned16(x) || !aligned16(y) || !aligned16(y_t)) return FP8_ERR_ALIGN;
   if (amax_out && !aligned4(amax_out)) return FP8_ERR_ALIGN;
   return launched(launch_cast(static_cast<const uint16_t*>(x), rows, cols, scale, fmt, y, y_t,
@@ -95,10 +96,11 @@ fp8_status fp8_cast_block(const void* x_bf16, int64_t rows, int64_t cols, fp8_fo
                           float* scale_inv_t, hipStream_t stream) {
   if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
   if (!fmt_ok(fmt) || (tile != FP8_SCALE_1x128 && tile != FP8_SCALE_128x128)) return FP8_ERR_ARG;
+  if (rows == 0 || cols == 0) return FP8_OK;  // nothing to quantise
   if ((y == nullptr) != (scale_inv == nullptr) || (y_t == nullptr) != (scale_inv_t == nullptr))
     return FP8_ERR_NULL;
   if (y == nullptr && y_t == nullptr) return FP8_ERR_NULL;
-  if (rows > 0 && cols > 0 && x_bf16 == nullptr) return FP8_ERR_NULL;
+  if (x_bf16 == nullptr) return FP8_ERR_NULL;
   if (!aligned16(x_bf16) || !aligned16(y) || !aligned16(y_t)) return FP8_ERR_ALIGN;
   if (!aligned4(scale_inv) || !aligned4(scale_inv_t)) return FP8_ERR_ALIGN;
   return launched(launch_cast_block(static_cast<const uint16_t*>(x_bf16), rows, cols, fmt, tile, y,

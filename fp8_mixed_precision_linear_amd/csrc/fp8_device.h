@@ -44,18 +44,30 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Saturation before the hardware conversion: finite values beyond the
-// format's largest magnitude and +-Inf become +-max; NaN passes through so
-// the conversion emits a NaN code.  Values between max and the rounding
-// midpoint above it round to max anyway, so clamping first and rounding
-// second equals rounding first and saturating second.
+// format's largest magnitude and +-Inf become +-max.  Values between max and
+// the rounding midpoint above it round to max anyway, so clamping first and
+// rounding second equals rounding first and saturating second.
 template <int FMT>
 __device__ __forceinline__ float sat(float v) {
-  float c = __builtin_amdgcn_fmed3f(v, -Fmt<FMT>::max, Fmt<FMT>::max);
-  return __builtin_isnan(v) ? v : c;
+  return __builtin_amdgcn_fmed3f(v, -Fmt<FMT>::max, Fmt<FMT>::max);
+}
+
+// The conversion instructions emit one fixed NaN code whatever the input's
+// sign; the layer's cast maps NaN to 0x7F | sign.  Only wavefronts that
+// actually hold a NaN take this path.
+__device__ __noinline__ uint32_t nan_patch(uint32_t w, float a, float b, float c, float d) {
+  const float v[4] = {a, b, c, d};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (__builtin_isnan(v[i])) {
+      const uint32_t code = 0x7Fu | ((__float_as_uint(v[i]) >> 24) & 0x80u);
+      w = (w & ~(0xFFu << (8 * i))) | (code << (8 * i));
+    }
+  return w;
 }
 
 // Four binary32 values -> four FP8 codes packed little-endian in a dword
-// (a in byte 0 ... d in byte 3), round to nearest even.
+// (a in byte 0 ... d in byte 3), round to nearest even, saturating.
 template <int FMT>
 __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
   int w;
@@ -66,6 +78,8 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
     w = __builtin_amdgcn_cvt_pk_bf8_f32(sat<1>(a), sat<1>(b), 0, false);
     w = __builtin_amdgcn_cvt_pk_bf8_f32(sat<1>(c), sat<1>(d), w, true);
   }
+  if (__builtin_isnan(a) | __builtin_isnan(b) | __builtin_isnan(c) | __builtin_isnan(d))
+    return nan_patch((uint32_t)w, a, b, c, d);
   return (uint32_t)w;
 }
 

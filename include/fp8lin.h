@@ -142,7 +142,8 @@ fp8_status fp8_amax_history_update(float* history, int64_t n, int64_t len,
  *   y         [rows][cols] FP8 codes, or NULL.
  *   y_t       [cols][rows] FP8 codes (y_t[c][r] = y[r][c]), or NULL.
  *   amax_out  1 float, overwritten with max |x| (as fp8_amax), or NULL.
- *   y and y_t must not both be NULL; y, y_t 16-byte aligned.
+ *   y and y_t must not both be NULL (unless the tensor is empty); y, y_t
+ *   16-byte aligned.
  * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN.
  * ---------------------------------------------------------------------- */
 fp8_status fp8_cast_e4m3(const void* x_bf16, int64_t rows, int64_t cols, const float* scale,
@@ -171,7 +172,8 @@ fp8_status fp8_cast_e5m2(const void* x_bf16, int64_t rows, int64_t cols, const f
  *     scale_inv   [ceil(cols/128)][ceil(rows/128)];
  *     scale_inv_t [ceil(rows/128)][ceil(cols/128)] (same values, transposed).
  *   Each of (y, scale_inv) and (y_t, scale_inv_t) is either both given or
- *   both NULL, and at least one pair is given.  y, y_t 16-byte aligned.
+ *   both NULL, and at least one pair is given (an empty tensor needs no
+ *   pointers and enqueues nothing).  y, y_t 16-byte aligned.
  * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_ARG.
  * ---------------------------------------------------------------------- */
 fp8_status fp8_cast_block(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,

@@ -409,8 +409,16 @@ typedef struct {
   const int64_t* ms; int64_t nm;
   const int64_t* ns; int64_t nn;
   double* E; float* F; double* Dm;
+  double* H; int hgroup; int hbits;   /* optional summation-precision bound */
   int64_t i0, i1;   /* range of ms indices for this worker */
 } gemm_job;
+
+/* floor(log2(v)) of a positive 128-bit integer */
+static int ilog2_u128(unsigned __int128 v) {
+  int e = -1;
+  while (v) { v >>= 1; ++e; }
+  return e;
+}
 
 static void* gemm_worker(void* p) {
   gemm_job* jb = (gemm_job*)p;
@@ -431,7 +439,7 @@ static void* gemm_worker(void* p) {
       const uint8_t* brow = g->B + n * g->ldb;
       int bnan = 0;
       long double e_sum = 0.0L;
-      double dsum = 0.0;
+      double dsum = 0.0, hsum = 0.0;
       float acc = 0.0f;
       for (int64_t k = 0; k < g->K; ++k) bnan |= nan_b[brow[k]];
       for (int64_t kb = 0; kb < nkb; ++kb) {
@@ -445,6 +453,26 @@ static void* gemm_worker(void* p) {
           S += p;
           Sabs += (unsigned __int128)(p < 0 ? -p : p);
         }
+        if (jb->H) {
+          /* per group of hgroup consecutive k: (hgroup-1) products may each
+           * lose less than 2^(e_max - hbits), e_max = exponent of the
+           * group's largest |product| */
+          for (int64_t k = k0; k < k1; k += jb->hgroup) {
+            unsigned __int128 gm = 0;
+            for (int64_t kk = k; kk < k + jb->hgroup && kk < k1; ++kk) {
+              __int128 p = (__int128)arow[kk] * (__int128)lut_b[brow[kk]];
+              unsigned __int128 ap = (unsigned __int128)(p < 0 ? -p : p);
+              if (ap > gm) gm = ap;
+            }
+            if (gm) {
+              int e = ilog2_u128(gm) - jb->hbits;
+              double t = (double)(jb->hgroup - 1) * ldexp(1.0, e - (qa + qb));
+              hsum += t * fabs((double)scale_at(g->a_scaling, g->a_sinv, g->M, m, kb)) *
+                      fabs((double)scale_at(g->b_scaling, g->b_sinv, g->N, n, kb));
+            }
+          }
+        }
+
         /* exact value of the block: S * 2^-(qa+qb) * sa * sb */
         long double Sl = (long double)S;               /* |S| < 2^65: exact to 2^-64 rel */
         long double blk = ldexpl(Sl, -(qa + qb));
@@ -475,6 +503,7 @@ static void* gemm_worker(void* p) {
       if (jb->E) jb->E[ii * jb->nn + jj] = (double)e_sum;
       if (jb->F) jb->F[ii * jb->nn + jj] = acc;
       if (jb->Dm) jb->Dm[ii * jb->nn + jj] = dsum;
+      if (jb->H) jb->H[ii * jb->nn + jj] = hsum;
     }
   }
   free(arow);
@@ -484,9 +513,24 @@ static void* gemm_worker(void* p) {
 /* ldexpf on a float: exact for the power-of-two scalings used above
  * (results stay normal for |S| >= 1). */
 
+void o_gemm_h(const o_gemm_args* g, const int64_t* ms, int64_t nm,
+              const int64_t* ns, int64_t nn, double* E, float* F, double* Dm,
+              double* H, int hgroup, int hbits, int nthreads);
+
 void o_gemm(const o_gemm_args* g, const int64_t* ms, int64_t nm,
             const int64_t* ns, int64_t nn, double* E, float* F, double* Dm,
             int nthreads) {
+  o_gemm_h(g, ms, nm, ns, nn, E, F, Dm, NULL, 8, 13, nthreads);
+}
+
+/* As o_gemm, plus H: a bound on the error of a matrix unit that sums each
+ * group of `hgroup` consecutive products exactly after truncating every
+ * product below 2^(e_max - hbits) (e_max: exponent of the group's largest
+ * product), in original (dequantised) units.  This is a tolerance model for
+ * tests of a GPU implementation, not part of what the layer computes. */
+void o_gemm_h(const o_gemm_args* g, const int64_t* ms, int64_t nm,
+              const int64_t* ns, int64_t nn, double* E, float* F, double* Dm,
+              double* H, int hgroup, int hbits, int nthreads) {
   pthread_t th[256];
   gemm_job jobs[256];
   if (nthreads < 1) nthreads = 1;
@@ -495,6 +539,7 @@ void o_gemm(const o_gemm_args* g, const int64_t* ms, int64_t nm,
   for (int t = 0; t < nthreads; ++t) {
     jobs[t].g = g; jobs[t].ms = ms; jobs[t].nm = nm; jobs[t].ns = ns; jobs[t].nn = nn;
     jobs[t].E = E; jobs[t].F = F; jobs[t].Dm = Dm;
+    jobs[t].H = H; jobs[t].hgroup = hgroup < 1 ? 1 : hgroup; jobs[t].hbits = hbits;
     jobs[t].i0 = nm * t / nthreads; jobs[t].i1 = nm * (t + 1) / nthreads;
   }
   for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, gemm_worker, &jobs[t]);

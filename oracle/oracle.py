@@ -93,6 +93,10 @@ def lib():
         L.o_gemm.restype = None
         L.o_gemm.argtypes = [C.POINTER(_GemmArgs), C.c_void_p, C.c_int64, C.c_void_p, C.c_int64,
                              C.c_void_p, C.c_void_p, C.c_void_p, C.c_int]
+        L.o_gemm_h.restype = None
+        L.o_gemm_h.argtypes = [C.POINTER(_GemmArgs), C.c_void_p, C.c_int64, C.c_void_p, C.c_int64,
+                               C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int,
+                               C.c_int]
         L.o_gemm_ref_bound.restype = None
         L.o_gemm_ref_bound.argtypes = [C.POINTER(_GemmArgs), C.c_void_p, C.c_void_p,
                                        C.c_void_p, C.c_int64, C.c_void_p, C.c_int64,
@@ -304,10 +308,12 @@ def _gemm_args(A, a_fmt, a_scaling, a_sinv, B, b_fmt, b_scaling, b_sinv, keep):
 
 
 def gemm(A, a_fmt, a_scaling, a_sinv, B, b_fmt, b_scaling, b_sinv, ms=None, ns=None,
-         want=("E", "F", "D")):
+         want=("E", "F", "D"), hgroup=8, hbits=13):
     """Oracle GEMM D = A B^T (both K-contiguous) with dequant scales.
     Returns dict E (float64), F (float32), D (float64 magnitude), each
-    [len(ms)][len(ns)]."""
+    [len(ms)][len(ns)]; with "H" in `want` also the group-truncation bound
+    (a tolerance model: groups of `hgroup` consecutive products, products
+    below 2^(e_max - hbits) of the group's largest may be lost)."""
     keep = []
     g = _gemm_args(A, a_fmt, a_scaling, a_sinv, B, b_fmt, b_scaling, b_sinv, keep)
     ms = np.arange(g.M, dtype=np.int64) if ms is None else _c(ms, np.int64)
@@ -315,10 +321,12 @@ def gemm(A, a_fmt, a_scaling, a_sinv, B, b_fmt, b_scaling, b_sinv, ms=None, ns=N
     E = np.empty((ms.size, ns.size), np.float64) if "E" in want else None
     F = np.empty((ms.size, ns.size), np.float32) if "F" in want else None
     D = np.empty((ms.size, ns.size), np.float64) if "D" in want else None
-    lib().o_gemm(C.byref(g), _p(ms), ms.size, _p(ns), ns.size,
-                 _p(E) if E is not None else None, _p(F) if F is not None else None,
-                 _p(D) if D is not None else None, nthreads())
-    return {"E": E, "F": F, "D": D}
+    H = np.empty((ms.size, ns.size), np.float64) if "H" in want else None
+    lib().o_gemm_h(C.byref(g), _p(ms), ms.size, _p(ns), ns.size,
+                   _p(E) if E is not None else None, _p(F) if F is not None else None,
+                   _p(D) if D is not None else None, _p(H) if H is not None else None,
+                   hgroup, hbits, nthreads())
+    return {"E": E, "F": F, "D": D, "H": H}
 
 
 def gemm_ref_bound(A, a_fmt, a_scaling, a_sinv, B, b_fmt, b_scaling, b_sinv,

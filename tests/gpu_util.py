@@ -57,9 +57,9 @@ def bf16_half_ulp(f: np.ndarray) -> np.ndarray:
 
 
 def gemm_gate(G: np.ndarray, F: np.ndarray, D: np.ndarray, bf16: bool, tol: float = 1e-3):
-    """GPU result G against the oracle's FP32-accumulated F with magnitude D:
-    rel = |G - F| / max(|F|, D/64) <= tol (plus half a bf16 ulp of F for BF16
-    outputs).  Returns (ok, max_rel, n_floored)."""
+    """Strict gate: rel = |G - F| / max(|F|, D/64) <= tol (less half a bf16
+    ulp of F for BF16 outputs).  For data the matrix unit sums exactly.
+    Returns (ok, max_rel, n_floored)."""
     G = G.astype(np.float64)
     Fd = F.astype(np.float64)
     floor = np.maximum(np.abs(Fd), D / 64.0)
@@ -69,3 +69,31 @@ def gemm_gate(G: np.ndarray, F: np.ndarray, D: np.ndarray, bf16: bool, tol: floa
     with np.errstate(invalid="ignore", divide="ignore"):
         rel = np.where(floor > 0, err / floor, np.where(err == 0, 0.0, np.inf))
     return bool(np.all(rel <= tol)), float(np.max(rel)) if rel.size else 0.0, int(np.sum(np.abs(Fd) < D / 64.0))
+
+
+def gemm_check(G: np.ndarray, ref: dict, K: int, bf16: bool, tol: float = 1e-3):
+    """General gate for any data, two conditions on every element:
+      (1) |G - F| <= tol * D            (relative error against sum |a^ b^|,
+                                         less half a bf16 ulp for BF16 out);
+      (2) |G - E| <= H + gamma * D + u_out |G|: the matrix unit's own
+          summation model (products below 2^(e_max-13) of their group of 8
+          may be lost), binary32 combination of the K/8 group sums
+          (gamma_{K/8+3} with 2^-23 per operation), and the output rounding.
+    Returns (ok1, ok2, max componentwise rel, max ratio to the model bound)."""
+    G = G.astype(np.float64)
+    F = ref["F"].astype(np.float64)
+    E, D, H = ref["E"], ref["D"], ref["H"]
+    e1 = np.abs(G - F)
+    if bf16:
+        e1 = np.maximum(e1 - bf16_half_ulp(ref["F"]), 0.0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        r1 = np.where(D > 0, e1 / D, np.where(e1 == 0, 0.0, np.inf))
+    j = K / 8 + 3
+    gam = j * 2.0 ** -23 / (1 - j * 2.0 ** -23)
+    bound = H + gam * D + (2.0 ** -8 if bf16 else 0.0) * np.abs(G)
+    e2 = np.abs(G - E)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        r2 = np.where(bound > 0, e2 / bound, np.where(e2 == 0, 0.0, np.inf))
+    m1 = float(np.max(r1)) if r1.size else 0.0
+    m2 = float(np.max(r2)) if r2.size else 0.0
+    return m1 <= tol, m2 <= 1.0, m1, m2

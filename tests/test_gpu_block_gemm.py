@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from fp8_mixed_precision_linear_amd import datagen
-from tests.gpu_util import Guarded, dev, dev_bf16, gemm_gate, host_u16, say
+from tests.gpu_util import Guarded, dev, dev_bf16, gemm_check, gemm_gate, host_u16, say
 
 pytestmark = pytest.mark.gpu
 
@@ -128,7 +128,46 @@ def test_gemm_random_codes(O, L, shape, mode, fmts, out_f32):
     sa = rand_scales(rng, asc, M, K)
     sb = rand_scales(rng, bsc, N, K)
     G, raw, am = run_gemm(L, A, af, asc, sa, B, bf, bsc, sb, out_f32)
-    ref = O.gemm(A, af, asc, sa, B, bf, bsc, sb)
+    ref = O.gemm(A, af, asc, sa, B, bf, bsc, sb, want=("E", "F", "D", "H"))
+    ok1, ok2, m1, m2 = gemm_check(G, ref, K, bf16=not out_f32)
+    assert ok1 and ok2, f"componentwise rel {m1:.3e}, model-bound ratio {m2:.3f}"
+    assert bits(am) == bits(amax_of_output(raw, out_f32))
+
+
+def narrow_codes(rng, shape, fmt):
+    """Codes whose magnitudes lie in [1, 8): every product of two such
+    values is a multiple of 2^-6 below 64, so a group of 8 never loses a
+    bit to the matrix unit's alignment: the block sums are exact."""
+    if fmt == 0:
+        e = rng.integers(7, 10, size=shape)        # E4M3 exponent field 7..9 -> 1..<8
+        m = rng.integers(0, 8, size=shape)
+        c = (e << 3) | m
+    else:
+        e = rng.integers(15, 18, size=shape)       # E5M2 exponent field 15..17
+        m = rng.integers(0, 4, size=shape)
+        c = (e << 2) | m
+    sgn = rng.integers(0, 2, size=shape) << 7
+    return (c | sgn).astype(np.uint8)
+
+
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("fmts", [(0, 0), (1, 0), (0, 1)])
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_gemm_exact_band_strict(O, L, shape, mode, fmts, out_f32):
+    """Data the matrix unit sums exactly, with per-block scales spread over
+    16 binades: the strict 1e-3 gate (floor D/64) must hold everywhere."""
+    M, N, K = shape
+    af, bf = fmts
+    asc, bsc = mode
+    say("gemm strict", shape, mode, fmts, out_f32)
+    rng = np.random.default_rng(M * 5 + N * 11 + K + 7 * asc + bsc + 3 * af + bf)
+    A = narrow_codes(rng, (M, K), af)
+    B = narrow_codes(rng, (N, K), bf)
+    sa = rand_scales(rng, asc, M, K)
+    sb = rand_scales(rng, bsc, N, K)
+    G, raw, am = run_gemm(L, A, af, asc, sa, B, bf, bsc, sb, out_f32)
+    ref = O.gemm(A, af, asc, sa, B, bf, bsc, sb, want=("E", "F", "D", "H"))
     ok, mx, nfl = gemm_gate(G, ref["F"], ref["D"], bf16=not out_f32)
     assert ok, f"max rel err {mx} (floored {nfl})"
     assert bits(am) == bits(amax_of_output(raw, out_f32))
@@ -148,9 +187,9 @@ def test_gemm_tensor_ragged_k(O, L, shape):
         if K == 0:
             assert np.all(G == 0) and am == 0
             continue
-        ref = O.gemm(A, 0, 0, sa, B, 1, 0, sb)
-        ok, mx, _ = gemm_gate(G, ref["F"], ref["D"], bf16=not out_f32)
-        assert ok, mx
+        ref = O.gemm(A, 0, 0, sa, B, 1, 0, sb, want=("E", "F", "D", "H"))
+        ok1, ok2, m1, m2 = gemm_check(G, ref, K, bf16=not out_f32)
+        assert ok1 and ok2, (m1, m2)
 
 
 def test_gemm_accumulate_fp32(O, L):
@@ -162,10 +201,13 @@ def test_gemm_accumulate_fp32(O, L):
     sa, sb = rand_scales(rng, 1, M, K), rand_scales(rng, 1, N, K)
     prev = rng.standard_normal((M, N)).astype(np.float32) * np.float32(100)
     G, raw, am = run_gemm(L, A, 0, 1, sa, B, 1, 1, sb, True, accumulate=prev)
-    ref = O.gemm(A, 0, 1, sa, B, 1, 1, sb)
-    want = ref["F"].astype(np.float64) + prev
-    floor = np.maximum(np.abs(want), (ref["D"] + np.abs(prev)) / 64)
-    assert np.max(np.abs(G - want) / floor) <= 1e-3
+    ref = O.gemm(A, 0, 1, sa, B, 1, 1, sb, want=("E", "F", "D", "H"))
+    shifted = dict(ref)
+    shifted["F"] = (ref["F"].astype(np.float64) + prev).astype(np.float32)
+    shifted["E"] = ref["E"] + prev
+    shifted["D"] = ref["D"] + np.abs(prev)
+    ok1, ok2, m1, m2 = gemm_check(G, shifted, K, bf16=False)
+    assert ok1 and ok2, (m1, m2)
     assert bits(am) == bits(amax_of_output(raw, True))
 
 
@@ -190,9 +232,9 @@ def test_gemm_quantised_data_vs_unquantised_reference(O, L, mode):
         B, bsc, sb = gb["y"], 2 if mode == "block" else 1, gb["sinv"]
     for out_f32 in (False, True):
         G, raw, am = run_gemm(L, A, 0, asc, sa, B, 0, bsc, sb, out_f32)
-        ref = O.gemm(A, 0, asc, sa, B, 0, bsc, sb)
-        ok, mx, _ = gemm_gate(G, ref["F"], ref["D"], bf16=not out_f32)
-        assert ok, mx
+        ref = O.gemm(A, 0, asc, sa, B, 0, bsc, sb, want=("E", "F", "D", "H"))
+        ok1, ok2, m1, m2 = gemm_check(G, ref, K, bf16=not out_f32)
+        assert ok1 and ok2, (m1, m2)
         R, Bd = O.gemm_ref_bound(A, 0, asc, sa, B, 0, bsc, sb, a16, b16)
         u_out = 2.0 ** -8 if not out_f32 else 0.0
         assert np.all(np.abs(G - R) <= Bd + u_out * np.abs(G))

@@ -183,3 +183,36 @@ def test_bf16_output_rounding(O):
     bits = O.f32_to_bf16(x)
     assert list(bits) == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020, 0x7F80]
     assert np.array_equal(bits, datagen.bf16_bits(x))
+
+
+def test_group_truncation_bound_covers_a_simulated_unit(O):
+    """H bounds the error of a summation unit that truncates, in each group
+    of 8 consecutive products, everything below 2^(e_max - 13) toward zero:
+    simulate that unit exactly in Python (integers) and compare."""
+    rng = np.random.default_rng(41)
+    M, N, K = 6, 5, 256
+    for af, bf in [(0, 0), (1, 0)]:
+        A = rand_codes(rng, (M, K), af)
+        B = rand_codes(rng, (N, K), bf)
+        sa = np.array([1.0], np.float32)
+        sb = np.array([1.0], np.float32)
+        r = O.gemm(A, af, 0, sa, B, bf, 0, sb, want=("E", "D", "H"))
+        qa, qb = (9 if af == 0 else 16), (9 if bf == 0 else 16)
+        ia = np.round(O.decode(A, af) * 2.0 ** qa).astype(object)
+        ib = np.round(O.decode(B, bf) * 2.0 ** qb).astype(object)
+        worst = 0.0
+        for m in range(M):
+            for n in range(N):
+                tot = 0
+                for g0 in range(0, K, 8):
+                    p = [int(ia[m, k]) * int(ib[n, k]) for k in range(g0, g0 + 8)]
+                    mx = max(abs(v) for v in p)
+                    if mx == 0:
+                        continue
+                    grid = 1 << max(0, mx.bit_length() - 1 - 13)
+                    tot += sum((abs(v) // grid) * grid * (1 if v >= 0 else -1) for v in p)
+                sim = tot / 2.0 ** (qa + qb)
+                err = abs(sim - r["E"][m, n])
+                assert err <= r["H"][m, n] * (1 + 1e-12)
+                worst = max(worst, err / r["H"][m, n] if r["H"][m, n] else 0)
+        assert worst > 0.05   # the bound is not vacuous
