@@ -33,7 +33,7 @@ def hipcc() -> str:
 def device_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
+            "-Wall", "-Wno-unused-function", "-Wno-inline-asm", "-I", os.path.join(ROOT, "include")]
 
 
 def sources():

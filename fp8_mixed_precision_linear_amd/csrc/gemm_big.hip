@@ -1,0 +1,336 @@
+// gemm_big.hip -- the large-tile FP8 scaled GEMM for gfx950 (the main path).
+//
+// Same contract as k_gemm in gemm_kernels.hip (see there and the C ABI):
+// D = A . B^T, K-contiguous FP8 operands, FP32 accumulation; tensor scales
+// in the epilogue, block scales promoted per 128-wide K block.
+// [MPG] = "Mixed Precision LLM Training: The Complete Guide",
+//   "Skipping the BAcc accumulator promotion", "DeepSeek FP8 training recipe
+//   in detail > Block-wise scaling at 128 granularity" and "> Mixed-precision
+//   accumulation".
+//
+// Layout of one workgroup (512 threads, 8 wavefronts):
+//   output tile 256 x 256; wavefront w owns rows 128*(w/4).., columns
+//   64*(w%4).. (8 x 4 MFMA tiles of 16x16, one v_mfma_f32_16x16x128 per tile
+//   per 128-wide K block);
+//   K loop in 128-byte steps through two LDS stages of 66 KB (A 32 KB, B
+//   32 KB, 1 KB of row scales for each 1x128 operand);
+//   operands move global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+//   staging).  A lane's 16 bytes land at a fixed LDS slot, so the XOR
+//   swizzle (16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 7),
+//   which spreads the sixteen rows of one ds_read_b128 pass over sixteen
+//   bank groups) is applied by choosing which global chunk each lane
+//   fetches.  Buffer loads past the end of an operand return zeros, which
+//   covers the M / N / K tails without branches.
+//   The prefetch is issued from inline assembly: the compiler then neither
+//   waits for it before reading the other stage nor keeps it ordered with
+//   anything else; each step ends with an explicit vmcnt(0) and a barrier.
+//   Inside the loop there is no other vector-memory access: per-K-block
+//   scales come from LDS (1x128 rows arrive with the operands; per-tensor and
+//   128x128 scales sit in a per-wavefront table filled before the loop).
+// Workgroup order: the hardware hands consecutive workgroups to the 8 XCDs in
+// turn; ids are remapped so each XCD gets a contiguous run of tiles, taken
+// 8 tile-rows at a time, so the A and B panels a tile needs sit in that
+// XCD's L2.
+#include "fp8_device.h"
+#include "launch.h"
+
+namespace fp8lin {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int THREADS = 512, NWAVES = 8;
+constexpr int WTM = 128, WTN = 64;       // wavefront tile
+constexpr int TI = WTM / 16, TJ = WTN / 16;
+constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+constexpr int SA_OFF = A_BYTES + B_BYTES;
+constexpr int SB_OFF = SA_OFF + BM * 4;
+constexpr int STAGE = SB_OFF + BN * 4;
+constexpr int MAX_KB = 512;              // per-wavefront scale table: K <= 65536
+constexpr int GROUP_M = 8;
+constexpr uint32_t kOOB = 0x7FFFFFF0u;   // a buffer offset past any operand
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <int AF, int BF>
+__device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// Raw buffer resource (wave-uniform): base, no stride, `bytes` records.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(a & 0xFFFFFFFFu));
+  r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = kRsrcWord3;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)p));
+}
+
+// 16 bytes per lane from buffer offset `off` into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(uint32_t m0, uint32_t off, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(off), "s"(rsrc) : "memory", "m0");
+}
+// 4 bytes per lane into LDS at m0 + 4 * lane.
+__device__ __forceinline__ void dma4(uint32_t m0, uint32_t off, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(off), "s"(rsrc) : "memory", "m0");
+}
+
+// 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ v8i frag(const uint8_t* tile, int row, int g) {
+  const int sw = swz(row);
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * BK + (((2 * g) ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * BK + (((2 * g + 1) ^ sw) << 4));
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// BLOCK : block-mode promotion per 128-wide K block;
+// SA_ROWS: A has 1x128 scales (one per row and K block), else one per wave;
+// SB_COL : B has 1x128 scales (one per column and K block), else one per wave.
+template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL>
+__global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
+  __shared__ float su_tab[NWAVES][MAX_KB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int nk = (int)((K + BK - 1) / BK);
+
+  // ---- tile id: contiguous runs per XCD, grouped by 8 tile-rows
+  const int nblk = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int group = bid / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int in_group = bid - group * GROUP_M * tiles_n;
+  const int tm = first_m + in_group % gm, tn = in_group / gm;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int64_t rows_a = min((int64_t)BM, M - m0), rows_b = min((int64_t)BN, N - n0);
+  const i32x4 ra = make_rsrc(p.A + m0 * p.lda, (uint32_t)(rows_a * p.lda));
+  const i32x4 rb = make_rsrc(p.B + n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
+  const int lda = (int)p.lda, ldb = (int)p.ldb;
+  const int lrow = 32 * wave + (lane >> 3);
+
+  // ---- per-wavefront table of the uniform part of each K block's scale
+  if constexpr (BLOCK && !(SA_ROWS && SB_COL)) {
+    const int64_t mb = min((m0 + wm * WTM) / 128, (M + 127) / 128 - 1);
+    const int64_t nb = min((n0 + wn * WTN) / 128, (N + 127) / 128 - 1);
+    for (int kb = lane; kb < nk; kb += 64) {
+      float s = 1.0f;
+      if constexpr (!SA_ROWS)
+        s = p.a_scaling == 0 ? p.a_sinv[0] : p.a_sinv[kb * ((M + 127) / 128) + mb];
+      if constexpr (!SB_COL)
+        s *= p.b_scaling == 0 ? p.b_sinv[0] : p.b_sinv[kb * ((N + 127) / 128) + nb];
+      su_tab[wave][kb] = s;
+    }
+  }
+
+  auto load_stage = [&](int kb, uint8_t* base) {
+    const int k0 = kb * BK;
+    const uint32_t lb = lds_addr(base);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = lrow + 8 * it;
+      const int kc = k0 + 16 * ((lane & 7) ^ swz(row));
+      const bool kin = kc < (int)K;
+      const uint32_t oa = kin ? (uint32_t)(row * lda + kc) : kOOB;
+      const uint32_t ob = kin ? (uint32_t)(row * ldb + kc) : kOOB;
+      dma16(lb + (32 * wave + 8 * it) * BK, oa, ra);
+      dma16(lb + A_BYTES + (32 * wave + 8 * it) * BK, ob, rb);
+    }
+    if constexpr (BLOCK && SA_ROWS) {
+      if (wave == 0) {   // 256 row scales of this K block
+        const i32x4 rs = make_rsrc(p.a_sinv + (int64_t)kb * M + m0, (uint32_t)(rows_a * 4));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dma4(lb + SA_OFF + q * 256, (uint32_t)(q * 256 + lane * 4), rs);
+      }
+    }
+    if constexpr (BLOCK && SB_COL) {
+      if (wave == 1) {   // 256 column scales of this K block
+        const i32x4 rs = make_rsrc(p.b_sinv + (int64_t)kb * N + n0, (uint32_t)(rows_b * 4));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dma4(lb + SB_OFF + q * 256, (uint32_t)(q * 256 + lane * 4), rs);
+      }
+    }
+  };
+
+  v4f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  load_stage(0, lds[0]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int kb = 0; kb < nk; ++kb) {
+    const int stage = kb & 1;
+    if (kb + 1 < nk) load_stage(kb + 1, lds[stage ^ 1]);
+    const uint8_t* As = lds[stage];
+    const uint8_t* Bs = As + A_BYTES;
+
+    v8i bfr[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) bfr[j] = frag(Bs, wn * WTN + 16 * j + l16, g);
+
+    if constexpr (BLOCK) {
+      float scol[TJ];
+      if constexpr (SB_COL) {
+        const float* sb = reinterpret_cast<const float*>(As + SB_OFF);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) scol[j] = sb[wn * WTN + 16 * j + l16];
+      }
+      float suni = 1.0f;
+      if constexpr (!(SA_ROWS && SB_COL)) suni = su_tab[wave][kb];
+      // one row-tile at a time: the next A fragment is read while this
+      // tile's MFMAs run; each MFMA's block partial is promoted right after
+      // the next MFMA is issued; the scheduling barrier bounds live ranges.
+      v8i a_cur = frag(As, wm * WTM + l16, g);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        v8i a_nxt = a_cur;
+        if (i + 1 < TI) a_nxt = frag(As, wm * WTM + 16 * (i + 1) + l16, g);
+        float srow[4];
+        if constexpr (SA_ROWS) {
+          const float4 sv =
+              *reinterpret_cast<const float4*>(As + SA_OFF + (wm * WTM + 16 * i + 4 * g) * 4);
+          srow[0] = sv.x; srow[1] = sv.y; srow[2] = sv.z; srow[3] = sv.w;
+          if constexpr (!SB_COL) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) srow[r] *= suni;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) srow[r] = suni;
+        }
+        v4f prev = mfma<AF, BF>(a_cur, bfr[0], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          v4f cur = prev;
+          if (j + 1 < TJ) cur = mfma<AF, BF>(a_cur, bfr[j + 1], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (SB_COL)
+              acc[i][j][r] = __builtin_fmaf(prev[r] * srow[r], scol[j], acc[i][j][r]);
+            else
+              acc[i][j][r] = __builtin_fmaf(prev[r], srow[r], acc[i][j][r]);
+          }
+          prev = cur;
+        }
+        a_cur = a_nxt;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const v8i afr = frag(As, wm * WTM + 16 * i + l16, g);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma<AF, BF>(afr, bfr[j], acc[i][j]);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  float sa = 1.0f, sb = 1.0f;
+  if constexpr (!BLOCK) {
+    sa = p.a_sinv[0];
+    sb = p.b_sinv[0];
+  }
+  const int64_t mrow0 = m0 + wm * WTM + 4 * g;
+  const int64_t ncol0 = n0 + wn * WTN + l16;
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = mrow0 + 16 * i + r, n = ncol0 + 16 * j;
+        if (m >= M || n >= N) continue;
+        float v = acc[i][j][r];
+        if constexpr (!BLOCK) v = (v * sa) * sb;
+        if (p.d_f32) {
+          float* d = reinterpret_cast<float*>(p.D) + m * p.ldd + n;
+          if (p.accumulate) v = *d + v;
+          *d = v;
+          const uint32_t b = __float_as_uint(v) & 0x7FFFFFFFu;
+          amax_bits = b > amax_bits ? b : amax_bits;
+        } else {
+          const uint16_t h = f32_to_bf16_rne(v);
+          reinterpret_cast<uint16_t*>(p.D)[m * p.ldd + n] = h;
+          const uint32_t b = (uint32_t)(h & 0x7FFFu) << 16;
+          amax_bits = b > amax_bits ? b : amax_bits;
+        }
+      }
+  if (p.d_amax) {
+    amax_bits = wave_max_u32(amax_bits);
+    if (lane == 0 && amax_bits != 0u) atomic_max_bits(p.d_amax, amax_bits);
+  }
+}
+
+template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL>
+hipError_t launch_one(const GemmParams& p, hipStream_t s) {
+  auto kern = k_gemm_big<AF, BF, BLOCK, SA_ROWS, SB_COL>;
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(THREADS), 0, s, p, tiles_m,
+                     tiles_n);
+  return hipGetLastError();
+}
+
+template <int AF, int BF>
+hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
+  const bool block = !(p.a_scaling == 0 && p.b_scaling == 0);
+  if (!block) return launch_one<AF, BF, false, false, false>(p, s);
+  const bool sa = p.a_scaling == 1, sb = p.b_scaling == 1;
+  if (sa && sb) return launch_one<AF, BF, true, true, true>(p, s);
+  if (sa) return launch_one<AF, BF, true, true, false>(p, s);
+  if (sb) return launch_one<AF, BF, true, false, true>(p, s);
+  return launch_one<AF, BF, true, false, false>(p, s);
+}
+
+}  // namespace
+
+bool gemm_big_supported(const GemmParams& p) {
+  // buffer offsets are 32-bit: a 256-row panel of each operand must stay
+  // below the out-of-range marker; the scale table covers 512 K blocks
+  if ((int64_t)BM * p.lda >= (int64_t)kOOB || (int64_t)BN * p.ldb >= (int64_t)kOOB) return false;
+  if ((p.M + BM - 1) / BM * ((p.N + BN - 1) / BN) >= (int64_t)1 << 31) return false;
+  if ((p.K + BK - 1) / BK > MAX_KB) return false;
+  return true;
+}
+
+hipError_t launch_gemm_big(const GemmParams& p, hipStream_t s) {
+  if (p.a_fmt == 0 && p.b_fmt == 0) return launch_fmt<0, 0>(p, s);
+  if (p.a_fmt == 1 && p.b_fmt == 0) return launch_fmt<1, 0>(p, s);
+  if (p.a_fmt == 0 && p.b_fmt == 1) return launch_fmt<0, 1>(p, s);
+  return launch_fmt<1, 1>(p, s);
+}
+
+}  // namespace fp8lin

@@ -262,6 +262,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     hipLaunchKernelGGL(k_zero_out, dim3((unsigned)blocks), dim3(256), 0, s, p);
     return hipGetLastError();
   }
+  if (gemm_big_supported(p)) return launch_gemm_big(p, s);
   if (p.a_fmt == 0 && p.b_fmt == 0) return launch_fmt<0, 0>(p, s);
   if (p.a_fmt == 1 && p.b_fmt == 0) return launch_fmt<1, 0>(p, s);
   if (p.a_fmt == 0 && p.b_fmt == 1) return launch_fmt<0, 1>(p, s);

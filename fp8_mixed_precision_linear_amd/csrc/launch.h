@@ -46,4 +46,9 @@ struct GemmParams {
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
+// Large-tile GEMM (gemm_big.hip): used when supported (32-bit buffer offsets
+// cover a 256-row panel of each operand).
+bool gemm_big_supported(const GemmParams& p);
+hipError_t launch_gemm_big(const GemmParams& p, hipStream_t s);
+
 }  // namespace fp8lin
