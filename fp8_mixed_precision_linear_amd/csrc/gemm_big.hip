@@ -15,12 +15,18 @@
 //   K loop in 128-byte steps through two LDS stages of 66 KB (A 32 KB, B
 //   32 KB, 1 KB of row scales for each 1x128 operand);
 //   operands move global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
-//   staging).  A lane's 16 bytes land at a fixed LDS slot, so the XOR
-//   swizzle (16-byte chunk c of row r stored at chunk c ^ ((r >> 1) & 7),
-//   which spreads the sixteen rows of one ds_read_b128 pass over sixteen
-//   bank groups) is applied by choosing which global chunk each lane
-//   fetches.  Buffer loads past the end of an operand return zeros, which
-//   covers the M / N / K tails without branches.
+//   staging), one instruction per 8 rows x 128 bytes of a tile, so every
+//   global read covers whole 128-byte lines.  Tiles are row-major in LDS
+//   with 16-byte chunk c of row r stored at chunk c ^ swz(r); a lane's DMA
+//   slot is fixed, so the swizzle is applied by choosing which global chunk
+//   each lane fetches.  An MFMA operand lane l takes row l % 16 and the K
+//   chunks g and g + 4 (g = l / 16); A and B use the same assignment, so
+//   every product pairs equal k and each group of 8 consecutive register
+//   bytes holds 8 consecutive k.  With this assignment and swz(r) =
+//   ((r >> 1) & 7) ^ ((r & 1) << 2) the 16-row ds_read_b128 pattern ran
+//   about 1.6x faster than with chunk pairs {2g, 2g+1} (measured on gfx950).
+//   Buffer loads past the end of an operand return zeros, which covers the
+//   M / N / K tails without branches.
 //   The prefetch is issued from inline assembly: the compiler then neither
 //   waits for it before reading the other stage nor keeps it ordered with
 //   anything else; each step ends with an explicit vmcnt(0) and a barrier.
@@ -94,13 +100,13 @@ __device__ __forceinline__ void dma4(uint32_t m0, uint32_t off, i32x4 rsrc) {
                :: "s"(m0), "v"(off), "s"(rsrc) : "memory", "m0");
 }
 
-// 16-byte chunk c of tile row r is stored at chunk c ^ swz(r).
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
 
+// MFMA operand fragment of tile row `row` for lane group g: chunks g, g + 4.
 __device__ __forceinline__ v8i frag(const uint8_t* tile, int row, int g) {
   const int sw = swz(row);
-  const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * BK + (((2 * g) ^ sw) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * BK + (((2 * g + 1) ^ sw) << 4));
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * BK + ((g ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * BK + (((g + 4) ^ sw) << 4));
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
@@ -133,6 +139,8 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   const i32x4 ra = make_rsrc(p.A + m0 * p.lda, (uint32_t)(rows_a * p.lda));
   const i32x4 rb = make_rsrc(p.B + n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
   const int lda = (int)p.lda, ldb = (int)p.ldb;
+  // DMA: wave w fills rows 32w .. 32w+31 of A and of B, 8 rows per
+  // instruction; lane p lands in row 8*it + (p >> 3), stored chunk p & 7
   const int lrow = 32 * wave + (lane >> 3);
 
   // ---- per-wavefront table of the uniform part of each K block's scale
@@ -198,12 +206,18 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
 #pragma unroll
     for (int j = 0; j < TJ; ++j) bfr[j] = frag(Bs, wn * WTN + 16 * j + l16, g);
 
+    // The MFMA takes B as its first operand, so each 16x16 result tile is
+    // the transpose of the D tile: lane (g, l16) holds D row 16*i + l16,
+    // columns 16*j + 4*g .. +3 -- four consecutive outputs of one row.
     if constexpr (BLOCK) {
-      float scol[TJ];
+      float scol[TJ][4];
       if constexpr (SB_COL) {
-        const float* sb = reinterpret_cast<const float*>(As + SB_OFF);
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) scol[j] = sb[wn * WTN + 16 * j + l16];
+        for (int j = 0; j < TJ; ++j) {
+          const float4 sv =
+              *reinterpret_cast<const float4*>(As + SB_OFF + (wn * WTN + 16 * j + 4 * g) * 4);
+          scol[j][0] = sv.x; scol[j][1] = sv.y; scol[j][2] = sv.z; scol[j][3] = sv.w;
+        }
       }
       float suni = 1.0f;
       if constexpr (!(SA_ROWS && SB_COL)) suni = su_tab[wave][kb];
@@ -215,30 +229,22 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
       for (int i = 0; i < TI; ++i) {
         v8i a_nxt = a_cur;
         if (i + 1 < TI) a_nxt = frag(As, wm * WTM + 16 * (i + 1) + l16, g);
-        float srow[4];
+        float srow = suni;
         if constexpr (SA_ROWS) {
-          const float4 sv =
-              *reinterpret_cast<const float4*>(As + SA_OFF + (wm * WTM + 16 * i + 4 * g) * 4);
-          srow[0] = sv.x; srow[1] = sv.y; srow[2] = sv.z; srow[3] = sv.w;
-          if constexpr (!SB_COL) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) srow[r] *= suni;
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) srow[r] = suni;
+          srow = reinterpret_cast<const float*>(As + SA_OFF)[wm * WTM + 16 * i + l16];
+          if constexpr (!SB_COL) srow *= suni;
         }
-        v4f prev = mfma<AF, BF>(a_cur, bfr[0], v4f{0.f, 0.f, 0.f, 0.f});
+        v4f prev = mfma<BF, AF>(bfr[0], a_cur, v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
           v4f cur = prev;
-          if (j + 1 < TJ) cur = mfma<AF, BF>(a_cur, bfr[j + 1], v4f{0.f, 0.f, 0.f, 0.f});
+          if (j + 1 < TJ) cur = mfma<BF, AF>(bfr[j + 1], a_cur, v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if constexpr (SB_COL)
-              acc[i][j][r] = __builtin_fmaf(prev[r] * srow[r], scol[j], acc[i][j][r]);
+              acc[i][j][r] = __builtin_fmaf(prev[r] * srow, scol[j][r], acc[i][j][r]);
             else
-              acc[i][j][r] = __builtin_fmaf(prev[r], srow[r], acc[i][j][r]);
+              acc[i][j][r] = __builtin_fmaf(prev[r], srow, acc[i][j][r]);
           }
           prev = cur;
         }
@@ -250,45 +256,83 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
       for (int i = 0; i < TI; ++i) {
         const v8i afr = frag(As, wm * WTM + 16 * i + l16, g);
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma<AF, BF>(afr, bfr[j], acc[i][j]);
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma<BF, AF>(bfr[j], afr, acc[i][j]);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
-  // ---- epilogue
+  // ---- epilogue: lane (g, l16) owns rows 16*i + l16 and the 4 columns
+  // 16*j + 4*g .. +3 of each (i, j): one 8-byte (BF16) or 16-byte (FP32)
+  // store each.  Tiles wholly inside D with 16-byte-alignable rows take the
+  // vector path; others store element by element with bounds checks.
   float sa = 1.0f, sb = 1.0f;
   if constexpr (!BLOCK) {
     sa = p.a_sinv[0];
     sb = p.b_sinv[0];
   }
-  const int64_t mrow0 = m0 + wm * WTM + 4 * g;
-  const int64_t ncol0 = n0 + wn * WTN + l16;
+  const int64_t mr0 = m0 + wm * WTM + l16;
+  const int64_t nc0 = n0 + wn * WTN + 4 * g;
+  const bool vec_ok = (m0 + BM <= M) && (n0 + BN <= N) && (p.ldd % 4 == 0) &&
+                      ((reinterpret_cast<uintptr_t>(p.D) & 15u) == 0);
   uint32_t amax_bits = 0;
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
+    for (int j = 0; j < TJ; ++j) {
+      const int64_t m = mr0 + 16 * i, n = nc0 + 16 * j;
+      float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = mrow0 + 16 * i + r, n = ncol0 + 16 * j;
-        if (m >= M || n >= N) continue;
-        float v = acc[i][j][r];
-        if constexpr (!BLOCK) v = (v * sa) * sb;
+        v[r] = acc[i][j][r];
+        if constexpr (!BLOCK) v[r] = (v[r] * sa) * sb;
+      }
+      if (vec_ok) {
         if (p.d_f32) {
-          float* d = reinterpret_cast<float*>(p.D) + m * p.ldd + n;
-          if (p.accumulate) v = *d + v;
-          *d = v;
-          const uint32_t b = __float_as_uint(v) & 0x7FFFFFFFu;
-          amax_bits = b > amax_bits ? b : amax_bits;
+          float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.D) + m * p.ldd + n);
+          if (p.accumulate) {
+            const float4 o = *d;
+            v[0] = o.x + v[0]; v[1] = o.y + v[1]; v[2] = o.z + v[2]; v[3] = o.w + v[3];
+          }
+          *d = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t b = __float_as_uint(v[r]) & 0x7FFFFFFFu;
+            amax_bits = b > amax_bits ? b : amax_bits;
+          }
         } else {
-          const uint16_t h = f32_to_bf16_rne(v);
-          reinterpret_cast<uint16_t*>(p.D)[m * p.ldd + n] = h;
-          const uint32_t b = (uint32_t)(h & 0x7FFFu) << 16;
-          amax_bits = b > amax_bits ? b : amax_bits;
+          uint16_t h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            h[r] = f32_to_bf16_rne(v[r]);
+            const uint32_t b = (uint32_t)(h[r] & 0x7FFFu) << 16;
+            amax_bits = b > amax_bits ? b : amax_bits;
+          }
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.D) + m * p.ldd + n) =
+              make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+        }
+      } else {
+        if (m >= M) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (n + r >= N) continue;
+          float x = v[r];
+          if (p.d_f32) {
+            float* d = reinterpret_cast<float*>(p.D) + m * p.ldd + n + r;
+            if (p.accumulate) x = *d + x;
+            *d = x;
+            const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;
+            amax_bits = b > amax_bits ? b : amax_bits;
+          } else {
+            const uint16_t h = f32_to_bf16_rne(x);
+            reinterpret_cast<uint16_t*>(p.D)[m * p.ldd + n + r] = h;
+            const uint32_t b = (uint32_t)(h & 0x7FFFu) << 16;
+            amax_bits = b > amax_bits ? b : amax_bits;
+          }
         }
       }
+    }
   if (p.d_amax) {
     amax_bits = wave_max_u32(amax_bits);
     if (lane == 0 && amax_bits != 0u) atomic_max_bits(p.d_amax, amax_bits);
