@@ -18,10 +18,16 @@ namespace fp8lin {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;      // generic kernel
+constexpr int kBig = 1024;         // persistent kernels: one workgroup per CU
 
+// Workgroup maximum, then one device atomic per workgroup.  The casts with
+// an amax run persistent grids of one workgroup per CU: device atomics on
+// one address are serialised, so their number, not the data volume, sets
+// the cost of the reduction.
+template <int NT>
 __device__ __forceinline__ void block_amax_to(float* out, uint32_t v) {
-  __shared__ uint32_t part[kThreads / 64];
+  __shared__ uint32_t part[NT / 64];
   v = wave_max_u32(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) part[wave] = v;
@@ -29,7 +35,7 @@ __device__ __forceinline__ void block_amax_to(float* out, uint32_t v) {
   if (threadIdx.x == 0) {
     uint32_t w = part[0];
 #pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) w = w > part[i] ? w : part[i];
+    for (int i = 1; i < NT / 64; ++i) w = w > part[i] ? w : part[i];
     if (w != 0u) atomic_max_bits(out, w);
   }
 }
@@ -40,7 +46,7 @@ __device__ __forceinline__ void block_amax_to(float* out, uint32_t v) {
 // the first threads of block 0.
 // ---------------------------------------------------------------------
 template <int FMT, bool AMAX>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kBig)
     k_cast_flat(const uint16_t* __restrict__ x, int64_t n, const float* __restrict__ scale,
                 uint8_t* __restrict__ y, float* __restrict__ amax) {
   const float s = *scale;
@@ -71,7 +77,7 @@ __global__ void __launch_bounds__(kThreads)
       mb = mb > t ? mb : t;
     }
   }
-  if (AMAX) block_amax_to(amax, mb);
+  if (AMAX) block_amax_to<kBig>(amax, mb);
 }
 
 // ---------------------------------------------------------------------
@@ -99,67 +105,78 @@ __device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t 
 }
 
 template <int FMT, bool AMAX, bool WANT_Y>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kBig)
     k_cast_transpose(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                      const float* __restrict__ scale, uint8_t* __restrict__ y,
-                     uint8_t* __restrict__ yt, float* __restrict__ amax) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[128 * 128];
+                     uint8_t* __restrict__ yt, float* __restrict__ amax, int tiles_c,
+                     int ntiles) {
+  // four 256-thread groups, each on its own tile and 16 KB of LDS; the grid
+  // walks the tiles row-major, four per workgroup per pass
+  __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][128 * 128];
   const float s = *scale;
-  const int t = threadIdx.x;
+  const int grp = threadIdx.x >> 8, t = threadIdx.x & 255;
+  uint8_t* lds = lds_all[grp];
   const int cg = t & 7, rg = t >> 3;
-  const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
-  const int64_t cbase = c0 + 16 * cg;
-  const bool col_ok = cbase < cols;  // cols % 16 == 0: whole 16-col group in or out
-  uint32_t w[4][4];                  // [row i][dword j]: codes of cols 4j..4j+3
+  const int per_pass = (int)gridDim.x * 4;
+  const int passes = (ntiles + per_pass - 1) / per_pass;   // uniform over the grid
   uint32_t m = 0;
+  for (int ps = 0; ps < passes; ++ps) {
+    const int tile = ps * per_pass + (int)blockIdx.x * 4 + grp;
+    const bool have = tile < ntiles;
+    const int64_t r0 = have ? (int64_t)(tile / tiles_c) * 128 : rows;
+    const int64_t c0 = have ? (int64_t)(tile % tiles_c) * 128 : cols;
+    const int64_t cbase = c0 + 16 * cg;
+    const bool col_ok = cbase < cols;  // cols % 16 == 0: whole 16-col group in or out
+    uint32_t w[4][4];                  // [row i][dword j]: codes of cols 4j..4j+3
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t r = r0 + 4 * rg + i;
-    uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-    if (col_ok && r < rows) {
-      const uint4* p = reinterpret_cast<const uint4*>(x + r * cols + cbase);
-      a = ld_nt16(p);
-      b = ld_nt16(p + 1);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + 4 * rg + i;
+      uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+      if (col_ok && r < rows) {
+        const uint4* p = reinterpret_cast<const uint4*>(x + r * cols + cbase);
+        a = ld_nt16(p);
+        b = ld_nt16(p + 1);
+      }
+      if (AMAX) {
+        m = absmax_pk(m, a.x); m = absmax_pk(m, a.y); m = absmax_pk(m, a.z); m = absmax_pk(m, a.w);
+        m = absmax_pk(m, b.x); m = absmax_pk(m, b.y); m = absmax_pk(m, b.z); m = absmax_pk(m, b.w);
+      }
+      uint2 qa = cvt8_bf16<FMT>(a, s);
+      uint2 qb = cvt8_bf16<FMT>(b, s);
+      w[i][0] = qa.x; w[i][1] = qa.y; w[i][2] = qb.x; w[i][3] = qb.y;
+      if (WANT_Y && col_ok && r < rows)
+        st_nt16(make_uint4(qa.x, qa.y, qb.x, qb.y), reinterpret_cast<uint4*>(y + r * cols + cbase));
     }
-    if (AMAX) {
-      m = absmax_pk(m, a.x); m = absmax_pk(m, a.y); m = absmax_pk(m, a.z); m = absmax_pk(m, a.w);
-      m = absmax_pk(m, b.x); m = absmax_pk(m, b.y); m = absmax_pk(m, b.z); m = absmax_pk(m, b.w);
+    // transposed dwords into LDS: column c = 16*cg + 4*j + k, rows 4*rg..+3
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t t0, t1, t2, t3;
+      transpose4x4(w[0][j], w[1][j], w[2][j], w[3][j], t0, t1, t2, t3);
+      const uint32_t tv[4] = {t0, t1, t2, t3};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = 16 * cg + 4 * j + k;
+        const int ch = rg >> 2, within = rg & 3;
+        const int phys = ch ^ ((c >> 4) & 7);
+        *reinterpret_cast<uint32_t*>(lds + c * 128 + phys * 16 + within * 4) = tv[k];
+      }
     }
-    uint2 qa = cvt8_bf16<FMT>(a, s);
-    uint2 qb = cvt8_bf16<FMT>(b, s);
-    w[i][0] = qa.x; w[i][1] = qa.y; w[i][2] = qb.x; w[i][3] = qb.y;
-    if (WANT_Y && col_ok && r < rows)
-      st_nt16(make_uint4(qa.x, qa.y, qb.x, qb.y),
-                                  reinterpret_cast<uint4*>(y + r * cols + cbase));
-  }
-  // transposed dwords into LDS: column c = 16*cg + 4*j + k, rows 4*rg..+3
+    __syncthreads();
+    // y_t rows: tile column c -> y_t row c0 + c, 16 bytes = rows 16*ch..+15
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint32_t t0, t1, t2, t3;
-    transpose4x4(w[0][j], w[1][j], w[2][j], w[3][j], t0, t1, t2, t3);
-    const uint32_t tv[4] = {t0, t1, t2, t3};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = 16 * cg + 4 * j + k;
-      const int ch = rg >> 2, within = rg & 3;
+    for (int it = 0; it < 4; ++it) {
+      const int idx = it * 256 + t;  // 0..1023
+      const int c = idx >> 3, ch = idx & 7;
       const int phys = ch ^ ((c >> 4) & 7);
-      *reinterpret_cast<uint32_t*>(lds + c * 128 + phys * 16 + within * 4) = tv[k];
+      const int64_t gc = c0 + c, gr = r0 + 16 * ch;
+      if (gc < cols && gr < rows) {
+        uint4 v = *reinterpret_cast<const uint4*>(lds + c * 128 + phys * 16);
+        st_nt16(v, (yt + gc * rows + gr));
+      }
     }
+    __syncthreads();   // the next pass overwrites the LDS tile
   }
-  __syncthreads();
-  // y_t rows: tile column c -> y_t row c0 + c, 16 bytes = rows 16*ch..+15
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = it * kThreads + t;  // 0..1023
-    const int c = idx >> 3, ch = idx & 7;
-    const int phys = ch ^ ((c >> 4) & 7);
-    const int64_t gc = c0 + c, gr = r0 + 16 * ch;
-    if (gc < cols && gr < rows) {
-      uint4 v = *reinterpret_cast<const uint4*>(lds + c * 128 + phys * 16);
-      st_nt16(v, (yt + gc * rows + gr));
-    }
-  }
-  if (AMAX) block_amax_to(amax, absmax_fold(m));
+  if (AMAX) block_amax_to<kBig>(amax, absmax_fold(m));
 }
 
 // ---------------------------------------------------------------------
@@ -187,34 +204,38 @@ __global__ void __launch_bounds__(kThreads)
       m = m > t ? m : t;
     }
   }
-  if (AMAX) block_amax_to(amax, m);
+  if (AMAX) block_amax_to<kThreads>(amax, m);
 }
 
 template <int FMT, bool AMAX>
 hipError_t launch_cast_t(const uint16_t* x, int64_t rows, int64_t cols, const float* scale,
                          uint8_t* y, uint8_t* yt, float* amax, hipStream_t s) {
   const int64_t n = rows * cols;
+  const int64_t cus = device_cu_count();
   if (yt == nullptr) {
     int64_t nu = n >> 4;
-    int64_t blocks = (nu + kThreads - 1) / kThreads;
-    if (blocks > 2048) blocks = 2048;
+    int64_t blocks = (nu + kBig - 1) / kBig;
+    if (blocks > cus) blocks = cus;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL((k_cast_flat<FMT, AMAX>), dim3((unsigned)blocks), dim3(kThreads), 0, s, x,
+    hipLaunchKernelGGL((k_cast_flat<FMT, AMAX>), dim3((unsigned)blocks), dim3(kBig), 0, s, x,
                        n, scale, y, amax);
     return hipGetLastError();
   }
-  if (rows % 16 == 0 && cols % 16 == 0) {
-    dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
+  if (rows % 16 == 0 && cols % 16 == 0 && (rows + 127) / 128 * ((cols + 127) / 128) < (1LL << 30)) {
+    const int tiles_c = (int)((cols + 127) / 128);
+    const int ntiles = (int)((rows + 127) / 128) * tiles_c;
+    int64_t blocks = (ntiles + 3) / 4;
+    if (blocks > cus) blocks = cus;
     if (y)
-      hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, true>), grid, dim3(kThreads), 0, s, x, rows,
-                         cols, scale, y, yt, amax);
+      hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, true>), dim3((unsigned)blocks), dim3(kBig), 0,
+                         s, x, rows, cols, scale, y, yt, amax, tiles_c, ntiles);
     else
-      hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, false>), grid, dim3(kThreads), 0, s, x, rows,
-                         cols, scale, y, yt, amax);
+      hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, false>), dim3((unsigned)blocks), dim3(kBig),
+                         0, s, x, rows, cols, scale, y, yt, amax, tiles_c, ntiles);
     return hipGetLastError();
   }
   int64_t blocks = (n + kThreads - 1) / kThreads;
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > cus) blocks = cus;
   hipLaunchKernelGGL((k_cast_generic<FMT, AMAX>), dim3((unsigned)blocks), dim3(kThreads), 0, s, x,
                      rows, cols, scale, y, yt, amax);
   return hipGetLastError();

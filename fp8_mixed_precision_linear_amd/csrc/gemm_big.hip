@@ -37,6 +37,8 @@
 // turn; ids are remapped so each XCD gets a contiguous run of tiles, taken
 // 8 tile-rows at a time, so the A and B panels a tile needs sit in that
 // XCD's L2.
+#include <type_traits>
+
 #include "fp8_device.h"
 #include "launch.h"
 
@@ -263,61 +265,98 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     __syncthreads();
   }
 
-  // ---- epilogue: lane (g, l16) owns rows 16*i + l16 and the 4 columns
-  // 16*j + 4*g .. +3 of each (i, j): one 8-byte (BF16) or 16-byte (FP32)
-  // store each.  Tiles wholly inside D with 16-byte-alignable rows take the
-  // vector path; others store element by element with bounds checks.
+  // ---- epilogue.  Lane (g, l16) holds, for each (i, j), D row 16*i + l16,
+  // columns 16*j + 4*g .. +3 of the wavefront's 128 x 64 tile.  Tiles wholly
+  // inside D with 16-byte-aligned rows are staged through LDS (each
+  // wavefront owns 16 KB of the freed operand stages: 16-byte chunk c of
+  // tile row r sits at chunk c ^ (r & 7)) and leave as whole rows, 16 bytes
+  // per lane: one 128-byte line per tile row for BF16, two for FP32 (FP32
+  // goes in two passes of 64 rows).  Other tiles store element by element
+  // with bounds checks.
   float sa = 1.0f, sb = 1.0f;
   if constexpr (!BLOCK) {
     sa = p.a_sinv[0];
     sb = p.b_sinv[0];
   }
-  const int64_t mr0 = m0 + wm * WTM + l16;
-  const int64_t nc0 = n0 + wn * WTN + 4 * g;
-  const bool vec_ok = (m0 + BM <= M) && (n0 + BN <= N) && (p.ldd % 4 == 0) &&
+  const int esz = p.d_f32 ? 4 : 2;
+  const bool staged = (m0 + BM <= M) && (n0 + BN <= N) && ((p.ldd * esz) % 16 == 0) &&
                       ((reinterpret_cast<uintptr_t>(p.D) & 15u) == 0);
   uint32_t amax_bits = 0;
+  if (staged) {
+    __syncthreads();   // every wavefront is done reading both stages
+    uint8_t* wl = &lds[0][0] + wave * 16384;
+    auto epi = [&](auto f32tag) {
+      constexpr bool F32 = decltype(f32tag)::value;
+      constexpr int ES = F32 ? 4 : 2;
+      constexpr int ROWS_PASS = F32 ? 64 : 128;
+      constexpr int ROW_BYTES = WTN * ES;
+      constexpr int LANES_ROW = ROW_BYTES / 16;
+      constexpr int ROWS_INST = 64 / LANES_ROW;
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+      for (int pass = 0; pass < WTM / ROWS_PASS; ++pass) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int64_t m = mr0 + 16 * i, n = nc0 + 16 * j;
-      float v[4];
+        for (int i = 0; i < TI; ++i) {
+          if ((16 * i) / ROWS_PASS != pass) continue;
+          const int r = 16 * i + l16 - pass * ROWS_PASS;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v[r] = acc[i][j][r];
-        if constexpr (!BLOCK) v[r] = (v[r] * sa) * sb;
-      }
-      if (vec_ok) {
-        if (p.d_f32) {
-          float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.D) + m * p.ldd + n);
-          if (p.accumulate) {
-            const float4 o = *d;
-            v[0] = o.x + v[0]; v[1] = o.y + v[1]; v[2] = o.z + v[2]; v[3] = o.w + v[3];
+          for (int j = 0; j < TJ; ++j) {
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = BLOCK ? acc[i][j][q] : (acc[i][j][q] * sa) * sb;
+            const int byte = (16 * j + 4 * g) * ES;
+            uint8_t* dst = wl + r * ROW_BYTES + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
+            if constexpr (F32) {
+              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              const uint32_t h0 = f32_to_bf16_rne(v[0]), h1 = f32_to_bf16_rne(v[1]);
+              const uint32_t h2 = f32_to_bf16_rne(v[2]), h3 = f32_to_bf16_rne(v[3]);
+              *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+            }
           }
-          *d = make_float4(v[0], v[1], v[2], v[3]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t b = __float_as_uint(v[r]) & 0x7FFFFFFFu;
-            amax_bits = b > amax_bits ? b : amax_bits;
-          }
-        } else {
-          uint16_t h[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            h[r] = f32_to_bf16_rne(v[r]);
-            const uint32_t b = (uint32_t)(h[r] & 0x7FFFu) << 16;
-            amax_bits = b > amax_bits ? b : amax_bits;
-          }
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.D) + m * p.ldd + n) =
-              make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
         }
-      } else {
+        // read back whole rows (same wavefront: LDS operations stay in order)
+        const int q = lane % LANES_ROW, rr = lane / LANES_ROW;
+#pragma unroll 4
+        for (int t = 0; t < ROWS_PASS / ROWS_INST; ++t) {
+          const int r = t * ROWS_INST + rr;
+          uint4 w = *reinterpret_cast<const uint4*>(wl + r * ROW_BYTES + ((q ^ (r & 7)) << 4));
+          const int64_t gm = m0 + wm * WTM + pass * ROWS_PASS + r;
+          uint8_t* gp = reinterpret_cast<uint8_t*>(p.D) + (gm * p.ldd + n0 + wn * WTN) * ES + q * 16;
+          if constexpr (F32) {
+            if (p.accumulate) {
+              const float4 o = *reinterpret_cast<const float4*>(gp);
+              w.x = __float_as_uint(o.x + __uint_as_float(w.x));
+              w.y = __float_as_uint(o.y + __uint_as_float(w.y));
+              w.z = __float_as_uint(o.z + __uint_as_float(w.z));
+              w.w = __float_as_uint(o.w + __uint_as_float(w.w));
+            }
+            const uint32_t m4[4] = {w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu, w.z & 0x7FFFFFFFu,
+                                    w.w & 0x7FFFFFFFu};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) amax_bits = m4[e] > amax_bits ? m4[e] : amax_bits;
+          } else {
+            const uint32_t m = absmax_fold(absmax_pk(absmax_pk(absmax_pk(absmax_pk(0u, w.x), w.y), w.z), w.w));
+            amax_bits = m > amax_bits ? m : amax_bits;
+          }
+          *reinterpret_cast<uint4*>(gp) = w;
+        }
+      }
+    };
+    if (p.d_f32) epi(std::true_type{});
+    else epi(std::false_type{});
+  } else {
+    const int64_t mr0 = m0 + wm * WTM + l16;
+    const int64_t nc0 = n0 + wn * WTN + 4 * g;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int64_t m = mr0 + 16 * i, n = nc0 + 16 * j;
         if (m >= M) continue;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (n + r >= N) continue;
-          float x = v[r];
+          float x = BLOCK ? acc[i][j][r] : (acc[i][j][r] * sa) * sb;
           if (p.d_f32) {
             float* d = reinterpret_cast<float*>(p.D) + m * p.ldd + n + r;
             if (p.accumulate) x = *d + x;
@@ -332,10 +371,18 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
           }
         }
       }
-    }
-  if (p.d_amax) {
+  }
+  if (p.d_amax) {   // one device atomic per workgroup
+    __shared__ uint32_t wmax[NWAVES];
     amax_bits = wave_max_u32(amax_bits);
-    if (lane == 0 && amax_bits != 0u) atomic_max_bits(p.d_amax, amax_bits);
+    if (lane == 0) wmax[wave] = amax_bits;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int w = 0; w < NWAVES; ++w) m = wmax[w] > m ? wmax[w] : m;
+      if (m != 0u) atomic_max_bits(p.d_amax, m);
+    }
   }
 }
 

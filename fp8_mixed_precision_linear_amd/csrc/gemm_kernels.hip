@@ -218,6 +218,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmParams p) {
 // Zero output for K == 0 (or leave it when accumulating).
 __global__ void k_zero_out(GemmParams p) {
   const int64_t total = p.M * p.N;
+  uint32_t amax_bits = 0;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t m = i / p.N, n = i - m * p.N;
@@ -226,11 +227,15 @@ __global__ void k_zero_out(GemmParams p) {
       if (p.d_amax) {
         const uint32_t b =
             __float_as_uint(reinterpret_cast<float*>(p.D)[m * p.ldd + n]) & 0x7FFFFFFFu;
-        if (b) atomic_max_bits(p.d_amax, b);
+        amax_bits = b > amax_bits ? b : amax_bits;
       }
     } else {
       reinterpret_cast<uint16_t*>(p.D)[m * p.ldd + n] = 0;
     }
+  }
+  if (p.d_amax) {
+    amax_bits = wave_max_u32(amax_bits);
+    if ((threadIdx.x & 63) == 0 && amax_bits != 0u) atomic_max_bits(p.d_amax, amax_bits);
   }
 }
 

@@ -8,6 +8,9 @@
 
 namespace fp8lin {
 
+// Compute units of the current device (queried once per device).
+int64_t device_cu_count();
+
 // Fill n dwords at p with v (a kernel, so it is safe inside graph capture).
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 

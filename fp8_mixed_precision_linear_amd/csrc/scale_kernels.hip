@@ -5,6 +5,8 @@
 //   "Transformer Engine internals > Per-tensor scaling" (amax -> scale),
 //   "Delayed scaling (the default recipe)", "History-based scaling",
 //   "Calibration deep dive > Dynamic calibration (delayed scaling)".
+#include <atomic>
+
 #include "fp8_device.h"
 #include "launch.h"
 
@@ -12,7 +14,7 @@ namespace fp8lin {
 
 namespace {
 
-constexpr int kAmaxThreads = 512;
+constexpr int kAmaxThreads = 1024;
 
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -109,6 +111,21 @@ inline float fmax_of(int fmt) { return fmt == 0 ? kMaxE4M3 : kMaxE5M2; }
 
 }  // namespace
 
+int64_t device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+    v = 256;
+  if (dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
@@ -121,11 +138,12 @@ hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t s)
   hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 1, 0u, s);
   if (e != hipSuccess || n == 0) return e;
   int64_t nv = n >> 3;
-  // enough blocks to keep every CU streaming: 2 blocks of 512 per CU on a
-  // 256-CU part, fewer for small tensors.
+  // a persistent grid of at most one 1024-thread workgroup per CU: each
+  // workgroup ends in one device atomic on the result, and those atomics
+  // are serialised, so the grid is kept no larger than streaming needs.
   int64_t blocks = (nv + 2 * kAmaxThreads - 1) / (2 * kAmaxThreads);
   if (blocks < 1) blocks = 1;
-  if (blocks > 1024) blocks = 1024;
+  if (blocks > device_cu_count()) blocks = device_cu_count();
   hipLaunchKernelGGL(k_amax, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, s, x, n, amax);
   return hipGetLastError();
 }
