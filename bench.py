@@ -7,11 +7,14 @@ resident in HBM before timing.  One step = the whole hot path:
   cast X -> E4M3 (+transpose, +amax), cast W -> E4M3 (+transpose, +amax),
   FWD GEMM (bf16 Y), cast dY -> E5M2 (+transpose, +amax), DGRAD GEMM (bf16
   dX), WGRAD GEMM (fp32 dW), amax-history update (len 16, max) for X, W, dY.
-`value` = GEMM FLOPs of the step (3 x 2*4096^3) / measured step time.
+`value` = GEMM FLOPs of the step (3 x 2*4096^3) / measured step time, with
+the K timed steps captured once into a HIP graph and replayed (the eager
+per-call time is reported beside it as ms_per_step_eager).
 
 Also reported (same JSON line):
   roofline      -- the dominant kernel (the GEMMs), per-launch duration from
-                   HIP events around repeated launches on the library's stream;
+                   HIP events around R launches captured in a HIP graph, on
+                   the stream the kernels run on;
   kernels       -- per-kernel throughput (GEMM TFLOP/s, cast GB/s of
                    algorithmic bytes) for this workload;
   blockwise     -- the block-wise path on 8192 tokens x 4096 in x 14336 out:
@@ -21,7 +24,7 @@ Also reported (same JSON line):
                    same step (rank 0, N = 1 only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--no-blockwise]
+       [--no-blockwise] [--no-graph] [--kernel-reps R]
 """
 from __future__ import annotations
 
@@ -49,6 +52,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-blockwise", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the eager launches only (default: the K steps are captured "
+                         "into one HIP graph and replayed)")
     return ap.parse_args()
 
 
@@ -105,30 +111,48 @@ def main():
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
+
+    # eager: one Python call per library entry point
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
     ev0.record(stream)
     for t in range(args.steps):
         step(args.warmup + t)
     ev1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    ms_step_eager = ev0.elapsed_time(ev1) / args.steps
+
+    # graph: the same K steps captured once into a HIP graph and replayed
+    # (no host launch cost; the GPU runs the identical kernel sequence)
+    ms_step_graph = None
+    wall = None
+    if not args.no_graph:
+        g = capture(torch, lambda: [step(args.warmup + t) for t in range(args.steps)])
+        g.replay()                      # warm-up replay (first launch uploads the graph)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_step_graph = ev0.elapsed_time(ev1) / args.steps
+        del g
+    ms_step = ms_step_graph if ms_step_graph is not None else ms_step_eager
     gemm_flops = 3 * 2.0 * T * DI * DO
     value = gemm_flops / (ms_step * 1e-3) / 1e12
 
-    # ---- per-kernel timing (HIP events on the same stream, repeated launches)
+    # ---- per-kernel timing: R launches captured in a graph, one replay timed
+    # with HIP events on the stream the kernels run on
     def time_launch(fn, reps):
-        fn()
+        g = capture(torch, lambda: [fn() for _ in range(reps)])
+        g.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        for _ in range(reps):
-            fn()
+        g.replay()
         b.record(stream)
         torch.cuda.synchronize()
+        del g
         return a.elapsed_time(b) / reps * 1e-3  # seconds per launch
 
     x0, w0, dy0 = data[0]
@@ -155,7 +179,8 @@ def main():
     }
     g_avg = (k["gemm_fwd_tensor"] + k["gemm_dgrad_tensor"] + k["gemm_wgrad_tensor"]) / 3
     g_ach = 2.0 * T * DI * DO / g_avg / 1e12
-    roofline = {"bound": "mfma", "kernel": "k_gemm (per-tensor, 4096^3, fwd/dgrad/wgrad average)",
+    roofline = {"bound": "mfma",
+                "kernel": "k_gemm_big, per-tensor scales, 4096^3 (fwd/dgrad/wgrad average)",
                 "achieved": round(g_ach, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(g_ach / FP8_PEAK_TFLOPS, 4), "traffic": None}
 
@@ -168,12 +193,14 @@ def main():
         "metric": "FP8 scaled-GEMM TFLOP/s (fwd+dgrad+wgrad, % FP8 peak) + cast GB/s",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "launch": "hip_graph" if ms_step_graph is not None else "eager",
+        "ms_per_step_eager": round(ms_step_eager, 4),
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3/e5m2 (fp32 accumulate)",
         "data": "synthetic (seeded numpy PCG64, bf16)",
         "config": {"workload": "delayed-scaling FP8 linear fwd+dgrad+wgrad, tokens 4096, in 4096, "
                                "out 4096, amax history 16, inputs regenerated per step (16 steps)",
                    "global_batch": T, "seq_len": None, "parallelism": "none (1 GPU)"},
-        "wall_s_timed": round(wall, 3),
+        "wall_s_timed": round(wall, 4) if wall is not None else None,
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "roofline": roofline,
         "kernels": {n: {kk: round(vv, 2) for kk, vv in d.items()} for n, d in kernels.items()},
@@ -227,6 +254,18 @@ def bench_blockwise(torch, L, datagen, dev, stream, d_bf16, time_launch, R):
     out["fwd_bwd_tflops_incl_casts"] = round(3 * fl / tot / 1e12, 2)
     out["fwd_bwd_ms"] = round(tot * 1e3, 3)
     return out
+
+
+def capture(torch, fn):
+    """Capture fn's launches into a HIP graph (torch makes its capture stream
+    the current stream, which is the stream the binding passes to the
+    library)."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
 
 
 def cpu_baseline(gemm_flops):

@@ -79,31 +79,45 @@ __global__ void k_compute_scale(const float* __restrict__ amax, int64_t n, float
   scale_inv[i] = si;
 }
 
-// Delayed scaling: one thread per tensor shifts its history (newest first),
-// inserts the new amax, takes the window maximum (NaN propagates: compared
-// as bit patterns of non-negative values) or the newest entry, and updates
-// the scale only for a positive finite effective amax.
-__global__ void k_history_update(float* __restrict__ history, int64_t n, int64_t len,
-                                 const float* __restrict__ amax_new, float fmax, int margin,
-                                 int algo, float* __restrict__ scale,
-                                 float* __restrict__ scale_inv) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
+// Delayed scaling: one wavefront per tensor shifts its history (newest
+// first), inserts the new amax, takes the window maximum (NaN propagates:
+// compared as bit patterns of non-negative values) or the newest entry, and
+// updates the scale only for a positive finite effective amax.  The shift
+// runs over 64-entry chunks from the end backwards.  Within a chunk the one
+// store instruction consumes the value of the one load instruction, so all
+// lanes have read their source entries before any lane writes; the next
+// (lower) chunk reads only entries below the ones already written.
+__global__ void __launch_bounds__(64) k_history_update(float* __restrict__ history, int64_t n,
+                                                       int64_t len,
+                                                       const float* __restrict__ amax_new,
+                                                       float fmax, int margin, int algo,
+                                                       float* __restrict__ scale,
+                                                       float* __restrict__ scale_inv) {
+  const int64_t i = blockIdx.x;
+  const int lane = threadIdx.x;
   float* h = history + i * len;
   const float a = amax_new[i];
   uint32_t best = __float_as_uint(a);
-  for (int64_t j = len - 1; j >= 1; --j) {
-    float v = h[j - 1];
-    h[j] = v;
-    uint32_t b = __float_as_uint(v);
-    best = b > best ? b : best;
+  for (int64_t base = ((len - 1) >> 6) << 6; base >= 0; base -= 64) {
+    const int64_t j = base + lane;
+    const bool have = j >= 1 && j < len;
+    float v = 0.0f;
+    if (have) v = h[j - 1];
+    if (have) {
+      h[j] = v;
+      const uint32_t b = __float_as_uint(v);
+      best = b > best ? b : best;
+    }
   }
-  h[0] = a;
-  float eff = algo == 1 ? a : __uint_as_float(best);
-  float s, si;
-  if (scale_from_amax(eff, fmax, margin, s, si)) {
-    scale[i] = s;
-    scale_inv[i] = si;
+  best = wave_max_u32(best);
+  if (lane == 0) {
+    h[0] = a;
+    const float eff = algo == 1 ? a : __uint_as_float(best);
+    float s, si;
+    if (scale_from_amax(eff, fmax, margin, s, si)) {
+      scale[i] = s;
+      scale_inv[i] = si;
+    }
   }
 }
 
@@ -161,8 +175,8 @@ hipError_t launch_history_update(float* history, int64_t n, int64_t len, const f
                                  int fmt, int margin, int algo, float* scale, float* scale_inv,
                                  hipStream_t s) {
   if (n == 0) return hipSuccess;
-  int64_t blocks = (n + 63) / 64;
-  hipLaunchKernelGGL(k_history_update, dim3((unsigned)blocks), dim3(64), 0, s, history, n, len,
+  if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_history_update, dim3((unsigned)n), dim3(64), 0, s, history, n, len,
                      amax_new, fmax_of(fmt), margin, algo, scale, scale_inv);
   return hipGetLastError();
 }

@@ -1,0 +1,135 @@
+"""GPU: the delayed-scaling step (three casts with transpose and amax, the
+three GEMMs, two amax-history updates) captured into a HIP graph and
+replayed gives the eager results bit for bit, replay after replay, with
+eager work and synchronisations between the replays.  Every library entry
+point the step uses launches kernels only on the caller's stream (zeroing
+is done by a fill kernel, not a memset), so the captured sequence is the
+eager one.  A GEMM with a fused output amax and a block-wise cast are
+captured too."""
+import numpy as np
+import pytest
+import torch
+
+from fp8_mixed_precision_linear_amd import datagen
+from tests.gpu_util import dev_bf16, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    from fp8_mixed_precision_linear_amd import lib
+    assert torch.cuda.is_available()
+    return lib
+
+
+def _capture(fn):
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_delayed_step_graph_replay(L):
+    T, DI, DO = 512, 384, 640
+    steps = []
+    for t in range(2):
+        s = datagen.config2_step(t)
+        steps.append((dev_bf16(s["x"][:T, :DI]), dev_bf16(s["w"][:DI, :DO]), dev_bf16(s["dy"][:T, :DO])))
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    out = {
+        "xq": torch.empty((T, DI), **u8), "xtq": torch.empty((DI, T), **u8),
+        "wq": torch.empty((DI, DO), **u8), "wtq": torch.empty((DO, DI), **u8),
+        "dyq": torch.empty((T, DO), **u8), "dytq": torch.empty((DO, T), **u8),
+        "y": torch.empty((T, DO), dtype=torch.bfloat16, device="cuda"),
+        "dx": torch.empty((T, DI), dtype=torch.bfloat16, device="cuda"),
+        "dw": torch.empty((DI, DO), dtype=torch.float32, device="cuda"),
+        "hist": torch.zeros((3, 16), dtype=torch.float32, device="cuda"),
+        "scale": torch.ones(3, dtype=torch.float32, device="cuda"),
+        "sinv": torch.ones(3, dtype=torch.float32, device="cuda"),
+        "amax": torch.zeros(3, dtype=torch.float32, device="cuda"),
+    }
+    o = out
+
+    def step(t):
+        x, w, dy = steps[t]
+        L.fp8_cast_e4m3(x, o["scale"][0:1], y=o["xq"], y_t=o["xtq"], amax_out=o["amax"][0:1])
+        L.fp8_cast_e4m3(w, o["scale"][1:2], y=o["wq"], y_t=o["wtq"], amax_out=o["amax"][1:2])
+        L.fp8_scaled_gemm(o["xq"], 0, 0, o["sinv"][0:1], o["wtq"], 0, 0, o["sinv"][1:2], o["y"])
+        L.fp8_cast_e5m2(dy, o["scale"][2:3], y=o["dyq"], y_t=o["dytq"], amax_out=o["amax"][2:3])
+        L.fp8_scaled_gemm(o["dyq"], 1, 0, o["sinv"][2:3], o["wq"], 0, 0, o["sinv"][1:2], o["dx"])
+        L.fp8_scaled_gemm(o["xtq"], 0, 0, o["sinv"][0:1], o["dytq"], 1, 0, o["sinv"][2:3], o["dw"])
+        L.fp8_amax_history_update(o["hist"][0:2], o["amax"][0:2], 0, 0, 0, o["scale"][0:2], o["sinv"][0:2])
+        L.fp8_amax_history_update(o["hist"][2:3], o["amax"][2:3], 1, 0, 0, o["scale"][2:3], o["sinv"][2:3])
+
+    def run_two():
+        step(0)
+        step(1)
+
+    # a non-trivial starting state (a history and scales from one eager step)
+    step(1)
+    torch.cuda.synchronize()
+    state0 = {k: o[k].clone() for k in ("hist", "scale", "sinv")}
+
+    def reset():
+        for k, v in state0.items():
+            o[k].copy_(v)
+        for k in ("xq", "xtq", "wq", "wtq", "dyq", "dytq", "y", "dx", "dw", "amax"):
+            o[k].view(torch.uint8).fill_(0x5A)
+
+    reset()
+    run_two()
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in o.items()}
+    g = _capture(run_two)
+    for r in range(3):
+        say("graph replay", r)
+        reset()
+        # unrelated eager work on the stream between replays
+        scratch = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in want.items():
+            got = o[k]
+            assert torch.equal(got.view(torch.uint8), v.view(torch.uint8)), (r, k)
+        assert torch.isfinite(scratch)
+
+
+def test_gemm_amax_and_block_cast_graph_replay(L):
+    rng = np.random.default_rng(5)
+    M, N, K = 384, 512, 640
+    A = torch.from_numpy(rng.integers(0, 0x7E, (M, K), dtype=np.uint8)).cuda()
+    B = torch.from_numpy(rng.integers(0, 0x7E, (N, K), dtype=np.uint8)).cuda()
+    sa = torch.tensor([0.5], device="cuda")
+    sb = torch.tensor([0.25], device="cuda")
+    D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    am = torch.empty(1, dtype=torch.float32, device="cuda")
+    x = dev_bf16(datagen.bf16_bits(rng.standard_normal((256, 384)).astype(np.float32)))
+    xq, sx = torch.empty((256, 384), dtype=torch.uint8, device="cuda"), torch.empty((3, 256), device="cuda")
+    xtq, sxt = torch.empty((384, 256), dtype=torch.uint8, device="cuda"), torch.empty((2, 384), device="cuda")
+
+    def work():
+        L.fp8_scaled_gemm(A, 0, 0, sa, B, 0, 0, sb, D, d_amax=am)
+        L.fp8_cast_block(x, 0, 1, xq, sx, xtq, sxt)
+
+    outs = (D, am, xq, sx, xtq, sxt)
+
+    def clear():
+        for t in outs:
+            t.view(torch.uint8).fill_(0xC3)
+
+    clear()
+    work()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outs]
+    g = _capture(work)
+    for r in range(3):
+        clear()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (t, w) in enumerate(zip(outs, want)):
+            assert torch.equal(t.view(torch.uint8), w.view(torch.uint8)), (r, i)

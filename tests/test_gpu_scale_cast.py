@@ -73,7 +73,8 @@ def test_compute_scale(O, L, fmt, margin):
     assert np.array_equal(bits(si.cpu().numpy()), bits([w[1] for w in want]))
 
 
-@pytest.mark.parametrize("ln,algo", [(16, 0), (32, 0), (16, 1), (1, 0)])
+@pytest.mark.parametrize("ln,algo", [(16, 0), (32, 0), (16, 1), (1, 0), (63, 0), (64, 0), (65, 0),
+                                     (130, 0), (1024, 0), (1024, 1)])
 def test_history_update(O, L, ln, algo):
     say("history", ln, algo)
     rng = np.random.default_rng(ln + algo)
@@ -87,6 +88,9 @@ def test_history_update(O, L, ln, algo):
     am[11:, 4] = 2.0 ** -140     # subnormal amax: the scale clamps to FLT_MAX
     for fmt in fmts[:2]:
         h = np.zeros((n, ln), np.float32); s = np.ones(n, np.float32); si = np.ones(n, np.float32)
+        if ln > 32:   # a full window: every entry, chunk boundaries included, holds a value
+            h = (np.abs(rng.standard_normal((n, ln))) * 3).astype(np.float32)
+            h[2, ln - 2] = 500.0   # about to leave the window after one step
         hd, sd, sid = dev(h), dev(s), dev(si)
         for t in range(steps):
             L.fp8_amax_history_update(hd, dev(am[t]), fmt, 0, algo, sd, sid)
