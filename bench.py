@@ -182,7 +182,7 @@ def main():
     roofline = {"bound": "mfma",
                 "kernel": "k_gemm_big, per-tensor scales, 4096^3 (fwd/dgrad/wgrad average)",
                 "achieved": round(g_ach, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(g_ach / FP8_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(g_ach / FP8_PEAK_TFLOPS, 4), "traffic": gemm_traffic()}
 
     # ---- block-wise path at 8192 x 4096 x 14336
     blockwise = None
@@ -254,6 +254,24 @@ def bench_blockwise(torch, L, datagen, dev, stream, d_bf16, time_launch, R):
     out["fwd_bwd_tflops_incl_casts"] = round(3 * fl / tot / 1e12, 2)
     out["fwd_bwd_ms"] = round(tot * 1e3, 3)
     return out
+
+
+def gemm_traffic():
+    """HBM bytes per launch of the per-tensor 4096^3 GEMM (average of fwd,
+    dgrad, wgrad) from the committed counter summary, or None when the
+    kernel sources changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "gemm_tensor4096_traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        from fp8_mixed_precision_linear_amd.traffic_probe import sources_sha256
+        if t.get("sources_sha256") != sources_sha256():
+            return None
+        k = t["kernels"]
+        names = ("gemm_fwd_tensor", "gemm_dgrad_tensor", "gemm_wgrad_tensor")
+        return round(sum(k[n]["traffic_bytes"] for n in names) / 3)
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def capture(torch, fn):
