@@ -224,9 +224,24 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
       float suni = 1.0f;
       if constexpr (!(SA_ROWS && SB_COL)) suni = su_tab[wave][kb];
       // one row-tile at a time: the next A fragment is read while this
-      // tile's MFMAs run; each MFMA's block partial is promoted right after
-      // the next MFMA is issued; the scheduling barrier bounds live ranges.
+      // tile's MFMAs run, and the block partials of the previous row-tile
+      // are promoted while this row's MFMAs execute (their results are
+      // long ready by then); the last row is promoted after the loop.  The
+      // scheduling barrier keeps each row's MFMAs ahead of the promotion.
+      auto promote = [&](int i, const v4f (&pp)[TJ], float sr) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (SB_COL)
+              acc[i][j][r] = __builtin_fmaf(pp[j][r] * sr, scol[j][r], acc[i][j][r]);
+            else
+              acc[i][j][r] = __builtin_fmaf(pp[j][r], sr, acc[i][j][r]);
+          }
+      };
       v8i a_cur = frag(As, wm * WTM + l16, g);
+      v4f pprev[TJ];
+      float sprev = 0.0f;
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
         v8i a_nxt = a_cur;
@@ -236,23 +251,17 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
           srow = reinterpret_cast<const float*>(As + SA_OFF)[wm * WTM + 16 * i + l16];
           if constexpr (!SB_COL) srow *= suni;
         }
-        v4f prev = mfma<BF, AF>(bfr[0], a_cur, v4f{0.f, 0.f, 0.f, 0.f});
+        v4f pcur[TJ];
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          v4f cur = prev;
-          if (j + 1 < TJ) cur = mfma<BF, AF>(bfr[j + 1], a_cur, v4f{0.f, 0.f, 0.f, 0.f});
+        for (int j = 0; j < TJ; ++j) pcur[j] = mfma<BF, AF>(bfr[j], a_cur, v4f{0.f, 0.f, 0.f, 0.f});
+        if (i > 0) promote(i - 1, pprev, sprev);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if constexpr (SB_COL)
-              acc[i][j][r] = __builtin_fmaf(prev[r] * srow, scol[j][r], acc[i][j][r]);
-            else
-              acc[i][j][r] = __builtin_fmaf(prev[r], srow, acc[i][j][r]);
-          }
-          prev = cur;
-        }
+        for (int j = 0; j < TJ; ++j) pprev[j] = pcur[j];
+        sprev = srow;
         a_cur = a_nxt;
         __builtin_amdgcn_sched_barrier(0);
       }
+      promote(TI - 1, pprev, sprev);
     } else {
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
