@@ -198,6 +198,44 @@ int o_compute_scale(float amax, int fmt, int margin, float fallback,
 }
 
 /* ------------------------------------------------------------------ */
+/* Power-of-two ("exponent bias") scale.                               */
+/* [P3] abstract and reviews: the scale is an exponent bias chosen     */
+/* from the tensor's maximum (FP8-AMAX) so that its range roughly      */
+/* matches the format's.  The page does not print the formula          */
+/* (its section 2.3 is not on the page).  Reading: s = 2^e with e the  */
+/* largest integer such that amax * 2^e <= fmax (no saturation, the    */
+/* amax lands in (fmax/2, fmax]), then e -= margin, e clamped to       */
+/* [-126, 126] so s and 1/s are normal binary32 powers of two;         */
+/* scale_inv = 2^-e.  Both are exact.  Same fallback rule as           */
+/* o_compute_scale for amax == 0 or non-finite.                        */
+/* e is found by comparing mantissas after frexp (exact on doubles).   */
+/* ------------------------------------------------------------------ */
+int o_pow2_exponent(float amax, int fmt) {
+  int ea, ef;
+  double ma = frexp((double)amax, &ea);          /* amax = ma * 2^ea, ma in [0.5, 1) */
+  double mf = frexp(o_fp8_max(fmt), &ef);        /* fmax = mf * 2^ef */
+  return ma <= mf ? ef - ea : ef - ea - 1;
+}
+
+int o_compute_scale_pow2(float amax, int fmt, int margin, float fallback,
+                         float* scale, float* scale_inv) {
+  int e;
+  if (!(amax > 0.0f) || isinf(amax) || isnan(amax)) {
+    *scale = fallback;
+    *scale_inv = 1.0f / fallback;
+    return 0;
+  }
+  e = o_pow2_exponent(amax, fmt) - margin;
+  if (e > 126) e = 126;
+  if (e < -126) e = -126;
+  *scale = ldexpf(1.0f, e);
+  *scale_inv = ldexpf(1.0f, -e);
+  return 1;
+}
+
+typedef int (*scale_rule_fn)(float, int, int, float, float*, float*);
+
+/* ------------------------------------------------------------------ */
 /* Delayed scaling with an amax history.                               */
 /* [MPG] "Delayed scaling (the default recipe)": the scale used at     */
 /* step t comes from earlier steps; "History-based scaling": the scale */
@@ -214,9 +252,9 @@ static int tot_gt(float a, float b) {  /* a > b in totalOrder on magnitudes >= 0
   return b_of(a) > b_of(b);
 }
 
-void o_history_update(float* history, int64_t n, int64_t len,
-                      const float* amax_new, int fmt, int margin, int algo,
-                      float* scale, float* scale_inv) {
+static void history_update_rule(float* history, int64_t n, int64_t len,
+                                const float* amax_new, int fmt, int margin, int algo,
+                                float* scale, float* scale_inv, scale_rule_fn rule) {
   for (int64_t t = 0; t < n; ++t) {
     float* h = history + t * len;
     float eff;
@@ -229,8 +267,21 @@ void o_history_update(float* history, int64_t n, int64_t len,
       for (int64_t j = 1; j < len; ++j)
         if (tot_gt(h[j], eff)) eff = h[j];
     }
-    o_compute_scale(eff, fmt, margin, scale[t], &scale[t], &scale_inv[t]);
+    rule(eff, fmt, margin, scale[t], &scale[t], &scale_inv[t]);
   }
+}
+
+void o_history_update(float* history, int64_t n, int64_t len, const float* amax_new, int fmt,
+                      int margin, int algo, float* scale, float* scale_inv) {
+  history_update_rule(history, n, len, amax_new, fmt, margin, algo, scale, scale_inv,
+                      o_compute_scale);
+}
+
+/* The same update with the power-of-two rule (o_compute_scale_pow2). */
+void o_history_update_pow2(float* history, int64_t n, int64_t len, const float* amax_new,
+                           int fmt, int margin, int algo, float* scale, float* scale_inv) {
+  history_update_rule(history, n, len, amax_new, fmt, margin, algo, scale, scale_inv,
+                      o_compute_scale_pow2);
 }
 
 /* ------------------------------------------------------------------ */
@@ -282,8 +333,9 @@ void o_cast_transpose(const uint16_t* x, int64_t rows, int64_t cols, float s,
 /*   and sinv_t[rb * ncb + cb] (layout [ceil(rows/128)][ceil(cols/128)]). */
 /* Any of y/sinv/y_t/sinv_t may be NULL.                               */
 /* ------------------------------------------------------------------ */
-void o_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int tile,
-                  uint8_t* y, float* sinv, uint8_t* y_t, float* sinv_t) {
+static void cast_block_rule(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int tile,
+                            uint8_t* y, float* sinv, uint8_t* y_t, float* sinv_t,
+                            scale_rule_fn rule) {
   int64_t nrb = (rows + 127) / 128, ncb = (cols + 127) / 128;
   float s, si;
   if (tile == O_SCALE_1x128) {
@@ -292,7 +344,7 @@ void o_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int ti
       for (int64_t cb = 0; cb < ncb; ++cb) {
         int64_t c0 = cb * 128, c1 = c0 + 128 < cols ? c0 + 128 : cols;
         float am = o_amax_bf16(x + r * cols + c0, c1 - c0);
-        o_compute_scale(am, fmt, 0, 1.0f, &s, &si);
+        rule(am, fmt, 0, 1.0f, &s, &si);
         if (sinv) sinv[cb * rows + r] = si;
         if (y)
           for (int64_t c = c0; c < c1; ++c)
@@ -306,7 +358,7 @@ void o_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int ti
           int64_t r0 = rb * 128, r1 = r0 + 128 < rows ? r0 + 128 : rows;
           for (int64_t r = r0; r < r1; ++r) seg[r - r0] = x[r * cols + c];
           float am = o_amax_bf16(seg, r1 - r0);
-          o_compute_scale(am, fmt, 0, 1.0f, &s, &si);
+          rule(am, fmt, 0, 1.0f, &s, &si);
           if (sinv_t) sinv_t[rb * cols + c] = si;
           if (y_t)
             for (int64_t r = r0; r < r1; ++r)
@@ -323,7 +375,7 @@ void o_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int ti
           float m = o_amax_bf16(x + r * cols + c0, c1 - c0);
           if (tot_gt(m, am)) am = m;
         }
-        o_compute_scale(am, fmt, 0, 1.0f, &s, &si);
+        rule(am, fmt, 0, 1.0f, &s, &si);
         if (sinv) sinv[cb * nrb + rb] = si;
         if (sinv_t) sinv_t[rb * ncb + cb] = si;
         for (int64_t r = r0; r < r1; ++r)
@@ -334,6 +386,17 @@ void o_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int ti
           }
       }
   }
+}
+
+void o_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int tile,
+                  uint8_t* y, float* sinv, uint8_t* y_t, float* sinv_t) {
+  cast_block_rule(x, rows, cols, fmt, tile, y, sinv, y_t, sinv_t, o_compute_scale);
+}
+
+/* The same tiles with power-of-two scales (o_compute_scale_pow2). */
+void o_cast_block_pow2(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int tile,
+                       uint8_t* y, float* sinv, uint8_t* y_t, float* sinv_t) {
+  cast_block_rule(x, rows, cols, fmt, tile, y, sinv, y_t, sinv_t, o_compute_scale_pow2);
 }
 
 /* ------------------------------------------------------------------ */

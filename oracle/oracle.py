@@ -35,7 +35,9 @@ def nthreads() -> int:
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (no contraction, no fast-math, generic x86-64)."""
-    if force or not os.path.exists(_SO):
+    stale = (not os.path.exists(_SO)
+             or any(os.path.getmtime(f) > os.path.getmtime(_SO) for f in _SRCS))
+    if force or stale:
         cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fno-strict-aliasing",
                "-Wall", "-pthread", "-shared", "-fPIC", *_SRCS, "-o", _SO + ".tmp", "-lm"]
         subprocess.run(cmd, check=True)
@@ -71,17 +73,24 @@ def lib():
         L.o_compute_scale.restype = C.c_int
         L.o_compute_scale.argtypes = [C.c_float, C.c_int, C.c_int, C.c_float,
                                       C.POINTER(C.c_float), C.POINTER(C.c_float)]
-        L.o_history_update.restype = None
-        L.o_history_update.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int,
+        L.o_compute_scale_pow2.restype = C.c_int
+        L.o_compute_scale_pow2.argtypes = [C.c_float, C.c_int, C.c_int, C.c_float,
+                                           C.POINTER(C.c_float), C.POINTER(C.c_float)]
+        L.o_pow2_exponent.restype = C.c_int
+        L.o_pow2_exponent.argtypes = [C.c_float, C.c_int]
+        for nm in ("o_history_update", "o_history_update_pow2"):
+            getattr(L, nm).restype = None
+            getattr(L, nm).argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_int,
                                        C.c_int, C.c_int, C.c_void_p, C.c_void_p]
         L.o_cast.restype = None
         L.o_cast.argtypes = [C.c_void_p, C.c_int64, C.c_float, C.c_int, C.c_void_p]
         L.o_cast_transpose.restype = None
         L.o_cast_transpose.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_float, C.c_int,
                                        C.c_void_p, C.c_void_p]
-        L.o_cast_block.restype = None
-        L.o_cast_block.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int, C.c_int,
-                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+        for nm in ("o_cast_block", "o_cast_block_pow2"):
+            getattr(L, nm).restype = None
+            getattr(L, nm).argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int, C.c_int,
+                                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
         L.o_f32_to_bf16.restype = C.c_uint16
         L.o_f32_to_bf16.argtypes = [C.c_float]
         L.o_encode_array.restype = None
@@ -181,21 +190,30 @@ def amax_parallel(x_bf16) -> np.float32:
     return best.view(np.float32)
 
 
-def compute_scale(amax_v: float, fmt: int, margin: int = 0, fallback: float = 1.0):
+def compute_scale(amax_v: float, fmt: int, margin: int = 0, fallback: float = 1.0,
+                  pow2: bool = False):
+    """(scale, scale_inv, updated).  pow2: the power-of-two (exponent-bias) rule."""
     s, si = C.c_float(), C.c_float()
-    ok = lib().o_compute_scale(float(np.float32(amax_v)), fmt, margin, float(np.float32(fallback)),
-                               C.byref(s), C.byref(si))
+    fn = lib().o_compute_scale_pow2 if pow2 else lib().o_compute_scale
+    ok = fn(float(np.float32(amax_v)), fmt, margin, float(np.float32(fallback)),
+            C.byref(s), C.byref(si))
     return np.float32(s.value), np.float32(si.value), bool(ok)
 
 
+def pow2_exponent(amax_v: float, fmt: int) -> int:
+    """Largest e with amax * 2^e <= fmax (before margin and clamping)."""
+    return int(lib().o_pow2_exponent(float(np.float32(amax_v)), fmt))
+
+
 def history_update(history: np.ndarray, amax_new, fmt: int, margin: int, algo: int,
-                   scale: np.ndarray, scale_inv: np.ndarray):
+                   scale: np.ndarray, scale_inv: np.ndarray, pow2: bool = False):
     """In-place on history [n][len], scale [n], scale_inv [n] (float32)."""
     assert history.dtype == np.float32 and history.flags.c_contiguous
     assert scale.dtype == np.float32 and scale_inv.dtype == np.float32
     a = _c(amax_new, np.float32)
     n, ln = history.shape
-    lib().o_history_update(_p(history), n, ln, _p(a), fmt, margin, algo, _p(scale), _p(scale_inv))
+    fn = lib().o_history_update_pow2 if pow2 else lib().o_history_update
+    fn(_p(history), n, ln, _p(a), fmt, margin, algo, _p(scale), _p(scale_inv))
 
 
 # -------------------------------------------------------------- casts ---
@@ -233,10 +251,12 @@ def cast_transpose_plain(x_bf16, s: float, fmt: int):
     return y, yt
 
 
-def cast_block(x_bf16, fmt: int, tile: int, want_y=True, want_t=False, plain=False):
+def cast_block(x_bf16, fmt: int, tile: int, want_y=True, want_t=False, plain=False,
+               pow2=False):
     """Block-wise cast of x [rows][cols].  Returns dict with y, sinv, y_t,
     sinv_t (the ones requested).  Row chunks of 128*k rows run on worker
-    threads (tiles never straddle chunks) unless plain=True."""
+    threads (tiles never straddle chunks) unless plain=True.  pow2: the
+    tile scales follow the power-of-two (exponent-bias) rule."""
     x = _c(x_bf16, np.uint16)
     rows, cols = x.shape
     nrb, ncb = (rows + 127) // 128, (cols + 127) // 128
@@ -265,7 +285,7 @@ def cast_block(x_bf16, fmt: int, tile: int, want_y=True, want_t=False, plain=Fal
         else:
             ss = np.empty((ncb, (cr + 127) // 128), np.float32)
             sts = np.empty(((cr + 127) // 128, ncb), np.float32)
-        L.o_cast_block(_p(xs), cr, cols, fmt, tile,
+        (L.o_cast_block_pow2 if pow2 else L.o_cast_block)(_p(xs), cr, cols, fmt, tile,
                        _p(ys) if ys is not None else None, _p(ss) if ss is not None else None,
                        _p(yts) if yts is not None else None, _p(sts) if sts is not None else None)
         rb0, rb1 = r0 // 128, (r1 + 127) // 128
