@@ -12,7 +12,8 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 inline bool fmt_ok(int f) { return f == FP8_E4M3 || f == FP8_E5M2; }
 inline bool scaling_ok(int s) {
-  return s == FP8_SCALE_TENSOR || s == FP8_SCALE_1x128 || s == FP8_SCALE_128x128;
+  return s == FP8_SCALE_TENSOR || s == FP8_SCALE_1x128 || s == FP8_SCALE_128x128 ||
+         s == FP8_SCALE_1x128_POW2 || s == FP8_SCALE_128x128_POW2;
 }
 inline fp8_status launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
 
@@ -56,19 +57,22 @@ fp8_status fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, float* amax,
   return launched(launch_amax(static_cast<const uint16_t*>(x_bf16), rows * cols, amax, stream));
 }
 
-fp8_status fp8_compute_scale(const float* amax, int64_t n, fp8_format fmt, int margin,
-                             float* scale, float* scale_inv, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+fp8_status compute_scale_common(const float* amax, int64_t n, fp8_format fmt, int margin, int pow2,
+                                float* scale, float* scale_inv, hipStream_t stream) {
   if (n < 0) return FP8_ERR_SHAPE;
   if (!fmt_ok(fmt) || margin < 0 || margin > 64) return FP8_ERR_ARG;
   if (n > 0 && (amax == nullptr || scale == nullptr || scale_inv == nullptr)) return FP8_ERR_NULL;
   if (!aligned4(amax) || !aligned4(scale) || !aligned4(scale_inv)) return FP8_ERR_ALIGN;
-  return launched(launch_compute_scale(amax, n, fmt, margin, scale, scale_inv, stream));
+  return launched(launch_compute_scale(amax, n, fmt, margin, pow2, scale, scale_inv, stream));
 }
 
-fp8_status fp8_amax_history_update(float* history, int64_t n, int64_t len,
-                                   const float* amax_new, fp8_format fmt, int margin,
-                                   fp8_amax_algo algo, float* scale, float* scale_inv,
-                                   hipStream_t stream) {
+fp8_status history_common(float* history, int64_t n, int64_t len, const float* amax_new,
+                          fp8_format fmt, int margin, fp8_amax_algo algo, int pow2, float* scale,
+                          float* scale_inv, hipStream_t stream) {
   if (n < 0 || len < 1 || len > 1024) return FP8_ERR_SHAPE;
   if (!fmt_ok(fmt) || margin < 0 || margin > 64) return FP8_ERR_ARG;
   if (algo != FP8_AMAX_MAX && algo != FP8_AMAX_MOST_RECENT) return FP8_ERR_ARG;
@@ -77,8 +81,52 @@ fp8_status fp8_amax_history_update(float* history, int64_t n, int64_t len,
     return FP8_ERR_NULL;
   if (!aligned4(history) || !aligned4(amax_new) || !aligned4(scale) || !aligned4(scale_inv))
     return FP8_ERR_ALIGN;
-  return launched(
-      launch_history_update(history, n, len, amax_new, fmt, margin, algo, scale, scale_inv, stream));
+  return launched(launch_history_update(history, n, len, amax_new, fmt, margin, algo, pow2, scale,
+                                        scale_inv, stream));
+}
+
+fp8_status cast_block_common(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                             fp8_scaling tile, int pow2, uint8_t* y, float* scale_inv,
+                             uint8_t* y_t, float* scale_inv_t, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
+  if (!fmt_ok(fmt) || (tile != FP8_SCALE_1x128 && tile != FP8_SCALE_128x128)) return FP8_ERR_ARG;
+  if (rows == 0 || cols == 0) return FP8_OK;  // nothing to quantise
+  if ((y == nullptr) != (scale_inv == nullptr) || (y_t == nullptr) != (scale_inv_t == nullptr))
+    return FP8_ERR_NULL;
+  if (y == nullptr && y_t == nullptr) return FP8_ERR_NULL;
+  if (x_bf16 == nullptr) return FP8_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(y) || !aligned16(y_t)) return FP8_ERR_ALIGN;
+  if (!aligned4(scale_inv) || !aligned4(scale_inv_t)) return FP8_ERR_ALIGN;
+  return launched(launch_cast_block(static_cast<const uint16_t*>(x_bf16), rows, cols, fmt, tile,
+                                    pow2, y, scale_inv, y_t, scale_inv_t, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8_status fp8_compute_scale(const float* amax, int64_t n, fp8_format fmt, int margin,
+                             float* scale, float* scale_inv, hipStream_t stream) {
+  return compute_scale_common(amax, n, fmt, margin, 0, scale, scale_inv, stream);
+}
+
+fp8_status fp8_compute_scale_pow2(const float* amax, int64_t n, fp8_format fmt, int margin,
+                                  float* scale, float* scale_inv, hipStream_t stream) {
+  return compute_scale_common(amax, n, fmt, margin, 1, scale, scale_inv, stream);
+}
+
+fp8_status fp8_amax_history_update(float* history, int64_t n, int64_t len,
+                                   const float* amax_new, fp8_format fmt, int margin,
+                                   fp8_amax_algo algo, float* scale, float* scale_inv,
+                                   hipStream_t stream) {
+  return history_common(history, n, len, amax_new, fmt, margin, algo, 0, scale, scale_inv, stream);
+}
+
+fp8_status fp8_amax_history_update_pow2(float* history, int64_t n, int64_t len,
+                                        const float* amax_new, fp8_format fmt, int margin,
+                                        fp8_amax_algo algo, float* scale, float* scale_inv,
+                                        hipStream_t stream) {
+  return history_common(history, n, len, amax_new, fmt, margin, algo, 1, scale, scale_inv, stream);
 }
 
 fp8_status fp8_cast_e4m3(const void* x_bf16, int64_t rows, int64_t cols, const float* scale,
@@ -94,17 +142,15 @@ fp8_status fp8_cast_e5m2(const void* x_bf16, int64_t rows, int64_t cols, const f
 fp8_status fp8_cast_block(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
                           fp8_scaling tile, uint8_t* y, float* scale_inv, uint8_t* y_t,
                           float* scale_inv_t, hipStream_t stream) {
-  if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
-  if (!fmt_ok(fmt) || (tile != FP8_SCALE_1x128 && tile != FP8_SCALE_128x128)) return FP8_ERR_ARG;
-  if (rows == 0 || cols == 0) return FP8_OK;  // nothing to quantise
-  if ((y == nullptr) != (scale_inv == nullptr) || (y_t == nullptr) != (scale_inv_t == nullptr))
-    return FP8_ERR_NULL;
-  if (y == nullptr && y_t == nullptr) return FP8_ERR_NULL;
-  if (x_bf16 == nullptr) return FP8_ERR_NULL;
-  if (!aligned16(x_bf16) || !aligned16(y) || !aligned16(y_t)) return FP8_ERR_ALIGN;
-  if (!aligned4(scale_inv) || !aligned4(scale_inv_t)) return FP8_ERR_ALIGN;
-  return launched(launch_cast_block(static_cast<const uint16_t*>(x_bf16), rows, cols, fmt, tile, y,
-                                    scale_inv, y_t, scale_inv_t, stream));
+  return cast_block_common(x_bf16, rows, cols, fmt, tile, 0, y, scale_inv, y_t, scale_inv_t,
+                           stream);
+}
+
+fp8_status fp8_cast_block_pow2(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                               fp8_scaling tile, uint8_t* y, float* scale_inv, uint8_t* y_t,
+                               float* scale_inv_t, hipStream_t stream) {
+  return cast_block_common(x_bf16, rows, cols, fmt, tile, 1, y, scale_inv, y_t, scale_inv_t,
+                           stream);
 }
 
 fp8_status fp8_scaled_gemm(const fp8_gemm_args* a, hipStream_t stream) {

@@ -43,12 +43,14 @@ __device__ __forceinline__ uint32_t absmax2(uint32_t w) {
   return umax(lo, hi);
 }
 
-// Scale for one tile from its amax bits (1 for all-zero / non-finite).
-template <int FMT>
+// Scale for one tile from its amax bits (1 for all-zero / non-finite);
+// P2: the power-of-two (exponent-bias) rule.
+template <int FMT, bool P2>
 __device__ __forceinline__ void tile_scale(uint32_t amax_bits, float& s, float& si) {
   s = 1.0f;
   si = 1.0f;
-  scale_from_amax(__uint_as_float(amax_bits), Fmt<FMT>::max, 0, s, si);
+  if constexpr (P2) pow2_scale_from_amax(__uint_as_float(amax_bits), Fmt<FMT>::max, 0, s, si);
+  else scale_from_amax(__uint_as_float(amax_bits), Fmt<FMT>::max, 0, s, si);
 }
 
 // Store the transposed tile from registers: w[i][j] holds the codes of row
@@ -88,7 +90,7 @@ __device__ __forceinline__ void store_transposed(uint8_t* lds, const uint32_t (&
 // Tiled kernel: rows % 16 == 0 and cols % 16 == 0.  Thread t owns rows
 // 4*(t/8)..+3 and columns 16*(t%8)..+15 of the tile, held as raw bf16.
 // ---------------------------------------------------------------------
-template <int FMT, int TILE, bool WANT_Y, bool WANT_T>
+template <int FMT, int TILE, bool WANT_Y, bool WANT_T, bool P2>
 __global__ void __launch_bounds__(kThreads)
     k_cast_block(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                  uint8_t* __restrict__ y, float* __restrict__ sinv, uint8_t* __restrict__ yt,
@@ -133,7 +135,7 @@ __global__ void __launch_bounds__(kThreads)
     __syncthreads();
     mb = umax(umax(red[0][0], red[1][0]), umax(red[2][0], red[3][0]));
     float s, si;
-    tile_scale<FMT>(mb, s, si);
+    tile_scale<FMT, P2>(mb, s, si);
     if (t == 0) {
       if (sinv) sinv[cb * nrb + rb] = si;
       if (sinv_t) sinv_t[rb * ncb + cb] = si;
@@ -164,7 +166,7 @@ __global__ void __launch_bounds__(kThreads)
         mb = umax(mb, __shfl_xor(mb, 2, 64));
         mb = umax(mb, __shfl_xor(mb, 4, 64));
         float s, si;
-        tile_scale<FMT>(mb, s, si);
+        tile_scale<FMT, P2>(mb, s, si);
         const int64_t r = r0 + 4 * rg + i;
         if (cg == 0 && r < rows) sinv[cb * rows + r] = si;
         if (col_ok && r < rows) {
@@ -207,7 +209,7 @@ __global__ void __launch_bounds__(kThreads)
       if (t < 128) {
         const uint32_t mb = umax(umax(red[0][t], red[1][t]), umax(red[2][t], red[3][t]));
         float s, si;
-        tile_scale<FMT>(mb, s, si);
+        tile_scale<FMT, P2>(mb, s, si);
         col_s[t] = s;
         if (c0 + t < cols) sinv_t[rb * cols + c0 + t] = si;
       }
@@ -234,7 +236,7 @@ __global__ void __launch_bounds__(kThreads)
 // t < 128 handles row t (1x128 rows) or column t (token-axis tiles) of the
 // tile with scalar loops; 128x128 reduces over the whole tile.
 // ---------------------------------------------------------------------
-template <int FMT, int TILE>
+template <int FMT, int TILE, bool P2>
 __global__ void __launch_bounds__(kThreads)
     k_cast_block_generic(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                          uint8_t* __restrict__ y, float* __restrict__ sinv,
@@ -256,7 +258,7 @@ __global__ void __launch_bounds__(kThreads)
     __syncthreads();
     m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
     float s, si;
-    tile_scale<FMT>(m, s, si);
+    tile_scale<FMT, P2>(m, s, si);
     if (t == 0) {
       if (sinv) sinv[cb * nrb + rb] = si;
       if (sinv_t) sinv_t[rb * ncb + cb] = si;
@@ -274,7 +276,7 @@ __global__ void __launch_bounds__(kThreads)
       uint32_t m = 0;
       for (int64_t c = c0; c < c1; ++c) m = umax(m, (uint32_t)(x[r * cols + c] & 0x7FFFu) << 16);
       float s, si;
-      tile_scale<FMT>(m, s, si);
+      tile_scale<FMT, P2>(m, s, si);
       sinv[cb * rows + r] = si;
       for (int64_t c = c0; c < c1; ++c)
         y[r * cols + c] = (uint8_t)(cvt4<FMT>(__uint_as_float((uint32_t)x[r * cols + c] << 16) * s,
@@ -285,7 +287,7 @@ __global__ void __launch_bounds__(kThreads)
       uint32_t m = 0;
       for (int64_t r = r0; r < r1; ++r) m = umax(m, (uint32_t)(x[r * cols + c] & 0x7FFFu) << 16);
       float s, si;
-      tile_scale<FMT>(m, s, si);
+      tile_scale<FMT, P2>(m, s, si);
       sinv_t[rb * cols + c] = si;
       for (int64_t r = r0; r < r1; ++r)
         yt[c * rows + r] = (uint8_t)(cvt4<FMT>(__uint_as_float((uint32_t)x[r * cols + c] << 16) * s,
@@ -294,22 +296,22 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-template <int FMT, int TILE>
+template <int FMT, int TILE, bool P2>
 hipError_t launch_block_t(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* y, float* sinv,
                           uint8_t* yt, float* sinv_t, hipStream_t s) {
   dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
   if (rows % 16 == 0 && cols % 16 == 0) {
     if (y && yt)
-      hipLaunchKernelGGL((k_cast_block<FMT, TILE, true, true>), grid, dim3(kThreads), 0, s, x,
+      hipLaunchKernelGGL((k_cast_block<FMT, TILE, true, true, P2>), grid, dim3(kThreads), 0, s, x,
                          rows, cols, y, sinv, yt, sinv_t);
     else if (y)
-      hipLaunchKernelGGL((k_cast_block<FMT, TILE, true, false>), grid, dim3(kThreads), 0, s, x,
+      hipLaunchKernelGGL((k_cast_block<FMT, TILE, true, false, P2>), grid, dim3(kThreads), 0, s, x,
                          rows, cols, y, sinv, yt, sinv_t);
     else
-      hipLaunchKernelGGL((k_cast_block<FMT, TILE, false, true>), grid, dim3(kThreads), 0, s, x,
+      hipLaunchKernelGGL((k_cast_block<FMT, TILE, false, true, P2>), grid, dim3(kThreads), 0, s, x,
                          rows, cols, y, sinv, yt, sinv_t);
   } else {
-    hipLaunchKernelGGL((k_cast_block_generic<FMT, TILE>), grid, dim3(kThreads), 0, s, x, rows,
+    hipLaunchKernelGGL((k_cast_block_generic<FMT, TILE, P2>), grid, dim3(kThreads), 0, s, x, rows,
                        cols, y, sinv, yt, sinv_t);
   }
   return hipGetLastError();
@@ -317,14 +319,22 @@ hipError_t launch_block_t(const uint16_t* x, int64_t rows, int64_t cols, uint8_t
 
 }  // namespace
 
-hipError_t launch_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int tile,
-                             uint8_t* y, float* sinv, uint8_t* y_t, float* sinv_t, hipStream_t s) {
-  if (rows == 0 || cols == 0) return hipSuccess;
+template <bool P2>
+hipError_t launch_block_p(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int tile,
+                          uint8_t* y, float* sinv, uint8_t* y_t, float* sinv_t, hipStream_t s) {
   if (fmt == 0)
-    return tile == 2 ? launch_block_t<0, 2>(x, rows, cols, y, sinv, y_t, sinv_t, s)
-                     : launch_block_t<0, 1>(x, rows, cols, y, sinv, y_t, sinv_t, s);
-  return tile == 2 ? launch_block_t<1, 2>(x, rows, cols, y, sinv, y_t, sinv_t, s)
-                   : launch_block_t<1, 1>(x, rows, cols, y, sinv, y_t, sinv_t, s);
+    return tile == 2 ? launch_block_t<0, 2, P2>(x, rows, cols, y, sinv, y_t, sinv_t, s)
+                     : launch_block_t<0, 1, P2>(x, rows, cols, y, sinv, y_t, sinv_t, s);
+  return tile == 2 ? launch_block_t<1, 2, P2>(x, rows, cols, y, sinv, y_t, sinv_t, s)
+                   : launch_block_t<1, 1, P2>(x, rows, cols, y, sinv, y_t, sinv_t, s);
+}
+
+hipError_t launch_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int tile,
+                             int pow2, uint8_t* y, float* sinv, uint8_t* y_t, float* sinv_t,
+                             hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  return pow2 ? launch_block_p<true>(x, rows, cols, fmt, tile, y, sinv, y_t, sinv_t, s)
+              : launch_block_p<false>(x, rows, cols, fmt, tile, y, sinv, y_t, sinv_t, s);
 }
 
 }  // namespace fp8lin

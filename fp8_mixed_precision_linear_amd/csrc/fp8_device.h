@@ -6,6 +6,8 @@
 //   [MPG] "Mixed Precision LLM Training: The Complete Guide":
 //         "The precision formats", "FP8 E4M3", "FP8 E5M2",
 //         "Transformer Engine internals > Per-tensor scaling".
+//   [P3]  "Training and inference of large language models using 8-bit
+//         floating point" (arXiv 2309.17224 library entry).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -132,6 +134,32 @@ __device__ __forceinline__ bool scale_from_amax(float amax, float fmax, int marg
   if (margin != 0) q = __builtin_ldexpf(q, -margin);
   s = q;
   s_inv = __fdiv_rn(1.0f, q);
+  return true;
+}
+
+// Power-of-two ("exponent bias") scale from an amax: s = 2^e with e the
+// largest integer such that amax * 2^e <= fmax, minus margin, clamped to
+// [-126, 126]; s_inv = 2^-e (both exact normal powers of two).  Returns
+// false (s, s_inv untouched) for amax == 0 or non-finite.  With
+// amax = 1.ma * 2^ea and fmax = 1.mf * 2^ef: e = ef - ea when ma <= mf,
+// else ef - ea - 1 (compared on the mantissa fields; a subnormal amax is
+// first scaled by 2^64, exactly).  [P3] "Training and inference of large
+// language models using 8-bit floating point": the exponent bias is chosen
+// from the tensor's maximum (FP8-AMAX).
+__device__ __forceinline__ bool pow2_scale_from_amax(float amax, float fmax, int margin, float& s,
+                                                     float& s_inv) {
+  if (!(amax > 0.0f) || __builtin_isinf(amax)) return false;   // also rejects NaN
+  int adj = 0;
+  if (amax < 1.17549435e-38f) {
+    amax *= 18446744073709551616.0f;   // 2^64
+    adj = 64;
+  }
+  const uint32_t b = __float_as_uint(amax), f = __float_as_uint(fmax);
+  const int ea = (int)(b >> 23) - 127 - adj, ef = (int)(f >> 23) - 127;
+  int e = ef - ea - ((b & 0x7FFFFFu) > (f & 0x7FFFFFu) ? 1 : 0) - margin;
+  e = e > 126 ? 126 : (e < -126 ? -126 : e);
+  s = __uint_as_float((uint32_t)(e + 127) << 23);
+  s_inv = __uint_as_float((uint32_t)(127 - e) << 23);
   return true;
 }
 

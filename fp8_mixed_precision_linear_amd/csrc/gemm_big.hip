@@ -68,6 +68,16 @@ __device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, 0, 0, 0);
 }
 
+// The same instruction with per-lane E8M0 block scales: lane l of operand
+// `a` holds one row and applies 2^(sa - 127) to it, likewise for `b`.
+template <int AF, int BF>
+__device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, sa, 0, sb);
+}
+
+// E8M0 code of a power of two 2^e (|e| <= 126): its binary32 exponent field.
+__device__ __forceinline__ int e8m0_of(float pow2) { return (int)(__float_as_uint(pow2) >> 23) & 0xFF; }
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t b = __float_as_uint(f);
   if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);
@@ -115,7 +125,7 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int row, int g) {
 // BLOCK : block-mode promotion per 128-wide K block;
 // SA_ROWS: A has 1x128 scales (one per row and K block), else one per wave;
 // SB_COL : B has 1x128 scales (one per column and K block), else one per wave.
-template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL>
+template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL, bool MX>
 __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
   __shared__ float su_tab[NWAVES][MAX_KB];
@@ -150,12 +160,24 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     const int64_t mb = min((m0 + wm * WTM) / 128, (M + 127) / 128 - 1);
     const int64_t nb = min((n0 + wn * WTN) / 128, (N + 127) / 128 - 1);
     for (int kb = lane; kb < nk; kb += 64) {
-      float s = 1.0f;
-      if constexpr (!SA_ROWS)
-        s = p.a_scaling == 0 ? p.a_sinv[0] : p.a_sinv[kb * ((M + 127) / 128) + mb];
-      if constexpr (!SB_COL)
-        s *= p.b_scaling == 0 ? p.b_sinv[0] : p.b_sinv[kb * ((N + 127) / 128) + nb];
-      su_tab[wave][kb] = s;
+      if constexpr (MX) {
+        // E8M0 codes of the uniform block scales: A in bits 0-7, B in 8-15
+        // (127 = 1.0 for a per-tensor operand, whose scale goes to the
+        // epilogue)
+        int ea = 127, eb = 127;
+        if constexpr (!SA_ROWS)
+          if (p.a_scaling != 0) ea = e8m0_of(p.a_sinv[kb * ((M + 127) / 128) + mb]);
+        if constexpr (!SB_COL)
+          if (p.b_scaling != 0) eb = e8m0_of(p.b_sinv[kb * ((N + 127) / 128) + nb]);
+        su_tab[wave][kb] = __uint_as_float((uint32_t)ea | ((uint32_t)eb << 8));
+      } else {
+        float s = 1.0f;
+        if constexpr (!SA_ROWS)
+          s = p.a_scaling == 0 ? p.a_sinv[0] : p.a_sinv[kb * ((M + 127) / 128) + mb];
+        if constexpr (!SB_COL)
+          s *= p.b_scaling == 0 ? p.b_sinv[0] : p.b_sinv[kb * ((N + 127) / 128) + nb];
+        su_tab[wave][kb] = s;
+      }
     }
   }
 
@@ -211,7 +233,31 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     // The MFMA takes B as its first operand, so each 16x16 result tile is
     // the transpose of the D tile: lane (g, l16) holds D row 16*i + l16,
     // columns 16*j + 4*g .. +3 -- four consecutive outputs of one row.
-    if constexpr (BLOCK) {
+    if constexpr (MX) {
+      // power-of-two block scales applied inside the matrix instruction
+      // (exact): lane l of the B fragment scales its row (a D column), lane
+      // l of the A fragment its row; no FP32 promotion, the accumulator
+      // stays in the instruction's C operand.
+      uint32_t eu = 0;
+      if constexpr (!(SA_ROWS && SB_COL)) eu = __float_as_uint(su_tab[wave][kb]);
+      int eb[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        if constexpr (SB_COL)
+          eb[j] = e8m0_of(reinterpret_cast<const float*>(As + SB_OFF)[wn * WTN + 16 * j + l16]);
+        else
+          eb[j] = (int)((eu >> 8) & 0xFFu);
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const v8i afr = frag(As, wm * WTM + 16 * i + l16, g);
+        int ea = (int)(eu & 0xFFu);
+        if constexpr (SA_ROWS)
+          ea = e8m0_of(reinterpret_cast<const float*>(As + SA_OFF)[wm * WTM + 16 * i + l16]);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_mx<BF, AF>(bfr[j], afr, acc[i][j], eb[j], ea);
+      }
+    } else if constexpr (BLOCK) {
       float scol[TJ][4];
       if constexpr (SB_COL) {
 #pragma unroll
@@ -287,6 +333,11 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     sa = p.a_sinv[0];
     sb = p.b_sinv[0];
   }
+  if constexpr (MX) {   // a per-tensor operand's scale is applied here
+    if (p.a_scaling == 0) sa = p.a_sinv[0];
+    if (p.b_scaling == 0) sb = p.b_sinv[0];
+  }
+  constexpr bool EPI_SCALE = !BLOCK || MX;
   const int esz = p.d_f32 ? 4 : 2;
   const bool staged = (m0 + BM <= M) && (n0 + BN <= N) && ((p.ldd * esz) % 16 == 0) &&
                       ((reinterpret_cast<uintptr_t>(p.D) & 15u) == 0);
@@ -311,7 +362,7 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
           for (int j = 0; j < TJ; ++j) {
             float v[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = BLOCK ? acc[i][j][q] : (acc[i][j][q] * sa) * sb;
+            for (int q = 0; q < 4; ++q) v[q] = EPI_SCALE ? (acc[i][j][q] * sa) * sb : acc[i][j][q];
             const int byte = (16 * j + 4 * g) * ES;
             uint8_t* dst = wl + r * ROW_BYTES + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
             if constexpr (F32) {
@@ -365,7 +416,7 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (n + r >= N) continue;
-          float x = BLOCK ? acc[i][j][r] : (acc[i][j][r] * sa) * sb;
+          float x = EPI_SCALE ? (acc[i][j][r] * sa) * sb : acc[i][j][r];
           if (p.d_f32) {
             float* d = reinterpret_cast<float*>(p.D) + m * p.ldd + n + r;
             if (p.accumulate) x = *d + x;
@@ -395,24 +446,35 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   }
 }
 
-template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL>
+template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL, bool MX>
 hipError_t launch_one(const GemmParams& p, hipStream_t s) {
-  auto kern = k_gemm_big<AF, BF, BLOCK, SA_ROWS, SB_COL>;
+  auto kern = k_gemm_big<AF, BF, BLOCK, SA_ROWS, SB_COL, MX>;
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
   hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(THREADS), 0, s, p, tiles_m,
                      tiles_n);
   return hipGetLastError();
 }
 
+template <int AF, int BF, bool MX>
+hipError_t launch_block(const GemmParams& p, hipStream_t s) {
+  const bool sa = p.a_scaling == 1 || p.a_scaling == 3, sb = p.b_scaling == 1 || p.b_scaling == 3;
+  if (sa && sb) return launch_one<AF, BF, true, true, true, MX>(p, s);
+  if (sa) return launch_one<AF, BF, true, true, false, MX>(p, s);
+  if (sb) return launch_one<AF, BF, true, false, true, MX>(p, s);
+  return launch_one<AF, BF, true, false, false, MX>(p, s);
+}
+
+// Scaling codes: 0 per-tensor, 1 / 2 block (1x128 / 128x128) with any
+// binary32 scales, 3 / 4 the same blocks with power-of-two scales.  When
+// every block-scaled operand has power-of-two scales the block scales go
+// into the matrix instruction; otherwise they are promoted in FP32 (a
+// power of two is a binary32 scale like any other).
 template <int AF, int BF>
 hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
   const bool block = !(p.a_scaling == 0 && p.b_scaling == 0);
-  if (!block) return launch_one<AF, BF, false, false, false>(p, s);
-  const bool sa = p.a_scaling == 1, sb = p.b_scaling == 1;
-  if (sa && sb) return launch_one<AF, BF, true, true, true>(p, s);
-  if (sa) return launch_one<AF, BF, true, true, false>(p, s);
-  if (sb) return launch_one<AF, BF, true, false, true>(p, s);
-  return launch_one<AF, BF, true, false, false>(p, s);
+  if (!block) return launch_one<AF, BF, false, false, false, false>(p, s);
+  const bool mx = (p.a_scaling == 0 || p.a_scaling >= 3) && (p.b_scaling == 0 || p.b_scaling >= 3);
+  return mx ? launch_block<AF, BF, true>(p, s) : launch_block<AF, BF, false>(p, s);
 }
 
 }  // namespace

@@ -268,10 +268,15 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
   }
   if (gemm_big_supported(p)) return launch_gemm_big(p, s);
-  if (p.a_fmt == 0 && p.b_fmt == 0) return launch_fmt<0, 0>(p, s);
-  if (p.a_fmt == 1 && p.b_fmt == 0) return launch_fmt<1, 0>(p, s);
-  if (p.a_fmt == 0 && p.b_fmt == 1) return launch_fmt<0, 1>(p, s);
-  return launch_fmt<1, 1>(p, s);
+  // this kernel promotes every block scale in FP32: power-of-two block
+  // scales (codes 3, 4) are binary32 scales of the same layouts (1, 2)
+  GemmParams q = p;
+  if (q.a_scaling >= 3) q.a_scaling -= 2;
+  if (q.b_scaling >= 3) q.b_scaling -= 2;
+  if (q.a_fmt == 0 && q.b_fmt == 0) return launch_fmt<0, 0>(q, s);
+  if (q.a_fmt == 1 && q.b_fmt == 0) return launch_fmt<1, 0>(q, s);
+  if (q.a_fmt == 0 && q.b_fmt == 1) return launch_fmt<0, 1>(q, s);
+  return launch_fmt<1, 1>(q, s);
 }
 
 }  // namespace fp8lin

@@ -17,21 +17,23 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 // amax over n bf16 values (x 16-byte aligned); writes the result to *amax.
 hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t s);
 
-hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, int margin, float* scale,
-                                float* scale_inv, hipStream_t s);
+// pow2 != 0: power-of-two (exponent-bias) scales instead of fmax / amax.
+hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, int margin, int pow2,
+                                float* scale, float* scale_inv, hipStream_t s);
 
 hipError_t launch_history_update(float* history, int64_t n, int64_t len, const float* amax_new,
-                                 int fmt, int margin, int algo, float* scale, float* scale_inv,
-                                 hipStream_t s);
+                                 int fmt, int margin, int algo, int pow2, float* scale,
+                                 float* scale_inv, hipStream_t s);
 
 // Per-tensor cast with optional transpose and amax (amax must be zeroed by
 // the caller first when given).
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, const float* scale, int fmt,
                        uint8_t* y, uint8_t* y_t, float* amax, hipStream_t s);
 
-// Block-wise cast (tile: 1 = 1x128, 2 = 128x128).
+// Block-wise cast (tile: 1 = 1x128, 2 = 128x128; pow2: power-of-two scales).
 hipError_t launch_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int tile,
-                             uint8_t* y, float* sinv, uint8_t* y_t, float* sinv_t, hipStream_t s);
+                             int pow2, uint8_t* y, float* sinv, uint8_t* y_t, float* sinv_t,
+                             hipStream_t s);
 
 struct GemmParams {
   int64_t M, N, K, lda, ldb, ldd;

@@ -70,11 +70,13 @@ __global__ void __launch_bounds__(kAmaxThreads) k_amax(const uint16_t* __restric
 
 // Current scaling: one thread per tensor.
 __global__ void k_compute_scale(const float* __restrict__ amax, int64_t n, float fmax, int margin,
-                                float* __restrict__ scale, float* __restrict__ scale_inv) {
+                                int pow2, float* __restrict__ scale,
+                                float* __restrict__ scale_inv) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   float s = 1.0f, si = 1.0f;
-  scale_from_amax(amax[i], fmax, margin, s, si);
+  if (pow2) pow2_scale_from_amax(amax[i], fmax, margin, s, si);
+  else scale_from_amax(amax[i], fmax, margin, s, si);
   scale[i] = s;
   scale_inv[i] = si;
 }
@@ -90,7 +92,7 @@ __global__ void k_compute_scale(const float* __restrict__ amax, int64_t n, float
 __global__ void __launch_bounds__(64) k_history_update(float* __restrict__ history, int64_t n,
                                                        int64_t len,
                                                        const float* __restrict__ amax_new,
-                                                       float fmax, int margin, int algo,
+                                                       float fmax, int margin, int algo, int pow2,
                                                        float* __restrict__ scale,
                                                        float* __restrict__ scale_inv) {
   const int64_t i = blockIdx.x;
@@ -114,7 +116,9 @@ __global__ void __launch_bounds__(64) k_history_update(float* __restrict__ histo
     h[0] = a;
     const float eff = algo == 1 ? a : __uint_as_float(best);
     float s, si;
-    if (scale_from_amax(eff, fmax, margin, s, si)) {
+    const bool ok = pow2 ? pow2_scale_from_amax(eff, fmax, margin, s, si)
+                         : scale_from_amax(eff, fmax, margin, s, si);
+    if (ok) {
       scale[i] = s;
       scale_inv[i] = si;
     }
@@ -162,22 +166,22 @@ hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, int margin, float* scale,
-                                float* scale_inv, hipStream_t s) {
+hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, int margin, int pow2,
+                                float* scale, float* scale_inv, hipStream_t s) {
   if (n == 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(k_compute_scale, dim3((unsigned)blocks), dim3(256), 0, s, amax, n,
-                     fmax_of(fmt), margin, scale, scale_inv);
+                     fmax_of(fmt), margin, pow2, scale, scale_inv);
   return hipGetLastError();
 }
 
 hipError_t launch_history_update(float* history, int64_t n, int64_t len, const float* amax_new,
-                                 int fmt, int margin, int algo, float* scale, float* scale_inv,
-                                 hipStream_t s) {
+                                 int fmt, int margin, int algo, int pow2, float* scale,
+                                 float* scale_inv, hipStream_t s) {
   if (n == 0) return hipSuccess;
   if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_history_update, dim3((unsigned)n), dim3(64), 0, s, history, n, len,
-                     amax_new, fmax_of(fmt), margin, algo, scale, scale_inv);
+                     amax_new, fmax_of(fmt), margin, algo, pow2, scale, scale_inv);
   return hipGetLastError();
 }
 

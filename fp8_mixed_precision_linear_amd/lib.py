@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
 
 E4M3, E5M2 = 0, 1
 SCALE_TENSOR, SCALE_1x128, SCALE_128x128 = 0, 1, 2
+SCALE_1x128_POW2, SCALE_128x128_POW2 = 3, 4
 OUT_BF16, OUT_F32 = 0, 1
 AMAX_MAX, AMAX_MOST_RECENT = 0, 1
 
@@ -53,10 +54,13 @@ def _load():
         "fp8_status_string": (C.c_char_p, [i32]),
         "fp8_amax": (i32, [vp, i64, i64, vp, vp]),
         "fp8_compute_scale": (i32, [vp, i64, i32, i32, vp, vp, vp]),
+        "fp8_compute_scale_pow2": (i32, [vp, i64, i32, i32, vp, vp, vp]),
         "fp8_amax_history_update": (i32, [vp, i64, i64, vp, i32, i32, i32, vp, vp, vp]),
+        "fp8_amax_history_update_pow2": (i32, [vp, i64, i64, vp, i32, i32, i32, vp, vp, vp]),
         "fp8_cast_e4m3": (i32, [vp, i64, i64, vp, vp, vp, vp, vp]),
         "fp8_cast_e5m2": (i32, [vp, i64, i64, vp, vp, vp, vp, vp]),
         "fp8_cast_block": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
+        "fp8_cast_block_pow2": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
         "fp8_scaled_gemm": (i32, [C.POINTER(GemmArgs), vp]),
     }
     for name, (res, args) in sig.items():
@@ -127,20 +131,36 @@ def fp8_amax(x, amax, stream=None):
                                    _stream(stream)))
 
 
+def _compute_scale(fn, amax, fmt, margin, scale, scale_inv, stream):
+    _check(fn.__name__,
+           fn(_ptr(amax, _F32, "amax"), amax.numel(), fmt, margin,
+              _ptr(scale, _F32, "scale"), _ptr(scale_inv, _F32, "scale_inv"), _stream(stream)))
+
+
 def fp8_compute_scale(amax, fmt, margin, scale, scale_inv, stream=None):
-    _check("fp8_compute_scale",
-           _L.fp8_compute_scale(_ptr(amax, _F32, "amax"), amax.numel(), fmt, margin,
-                                _ptr(scale, _F32, "scale"), _ptr(scale_inv, _F32, "scale_inv"),
-                                _stream(stream)))
+    _compute_scale(_L.fp8_compute_scale, amax, fmt, margin, scale, scale_inv, stream)
+
+
+def fp8_compute_scale_pow2(amax, fmt, margin, scale, scale_inv, stream=None):
+    _compute_scale(_L.fp8_compute_scale_pow2, amax, fmt, margin, scale, scale_inv, stream)
+
+
+def _history(fn, history, amax_new, fmt, margin, algo, scale, scale_inv, stream):
+    n, ln = history.shape
+    _check(fn.__name__,
+           fn(_ptr(history, _F32, "history"), n, ln, _ptr(amax_new, _F32, "amax_new"), fmt, margin,
+              algo, _ptr(scale, _F32, "scale"), _ptr(scale_inv, _F32, "scale_inv"), _stream(stream)))
 
 
 def fp8_amax_history_update(history, amax_new, fmt, margin, algo, scale, scale_inv, stream=None):
-    n, ln = history.shape
-    _check("fp8_amax_history_update",
-           _L.fp8_amax_history_update(_ptr(history, _F32, "history"), n, ln,
-                                      _ptr(amax_new, _F32, "amax_new"), fmt, margin, algo,
-                                      _ptr(scale, _F32, "scale"), _ptr(scale_inv, _F32, "scale_inv"),
-                                      _stream(stream)))
+    _history(_L.fp8_amax_history_update, history, amax_new, fmt, margin, algo, scale, scale_inv,
+             stream)
+
+
+def fp8_amax_history_update_pow2(history, amax_new, fmt, margin, algo, scale, scale_inv,
+                                 stream=None):
+    _history(_L.fp8_amax_history_update_pow2, history, amax_new, fmt, margin, algo, scale,
+             scale_inv, stream)
 
 
 def _cast(fn, x, scale, y, y_t, amax_out, stream):
@@ -158,12 +178,21 @@ def fp8_cast_e5m2(x, scale, y=None, y_t=None, amax_out=None, stream=None):
     _cast(_L.fp8_cast_e5m2, x, scale, y, y_t, amax_out, stream)
 
 
-def fp8_cast_block(x, fmt, tile, y=None, scale_inv=None, y_t=None, scale_inv_t=None, stream=None):
+def _cast_block(fn, x, fmt, tile, y, scale_inv, y_t, scale_inv_t, stream):
     rows, cols = _rc(x)
-    _check("fp8_cast_block",
-           _L.fp8_cast_block(_ptr(x, _BF16, "x"), rows, cols, fmt, tile, _ptr(y, _U8, "y"),
-                             _ptr(scale_inv, _F32, "scale_inv"), _ptr(y_t, _U8, "y_t"),
-                             _ptr(scale_inv_t, _F32, "scale_inv_t"), _stream(stream)))
+    _check(fn.__name__,
+           fn(_ptr(x, _BF16, "x"), rows, cols, fmt, tile, _ptr(y, _U8, "y"),
+              _ptr(scale_inv, _F32, "scale_inv"), _ptr(y_t, _U8, "y_t"),
+              _ptr(scale_inv_t, _F32, "scale_inv_t"), _stream(stream)))
+
+
+def fp8_cast_block(x, fmt, tile, y=None, scale_inv=None, y_t=None, scale_inv_t=None, stream=None):
+    _cast_block(_L.fp8_cast_block, x, fmt, tile, y, scale_inv, y_t, scale_inv_t, stream)
+
+
+def fp8_cast_block_pow2(x, fmt, tile, y=None, scale_inv=None, y_t=None, scale_inv_t=None,
+                        stream=None):
+    _cast_block(_L.fp8_cast_block_pow2, x, fmt, tile, y, scale_inv, y_t, scale_inv_t, stream)
 
 
 def fp8_scaled_gemm(A, a_fmt, a_scaling, a_scale_inv, B, b_fmt, b_scaling, b_scale_inv, D,

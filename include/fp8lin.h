@@ -11,6 +11,9 @@
  * Sources, cited by page title and section:
  *   [MPG]  "Mixed Precision LLM Training: The Complete Guide"
  *   [TALK] PyData Amsterdam 2026, "FP8 for pretraining" (talk abstract)
+ *   [P3]   "Training and inference of large language models using 8-bit
+ *          floating point" (arXiv 2309.17224 library entry: abstract and
+ *          reviews)
  *
  * Conventions for every entry point:
  *   - Pointers are caller-owned DEVICE memory on the current HIP device,
@@ -39,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 1
+#define FP8LIN_ABI_VERSION 2
 
 /* [MPG] "The precision formats", "FP8 E4M3", "FP8 E5M2": E4M3 = 4 exponent
  * and 3 mantissa bits, range about 2^-9..448; E5M2 = 5 and 2, range about
@@ -62,8 +65,17 @@ typedef enum { FP8_AMAX_MAX = 0, FP8_AMAX_MOST_RECENT = 1 } fp8_amax_algo;
 
 /* [MPG] "Per-row vs per-tensor scaling" and "DeepSeek FP8 training recipe
  * in detail > Block-wise scaling at 128 granularity": one scale per tensor,
- * per 128-element segment of a row (1x128), or per 128x128 block. */
-typedef enum { FP8_SCALE_TENSOR = 0, FP8_SCALE_1x128 = 1, FP8_SCALE_128x128 = 2 } fp8_scaling;
+ * per 128-element segment of a row (1x128), or per 128x128 block.
+ * The *_POW2 codes (GEMM operands only) are the same block layouts whose
+ * inverse scales are exact powers of two 2^e, |e| <= 126, as produced by
+ * fp8_cast_block_pow2 ([P3] exponent-bias scaling). */
+typedef enum {
+  FP8_SCALE_TENSOR = 0,
+  FP8_SCALE_1x128 = 1,
+  FP8_SCALE_128x128 = 2,
+  FP8_SCALE_1x128_POW2 = 3,
+  FP8_SCALE_128x128_POW2 = 4
+} fp8_scaling;
 
 typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_F32 = 1 } fp8_out_dtype;
 
@@ -108,6 +120,19 @@ fp8_status fp8_compute_scale(const float* amax, int64_t n, fp8_format fmt, int m
                              float* scale, float* scale_inv, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_compute_scale_pow2 -- current scaling with power-of-two scales.
+ * [P3] abstract and reviews: the scale is an exponent bias chosen from the
+ * tensor's maximum (FP8-AMAX), matching its range to the format's; the
+ * page does not print the formula.  Reading: scale = 2^e with e the largest
+ * integer such that amax * 2^e <= fmax (the amax lands in (fmax/2, fmax],
+ * nothing saturates), then e -= margin, e clamped to [-126, 126];
+ * scale_inv = 2^-e.  Both are exact, so dequantisation is exact.
+ * Arguments, fallback rule and errors as fp8_compute_scale.
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_compute_scale_pow2(const float* amax, int64_t n, fp8_format fmt, int margin,
+                                  float* scale, float* scale_inv, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fp8_amax_history_update -- delayed scaling from an amax history.
  * [MPG] "Delayed scaling (the default recipe)" and "History-based scaling":
  * the scale used at step t+1 comes from the maxima of the last `len` steps.
@@ -130,6 +155,14 @@ fp8_status fp8_amax_history_update(float* history, int64_t n, int64_t len,
                                    const float* amax_new, fp8_format fmt, int margin,
                                    fp8_amax_algo algo, float* scale, float* scale_inv,
                                    hipStream_t stream);
+
+/* fp8_amax_history_update_pow2 -- the same update with the power-of-two
+ * scale of fp8_compute_scale_pow2 ([P3] exponent bias) from the effective
+ * amax; arguments and errors as fp8_amax_history_update. */
+fp8_status fp8_amax_history_update_pow2(float* history, int64_t n, int64_t len,
+                                        const float* amax_new, fp8_format fmt, int margin,
+                                        fp8_amax_algo algo, float* scale, float* scale_inv,
+                                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * fp8_cast_e4m3 / fp8_cast_e5m2 -- per-tensor saturating RNE cast,
@@ -180,6 +213,16 @@ fp8_status fp8_cast_block(const void* x_bf16, int64_t rows, int64_t cols, fp8_fo
                           fp8_scaling tile, uint8_t* y, float* scale_inv, uint8_t* y_t,
                           float* scale_inv_t, hipStream_t stream);
 
+/* fp8_cast_block_pow2 -- fp8_cast_block with power-of-two tile scales (the
+ * rule of fp8_compute_scale_pow2 on each tile's amax, margin 0; [P3]
+ * exponent bias applied per DeepSeek-style block).  The scales it writes
+ * are valid FP8_SCALE_1x128_POW2 / FP8_SCALE_128x128_POW2 GEMM operands.
+ * Arguments (tile is FP8_SCALE_1x128 or FP8_SCALE_128x128) and errors as
+ * fp8_cast_block. */
+fp8_status fp8_cast_block_pow2(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                               fp8_scaling tile, uint8_t* y, float* scale_inv, uint8_t* y_t,
+                               float* scale_inv_t, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * fp8_scaled_gemm -- D[m][n] = sum_k A[m][k] * B[n][k] with FP8 operands,
  * FP32 accumulation and dequantisation.
@@ -196,7 +239,15 @@ fp8_status fp8_cast_block(const void* x_bf16, int64_t rows, int64_t cols, fp8_fo
  * Inverse-scale layouts (as produced by the casts):
  *   FP8_SCALE_TENSOR  : 1 float;
  *   FP8_SCALE_1x128   : [ceil(K/128)][rows]       (rows = M for A, N for B);
- *   FP8_SCALE_128x128 : [ceil(K/128)][ceil(rows/128)].
+ *   FP8_SCALE_128x128 : [ceil(K/128)][ceil(rows/128)];
+ *   FP8_SCALE_1x128_POW2, FP8_SCALE_128x128_POW2: the same layouts, every
+ *   value an exact power of two 2^e with |e| <= 126 (fp8_cast_block_pow2);
+ *   other values give unspecified (memory-safe) results.  When every
+ *   block-scaled operand is a *_POW2 one, the block scales are applied
+ *   inside the matrix instruction (exact power-of-two scaling of each
+ *   128-wide K block) and a per-tensor operand's scale in the epilogue;
+ *   mixed with a plain block operand, all block scales are promoted in
+ *   FP32 as for FP8_SCALE_1x128 / FP8_SCALE_128x128.
  * Result: tensor x tensor: D = (sum_k a b) * sa * sb; any block scaling:
  * D = sum_kb (sum_{k in kb} a b) * sa(m,kb) * sb(n,kb), each 128-wide K
  * block promoted into the FP32 accumulator.  D is [M][ldd], BF16 (round

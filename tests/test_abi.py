@@ -27,7 +27,8 @@ def test_header_declares_the_layer_calls():
     fns = declared_functions()
     for f in ["fp8_amax", "fp8_compute_scale", "fp8_amax_history_update", "fp8_cast_e4m3",
               "fp8_cast_e5m2", "fp8_cast_block", "fp8_scaled_gemm", "fp8_abi_version",
-              "fp8_status_string"]:
+              "fp8_status_string", "fp8_compute_scale_pow2", "fp8_amax_history_update_pow2",
+              "fp8_cast_block_pow2"]:
         assert f in fns
 
 
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.abi_version() == 1
+    assert L.abi_version() == 2
     for s in range(7):
         assert isinstance(L.status_string(s), str) and L.status_string(s)
     assert L.status_string(99) == "unknown status"
@@ -57,6 +58,10 @@ def test_host_validation_before_launch(L):
     assert f.fp8_compute_scale(None, 1, 0, 99, None, None, None) == 6
     assert f.fp8_compute_scale(None, -1, 0, 0, None, None, None) == 2
     assert f.fp8_compute_scale(None, 1, 0, 0, None, None, None) == 1
+    assert f.fp8_compute_scale_pow2(None, 1, 7, 0, None, None, None) == 6
+    assert f.fp8_compute_scale_pow2(None, 1, 0, 0, None, None, None) == 1
+    assert f.fp8_amax_history_update_pow2(None, 1, 0, None, 0, 0, 0, None, None, None) == 2
+    assert f.fp8_cast_block_pow2(None, 4, 4, 0, 0, None, None, None, None, None) == 6
     # history: len out of range, bad algo
     assert f.fp8_amax_history_update(None, 1, 0, None, 0, 0, 0, None, None, None) == 2
     assert f.fp8_amax_history_update(None, 1, 16, None, 0, 0, 5, None, None, None) == 6
@@ -87,7 +92,8 @@ def test_gemm_validation(L):
     assert _gemm(L, lda=264, K=256) == 3              # lda % 16
     assert _gemm(L, A=0x1008) == 3                    # A alignment
     assert _gemm(L, a_fmt=3) == 6
-    assert _gemm(L, b_scaling=4) == 6
+    assert _gemm(L, b_scaling=5) == 6
+    assert _gemm(L, K=272, b_scaling=4) == 2          # power-of-two block modes: K % 128 too
     assert _gemm(L, accumulate=1) == 4                # accumulate needs FP32 output
     assert _gemm(L, D=None) == 1
     assert _gemm(L, ldd=10) == 2
