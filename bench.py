@@ -19,7 +19,8 @@ Also reported (same JSON line):
                    algorithmic bytes) for this workload;
   blockwise     -- the block-wise path on 8192 tokens x 4096 in x 14336 out:
                    forward (1x128 activation tiles, 128x128 weight blocks)
-                   and backward (dgrad, wgrad with token-axis tiles);
+                   and backward (dgrad, wgrad with token-axis tiles), with
+                   binary32 block scales and with power-of-two ones;
   cpu_baseline  -- the plain CPU oracle timed on a bounded sample of the
                    same step (rank 0, N = 1 only).
 
@@ -238,14 +239,26 @@ def bench_blockwise(torch, L, datagen, dev, stream, d_bf16, time_launch, R):
     k["gemm_fwd_block"] = time_launch(lambda: L.fp8_scaled_gemm(xq, 0, 1, sx, wtq, 0, 2, swt, y), R)
     k["gemm_dgrad_block"] = time_launch(lambda: L.fp8_scaled_gemm(dyq, 1, 1, sdy, wq, 0, 2, sw, dx), R)
     k["gemm_wgrad_block"] = time_launch(lambda: L.fp8_scaled_gemm(xtq, 0, 1, sxt, dytq, 1, 1, sdyt, dw), R)
+    # the same path with power-of-two (exponent-bias) block scales: the GEMMs
+    # apply them inside the E8M0-scaled matrix instruction
+    k["cast_block_pow2_x_dual"] = time_launch(lambda: L.fp8_cast_block_pow2(x, 0, 1, xq, sx, xtq, sxt), R)
+    k["cast_block_pow2_w_128x128_both"] = time_launch(lambda: L.fp8_cast_block_pow2(w, 0, 2, wq, sw, wtq, swt), R)
+    k["cast_block_pow2_dy_dual"] = time_launch(lambda: L.fp8_cast_block_pow2(dy, 1, 1, dyq, sdy, dytq, sdyt), R)
+    k["gemm_fwd_block_pow2"] = time_launch(lambda: L.fp8_scaled_gemm(xq, 0, 3, sx, wtq, 0, 4, swt, y), R)
+    k["gemm_dgrad_block_pow2"] = time_launch(lambda: L.fp8_scaled_gemm(dyq, 1, 3, sdy, wq, 0, 4, sw, dx), R)
+    k["gemm_wgrad_block_pow2"] = time_launch(lambda: L.fp8_scaled_gemm(xtq, 0, 3, sxt, dytq, 1, 3, sdyt, dw), R)
     fl = 2.0 * T * DI * DO
     out = {"workload": "block-wise fwd (X 8192x4096 Student-t 1x128, W 4096x14336 128x128) + "
                        "bwd (dY 8192x14336 1x128 dual orientation; dgrad, wgrad)"}
-    for n in ("gemm_fwd_block", "gemm_dgrad_block", "gemm_wgrad_block"):
+    for n in ("gemm_fwd_block", "gemm_dgrad_block", "gemm_wgrad_block", "gemm_fwd_block_pow2",
+              "gemm_dgrad_block_pow2", "gemm_wgrad_block_pow2"):
         out[n] = {"tflops": round(fl / k[n] / 1e12, 2), "us": round(k[n] * 1e6, 1),
                   "pct_fp8_peak": round(100 * fl / k[n] / 1e12 / FP8_PEAK_TFLOPS, 2)}
     bytes_ = {"cast_block_x_dual": T * DI * (4 + 8 / 128), "cast_block_x_1x128": T * DI * (3 + 4 / 128),
-              "cast_block_w_128x128_both": DI * DO * 4.0, "cast_block_dy_dual": T * DO * (4 + 8 / 128)}
+              "cast_block_w_128x128_both": DI * DO * 4.0, "cast_block_dy_dual": T * DO * (4 + 8 / 128),
+              "cast_block_pow2_x_dual": T * DI * (4 + 8 / 128),
+              "cast_block_pow2_w_128x128_both": DI * DO * 4.0,
+              "cast_block_pow2_dy_dual": T * DO * (4 + 8 / 128)}
     for n, b in bytes_.items():
         out[n] = {"gbs": round(b / k[n] / 1e9, 1), "us": round(k[n] * 1e6, 1),
                   "pct_hbm_peak": round(100 * b / k[n] / 1e9 / HBM_PEAK_GBS, 2)}
@@ -253,6 +266,11 @@ def bench_blockwise(torch, L, datagen, dev, stream, d_bf16, time_launch, R):
            + k["gemm_fwd_block"] + k["gemm_dgrad_block"] + k["gemm_wgrad_block"])
     out["fwd_bwd_tflops_incl_casts"] = round(3 * fl / tot / 1e12, 2)
     out["fwd_bwd_ms"] = round(tot * 1e3, 3)
+    tot2 = (k["cast_block_pow2_x_dual"] + k["cast_block_pow2_w_128x128_both"]
+            + k["cast_block_pow2_dy_dual"] + k["gemm_fwd_block_pow2"] + k["gemm_dgrad_block_pow2"]
+            + k["gemm_wgrad_block_pow2"])
+    out["fwd_bwd_tflops_incl_casts_pow2"] = round(3 * fl / tot2 / 1e12, 2)
+    out["fwd_bwd_ms_pow2"] = round(tot2 * 1e3, 3)
     return out
 
 

@@ -158,9 +158,13 @@ fp8_status fp8_scaled_gemm(const fp8_gemm_args* a, hipStream_t stream) {
   if (a->M < 0 || a->N < 0 || a->K < 0) return FP8_ERR_SHAPE;
   if (!fmt_ok(a->a_fmt) || !fmt_ok(a->b_fmt)) return FP8_ERR_ARG;
   if (!scaling_ok(a->a_scaling) || !scaling_ok(a->b_scaling)) return FP8_ERR_ARG;
-  if (a->d_dtype != FP8_OUT_BF16 && a->d_dtype != FP8_OUT_F32) return FP8_ERR_ARG;
+  if (a->d_dtype != FP8_OUT_BF16 && a->d_dtype != FP8_OUT_F32 && a->d_dtype != FP8_OUT_E4M3 &&
+      a->d_dtype != FP8_OUT_E5M2)
+    return FP8_ERR_ARG;
+  const bool fp8_out = a->d_dtype == FP8_OUT_E4M3 || a->d_dtype == FP8_OUT_E5M2;
   if (a->accumulate != 0 && a->accumulate != 1) return FP8_ERR_ARG;
   if (a->accumulate && a->d_dtype != FP8_OUT_F32) return FP8_ERR_UNSUPPORTED;
+  if (!fp8_out && a->D_t != nullptr) return FP8_ERR_ARG;
   const bool block = !(a->a_scaling == FP8_SCALE_TENSOR && a->b_scaling == FP8_SCALE_TENSOR);
   if (a->K % (block ? 128 : 16) != 0) return FP8_ERR_SHAPE;
   if (a->M > 0 && a->N > 0) {
@@ -176,6 +180,11 @@ fp8_status fp8_scaled_gemm(const fp8_gemm_args* a, hipStream_t stream) {
       if (!aligned4(a->a_scale_inv) || !aligned4(a->b_scale_inv)) return FP8_ERR_ALIGN;
     }
     if (!aligned4(a->D)) return FP8_ERR_ALIGN;
+    if (fp8_out) {
+      if (a->d_scale == nullptr) return FP8_ERR_NULL;
+      if (!aligned4(a->d_scale)) return FP8_ERR_ALIGN;
+      if (a->D_t != nullptr && a->ldt < a->M) return FP8_ERR_SHAPE;
+    }
   }
   if (a->d_amax && !aligned4(a->d_amax)) return FP8_ERR_ALIGN;
   GemmParams p;
@@ -185,6 +194,12 @@ fp8_status fp8_scaled_gemm(const fp8_gemm_args* a, hipStream_t stream) {
   p.B = a->B; p.b_fmt = a->b_fmt; p.b_scaling = a->b_scaling; p.b_sinv = a->b_scale_inv;
   p.D = a->D; p.d_f32 = a->d_dtype == FP8_OUT_F32 ? 1 : 0;
   p.d_amax = a->d_amax; p.accumulate = a->accumulate;
+  p.d_fp8 = a->d_dtype == FP8_OUT_E4M3 ? 1 : (a->d_dtype == FP8_OUT_E5M2 ? 2 : 0);
+  p.d_scale = fp8_out ? a->d_scale : nullptr;
+  p.D_t = fp8_out ? a->D_t : nullptr;
+  p.ldt = a->ldt;
+  // the quantising epilogue lives in the large-tile kernel only
+  if (fp8_out && p.K > 0 && p.M > 0 && p.N > 0 && !gemm_big_supported(p)) return FP8_ERR_UNSUPPORTED;
   return launched(launch_gemm(p, stream));
 }
 

@@ -338,11 +338,72 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     if (p.b_scaling == 0) sb = p.b_sinv[0];
   }
   constexpr bool EPI_SCALE = !BLOCK || MX;
-  const int esz = p.d_f32 ? 4 : 2;
+  const int esz = p.d_fp8 ? 1 : (p.d_f32 ? 4 : 2);
   const bool staged = (m0 + BM <= M) && (n0 + BN <= N) && ((p.ldd * esz) % 16 == 0) &&
-                      ((reinterpret_cast<uintptr_t>(p.D) & 15u) == 0);
+                      ((reinterpret_cast<uintptr_t>(p.D) & 15u) == 0) &&
+                      (p.D_t == nullptr || ((p.ldt % 16 == 0) &&
+                                            ((reinterpret_cast<uintptr_t>(p.D_t) & 15u) == 0)));
   uint32_t amax_bits = 0;
-  if (staged) {
+  if (staged && p.d_fp8) {
+    // FP8 output: codes encode(fl32(v * d_scale)) of the dequantised value
+    // v, amax of |v|.  Codes go through the wavefront's LDS region twice:
+    // row-major (64 bytes per tile row, 16-byte chunk c at c ^ (r & 3)),
+    // then, for the transposed copy, column-major (row stride 144 bytes).
+    __syncthreads();
+    uint8_t* wl = &lds[0][0] + wave * 16384;
+    const float so = p.d_scale[0];
+    auto epi8 = [&](auto fmttag) {
+      constexpr int F = decltype(fmttag)::value;
+      uint32_t code[TI][TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[q] = EPI_SCALE ? (acc[i][j][q] * sa) * sb : acc[i][j][q];
+            const uint32_t b = __float_as_uint(v[q]) & 0x7FFFFFFFu;
+            amax_bits = b > amax_bits ? b : amax_bits;
+          }
+          code[i][j] = cvt4<F>(v[0] * so, v[1] * so, v[2] * so, v[3] * so);
+          const int r = 16 * i + l16;
+          *reinterpret_cast<uint32_t*>(wl + r * 64 + ((j ^ (r & 3)) << 4) + 4 * g) = code[i][j];
+        }
+      {
+        const int q = lane & 3, rr = lane >> 2;
+#pragma unroll
+        for (int t = 0; t < WTM / 16; ++t) {
+          const int r = 16 * t + rr;
+          const uint4 w = *reinterpret_cast<const uint4*>(wl + r * 64 + ((q ^ (r & 3)) << 4));
+          uint8_t* gp = reinterpret_cast<uint8_t*>(p.D) + (m0 + wm * WTM + r) * p.ldd + n0 +
+                        wn * WTN + q * 16;
+          *reinterpret_cast<uint4*>(gp) = w;
+        }
+      }
+      if (p.D_t) {
+        // same wavefront, LDS operations in order: the row-major reads above
+        // complete before these writes reuse the region
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              wl[(16 * j + 4 * g + q) * 144 + 16 * i + l16] = (uint8_t)(code[i][j] >> (8 * q));
+        const int c = lane & 7, rr = lane >> 3;
+#pragma unroll
+        for (int t = 0; t < WTN / 8; ++t) {
+          const int n = 8 * t + rr;
+          const uint4 w = *reinterpret_cast<const uint4*>(wl + n * 144 + 16 * c);
+          uint8_t* gp = p.D_t + (n0 + wn * WTN + n) * p.ldt + m0 + wm * WTM + 16 * c;
+          *reinterpret_cast<uint4*>(gp) = w;
+        }
+      }
+    };
+    if (p.d_fp8 == 1) epi8(std::integral_constant<int, 0>{});
+    else epi8(std::integral_constant<int, 1>{});
+  } else if (staged) {
     __syncthreads();   // every wavefront is done reading both stages
     uint8_t* wl = &lds[0][0] + wave * 16384;
     auto epi = [&](auto f32tag) {
@@ -417,7 +478,15 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
         for (int r = 0; r < 4; ++r) {
           if (n + r >= N) continue;
           float x = EPI_SCALE ? (acc[i][j][r] * sa) * sb : acc[i][j][r];
-          if (p.d_f32) {
+          if (p.d_fp8) {
+            const float xs = x * p.d_scale[0];
+            const uint8_t c = (uint8_t)((p.d_fp8 == 1 ? cvt4<0>(xs, 0.f, 0.f, 0.f)
+                                                      : cvt4<1>(xs, 0.f, 0.f, 0.f)) & 0xFFu);
+            reinterpret_cast<uint8_t*>(p.D)[m * p.ldd + n + r] = c;
+            if (p.D_t) p.D_t[(n + r) * p.ldt + m] = c;
+            const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;
+            amax_bits = b > amax_bits ? b : amax_bits;
+          } else if (p.d_f32) {
             float* d = reinterpret_cast<float*>(p.D) + m * p.ldd + n + r;
             if (p.accumulate) x = *d + x;
             *d = x;

@@ -229,6 +229,9 @@ __global__ void k_zero_out(GemmParams p) {
             __float_as_uint(reinterpret_cast<float*>(p.D)[m * p.ldd + n]) & 0x7FFFFFFFu;
         amax_bits = b > amax_bits ? b : amax_bits;
       }
+    } else if (p.d_fp8) {
+      reinterpret_cast<uint8_t*>(p.D)[m * p.ldd + n] = 0;
+      if (p.D_t) p.D_t[n * p.ldt + m] = 0;
     } else {
       reinterpret_cast<uint16_t*>(p.D)[m * p.ldd + n] = 0;
     }

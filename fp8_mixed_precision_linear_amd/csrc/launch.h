@@ -47,6 +47,10 @@ struct GemmParams {
   int d_f32;
   float* d_amax;  // zeroed by the caller first when given
   int accumulate;
+  int d_fp8;                // 0: BF16/FP32 output; 1: E4M3 codes; 2: E5M2 codes
+  const float* d_scale;     // FP8 output: quantisation scale (1 float)
+  uint8_t* D_t;             // FP8 output: optional transposed codes [N][ldt]
+  int64_t ldt;
 };
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
 E4M3, E5M2 = 0, 1
 SCALE_TENSOR, SCALE_1x128, SCALE_128x128 = 0, 1, 2
 SCALE_1x128_POW2, SCALE_128x128_POW2 = 3, 4
-OUT_BF16, OUT_F32 = 0, 1
+OUT_BF16, OUT_F32, OUT_E4M3, OUT_E5M2 = 0, 1, 2, 3
 AMAX_MAX, AMAX_MOST_RECENT = 0, 1
 
 STATUS = {0: "FP8_OK", 1: "FP8_ERR_NULL", 2: "FP8_ERR_SHAPE", 3: "FP8_ERR_ALIGN",
@@ -41,7 +41,8 @@ class GemmArgs(C.Structure):
                 ("B", C.c_void_p), ("b_fmt", C.c_int), ("b_scaling", C.c_int),
                 ("b_scale_inv", C.c_void_p),
                 ("D", C.c_void_p), ("d_dtype", C.c_int), ("d_amax", C.c_void_p),
-                ("accumulate", C.c_int)]
+                ("accumulate", C.c_int),
+                ("d_scale", C.c_void_p), ("D_t", C.c_void_p), ("ldt", C.c_int64)]
 
 
 def _load():
@@ -196,15 +197,25 @@ def fp8_cast_block_pow2(x, fmt, tile, y=None, scale_inv=None, y_t=None, scale_in
 
 
 def fp8_scaled_gemm(A, a_fmt, a_scaling, a_scale_inv, B, b_fmt, b_scaling, b_scale_inv, D,
-                    d_amax=None, accumulate=False, stream=None):
-    """D [M][N] (bf16 or fp32 tensor) = A [M][K] . B [N][K]^T with FP8 codes."""
+                    d_amax=None, accumulate=False, stream=None, d_scale=None, d_fmt=None, D_t=None):
+    """D [M][N] = A [M][K] . B [N][K]^T with FP8 codes.  D is a bf16 or fp32
+    tensor, or a uint8 tensor of FP8 codes (d_fmt E4M3 / E5M2, quantised
+    with d_scale; D_t optional [N][M] transposed codes)."""
     M, K = A.shape
     N = B.shape[0]
     if B.shape[1] != K or tuple(D.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, D {tuple(D.shape)}")
-    d_dtype = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[D.dtype]
+    if D.dtype in _U8:
+        if d_fmt not in (E4M3, E5M2):
+            raise ValueError("an FP8 output needs d_fmt (E4M3 or E5M2)")
+        d_dtype = OUT_E4M3 if d_fmt == E4M3 else OUT_E5M2
+        if D_t is not None and tuple(D_t.shape) != (N, M):
+            raise ValueError(f"D_t must be [{N}][{M}], got {tuple(D_t.shape)}")
+    else:
+        d_dtype = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[D.dtype]
     g = GemmArgs(M, N, K, K, K, N,
                  _ptr(A, _U8, "A"), a_fmt, a_scaling, _ptr(a_scale_inv, _F32, "a_scale_inv"),
                  _ptr(B, _U8, "B"), b_fmt, b_scaling, _ptr(b_scale_inv, _F32, "b_scale_inv"),
-                 _ptr(D, None, "D"), d_dtype, _ptr(d_amax, _F32, "d_amax"), 1 if accumulate else 0)
+                 _ptr(D, None, "D"), d_dtype, _ptr(d_amax, _F32, "d_amax"), 1 if accumulate else 0,
+                 _ptr(d_scale, _F32, "d_scale"), _ptr(D_t, _U8, "D_t"), M)
     _check("fp8_scaled_gemm", _L.fp8_scaled_gemm(C.byref(g), _stream(stream)))

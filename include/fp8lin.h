@@ -77,7 +77,9 @@ typedef enum {
   FP8_SCALE_128x128_POW2 = 4
 } fp8_scaling;
 
-typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_F32 = 1 } fp8_out_dtype;
+/* GEMM output: BF16, FP32, or FP8 codes quantised in the epilogue (the
+ * next layer's cast fused into this GEMM). */
+typedef enum { FP8_OUT_BF16 = 0, FP8_OUT_F32 = 1, FP8_OUT_E4M3 = 2, FP8_OUT_E5M2 = 3 } fp8_out_dtype;
 
 /* ABI version (FP8LIN_ABI_VERSION of the built library). */
 int fp8_abi_version(void);
@@ -254,12 +256,22 @@ fp8_status fp8_cast_block_pow2(const void* x_bf16, int64_t rows, int64_t cols, f
  * to nearest even) or FP32.  accumulate = 1 (FP32 output only) adds the
  * result to the existing D.  d_amax (nullable, 1 float) is overwritten with
  * max |D| of the stored output values.
+ * FP8 output (d_dtype FP8_OUT_E4M3 / FP8_OUT_E5M2; [TALK] outline
+ * "quantisation fusions"; [MPG] "Transformer Engine internals": the cast
+ * that the next layer would do, fused into this GEMM's epilogue): with v the
+ * FP32 result above (before any BF16 rounding), D[m][n] = encode(fl32(v *
+ * d_scale[0])) as in fp8_cast_e4m3 / e5m2; D_t (nullable) [N][ldt] receives
+ * the same codes transposed (the next layer's wgrad operand); d_amax is
+ * max |v| (the amax of the quantised tensor, for its delayed scaling).
+ * accumulate must be 0; requires ldt >= M when D_t is given.
  * Shape rules: M, N, K >= 0; K % 16 == 0 (tensor x tensor) or K % 128 == 0
  * (block modes); lda, ldb >= K and multiples of 16; ldd >= N; A, B 16-byte
  * aligned; D 4-byte aligned.  K == 0 gives D = 0 (or D unchanged when
  * accumulating).
- * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_ARG,
- * FP8_ERR_UNSUPPORTED (accumulate with BF16 output).
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_ARG (also
+ * D_t with a non-FP8 output), FP8_ERR_UNSUPPORTED (accumulate with a BF16
+ * or FP8 output; FP8 output with lda or ldb beyond the large-tile kernel's
+ * 32-bit panel offsets, i.e. 256 * ld >= 2^31).
  * ---------------------------------------------------------------------- */
 typedef struct {
   int64_t M, N, K;
@@ -269,6 +281,9 @@ typedef struct {
   void* D; fp8_out_dtype d_dtype;
   float* d_amax;
   int accumulate;
+  const float* d_scale;   /* FP8 output: quantisation scale (1 float); else ignored */
+  uint8_t* D_t;           /* FP8 output: transposed codes [N][ldt], or NULL */
+  int64_t ldt;
 } fp8_gemm_args;
 
 fp8_status fp8_scaled_gemm(const fp8_gemm_args* args, hipStream_t stream);

@@ -98,3 +98,9 @@ def test_gemm_validation(L):
     assert _gemm(L, D=None) == 1
     assert _gemm(L, ldd=10) == 2
     assert _gemm(L, M=-1) == 2
+    # FP8 output: scale required, no accumulation, D_t only with FP8 output
+    assert _gemm(L, d_dtype=4) == 6
+    assert _gemm(L, d_dtype=2) == 1                   # d_scale missing
+    assert _gemm(L, d_dtype=3, d_scale=0x6000, accumulate=1) == 4
+    assert _gemm(L, D_t=0x7000, ldt=64) == 6          # D_t with a BF16 output
+    assert _gemm(L, d_dtype=2, d_scale=0x6000, D_t=0x7000, ldt=10) == 2

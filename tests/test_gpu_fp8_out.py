@@ -1,0 +1,91 @@
+"""GPU parity of the quantising GEMM epilogue (FP8 output, the next layer's
+cast fused into the GEMM): the codes equal the saturating RNE encoding of
+the same kernel's FP32 result times the output scale (the decision is
+taken on the same binary32 value on both sides: the oracle's encoder on the
+GPU's FP32 output, which itself passes the oracle's gates), the transposed
+copy is the byte transpose, and the amax is max |FP32 result|; in tensor,
+block and power-of-two block modes, on whole and ragged tiles."""
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import Guarded, dev, gemm_check, say
+from tests.test_gpu_block_gemm import rand_codes, rand_scales
+from tests.test_gpu_pow2 import pow2_scales
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    from fp8_mixed_precision_linear_amd import lib
+    assert torch.cuda.is_available()
+    return lib
+
+
+def bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+SHAPES = [(256, 512, 384), (512, 256, 256), (200, 136, 384), (129, 257, 256), (1, 1, 128)]
+MODES = [(0, 0), (1, 2), (3, 4), (1, 1)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("out_fmt", [0, 1])
+@pytest.mark.parametrize("with_t", [True, False])
+def test_gemm_fp8_output(O, L, shape, mode, out_fmt, with_t):
+    M, N, K = shape
+    asc, bsc = mode
+    say("gemm fp8 out", shape, mode, out_fmt, with_t)
+    rng = np.random.default_rng(M + 3 * N + 7 * K + 11 * asc + bsc + 13 * out_fmt)
+    A = rand_codes(rng, (M, K), 0)
+    B = rand_codes(rng, (N, K), 1)
+    ora = {3: 1, 4: 2}
+    if asc >= 3:
+        sa, sb = pow2_scales(rng, ora[asc], M, K), pow2_scales(rng, ora[bsc], N, K)
+    else:
+        sa, sb = rand_scales(rng, asc, M, K), rand_scales(rng, bsc, N, K)
+    # FP32 result of the same kernel, checked against the oracle
+    D32 = Guarded((M, N), torch.float32)
+    L.fp8_scaled_gemm(dev(A), 0, asc, dev(sa), dev(B), 1, bsc, dev(sb), D32.t)
+    torch.cuda.synchronize()
+    D32.check()
+    G = D32.np()
+    ref = O.gemm(A, 0, ora.get(asc, asc), sa, B, 1, ora.get(bsc, bsc), sb, want=("E", "F", "D", "H"))
+    ok1, ok2, m1, m2 = gemm_check(G, ref, K, bf16=False)
+    assert ok1 and ok2, f"componentwise rel {m1:.3e}, model-bound ratio {m2:.3f}"
+    # an output scale that saturates the largest ~5% of the values
+    fmax = 448.0 if out_fmt == 0 else 57344.0
+    q95 = np.quantile(np.abs(G), 0.95) if G.size > 1 else float(np.abs(G).max())
+    s_out = np.float32(fmax / max(q95, 1e-30))
+    D8 = Guarded((M, N), torch.uint8)
+    Dt = Guarded((N, M), torch.uint8) if with_t else None
+    am = Guarded((1,), torch.float32)
+    L.fp8_scaled_gemm(dev(A), 0, asc, dev(sa), dev(B), 1, bsc, dev(sb), D8.t, d_amax=am.t,
+                      d_scale=dev(np.array([s_out], np.float32)), d_fmt=out_fmt,
+                      D_t=Dt.t if with_t else None)
+    torch.cuda.synchronize()
+    D8.check(); am.check()
+    want = O.encode((G * s_out).astype(np.float32), out_fmt).reshape(M, N)
+    assert np.array_equal(D8.np(), want)
+    if with_t:
+        Dt.check()
+        assert np.array_equal(Dt.np(), want.T)
+    assert bits(am.np()[0]) == bits(np.max(np.abs(G)) if G.size else np.float32(0))
+
+
+def test_gemm_fp8_output_k0(L):
+    M, N = 64, 48
+    D8 = Guarded((M, N), torch.uint8)
+    Dt = Guarded((N, M), torch.uint8)
+    D8.t.fill_(0x55); Dt.t.fill_(0x55)
+    one = torch.ones(1, device="cuda")
+    A = torch.empty((M, 0), dtype=torch.uint8, device="cuda")
+    B = torch.empty((N, 0), dtype=torch.uint8, device="cuda")
+    am = Guarded((1,), torch.float32)
+    L.fp8_scaled_gemm(A, 0, 0, one, B, 0, 0, one, D8.t, d_amax=am.t, d_scale=one, d_fmt=0, D_t=Dt.t)
+    torch.cuda.synchronize()
+    D8.check(); Dt.check(); am.check()
+    assert np.all(D8.np() == 0) and np.all(Dt.np() == 0) and am.np()[0] == 0.0
