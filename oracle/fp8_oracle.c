@@ -32,6 +32,7 @@
 #define O_SCALE_TENSOR 0
 #define O_SCALE_1x128 1
 #define O_SCALE_128x128 2
+#define O_SCALE_ROW 5   /* one scale per row of an operand, applied after the K sum */
 
 #define O_ALGO_MAX 0
 #define O_ALGO_MOST_RECENT 1
@@ -400,6 +401,44 @@ void o_cast_block_pow2(const uint16_t* x, int64_t rows, int64_t cols, int fmt, i
 }
 
 /* ------------------------------------------------------------------ */
+/* Row-wise cast.                                                      */
+/* [MPG] "Per-row vs per-tensor scaling": one scale per row (per       */
+/* output channel of a weight, per token of an activation), a middle   */
+/* ground between one scale per tensor and block scales.               */
+/* y [rows][cols]: each row r with s = o_compute_scale(amax of row r,  */
+/* fallback 1); sinv[r] = 1/s.                                         */
+/* y_t [cols][rows]: each column c of x (a row of the transposed       */
+/* operand) with its own scale from the column's amax; sinv_t[c].      */
+/* Either pair may be NULL.                                            */
+/* ------------------------------------------------------------------ */
+void o_cast_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* y,
+                    float* sinv, uint8_t* y_t, float* sinv_t) {
+  float s, si;
+  if (y || sinv)
+    for (int64_t r = 0; r < rows; ++r) {
+      float am = o_amax_bf16(x + r * cols, cols);
+      o_compute_scale(am, fmt, 0, 1.0f, &s, &si);
+      if (sinv) sinv[r] = si;
+      if (y)
+        for (int64_t c = 0; c < cols; ++c)
+          y[r * cols + c] = o_fp8_encode(o_bf16_to_f32(x[r * cols + c]) * s, fmt);
+    }
+  if (y_t || sinv_t)
+    for (int64_t c = 0; c < cols; ++c) {
+      float am = 0.0f;
+      for (int64_t r = 0; r < rows; ++r) {
+        float m = o_amax_bf16(x + r * cols + c, 1);
+        if (tot_gt(m, am)) am = m;
+      }
+      o_compute_scale(am, fmt, 0, 1.0f, &s, &si);
+      if (sinv_t) sinv_t[c] = si;
+      if (y_t)
+        for (int64_t r = 0; r < rows; ++r)
+          y_t[c * rows + r] = o_fp8_encode(o_bf16_to_f32(x[r * cols + c]) * s, fmt);
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* bf16 rounding of a binary32 value (round to nearest even; a NaN     */
 /* stays a quiet NaN).  Used to state the GEMM's BF16 output.          */
 /* [MPG] "Mixed-precision accumulation": the FP32 accumulation is cast */
@@ -456,6 +495,7 @@ typedef struct {
 
 static float scale_at(int scaling, const float* s, int64_t rows, int64_t row, int64_t kb) {
   if (scaling == O_SCALE_TENSOR) return s[0];
+  if (scaling == O_SCALE_ROW) return s[row];
   if (scaling == O_SCALE_1x128) return s[kb * rows + row];
   return s[kb * ((rows + 127) / 128) + row / 128];
 }
@@ -486,6 +526,12 @@ static int ilog2_u128(unsigned __int128 v) {
 static void* gemm_worker(void* p) {
   gemm_job* jb = (gemm_job*)p;
   const o_gemm_args* g = jb->g;
+  /* per-tensor and per-row scales do not depend on the K block: the sum
+   * over all of K is formed first and scaled once ([MPG] "Per-tensor
+   * scaling": the matmul result is multiplied by the inverse scales;
+   * "Per-row vs per-tensor scaling": one scale per row) */
+  const int epi = (g->a_scaling == O_SCALE_TENSOR || g->a_scaling == O_SCALE_ROW) &&
+                  (g->b_scaling == O_SCALE_TENSOR || g->b_scaling == O_SCALE_ROW);
   int64_t nkb = (g->K + 127) / 128;
   int qa = g->a_fmt == O_E4M3 ? 9 : 16, qb = g->b_fmt == O_E4M3 ? 9 : 16;
   int64_t* arow = (int64_t*)malloc(sizeof(int64_t) * (size_t)g->K);
@@ -539,7 +585,7 @@ static void* gemm_worker(void* p) {
         /* exact value of the block: S * 2^-(qa+qb) * sa * sb */
         long double Sl = (long double)S;               /* |S| < 2^65: exact to 2^-64 rel */
         long double blk = ldexpl(Sl, -(qa + qb));
-        if (g->a_scaling == O_SCALE_TENSOR && g->b_scaling == O_SCALE_TENSOR)
+        if (epi)
           e_sum += blk;                                  /* scales applied at the end */
         else
           e_sum += blk * (long double)sa * (long double)sb;
@@ -547,7 +593,7 @@ static void* gemm_worker(void* p) {
         /* FP32-accumulated partner */
         {
           float P = ldexpf((float)S, -(qa + qb));      /* (float)S rounds once (RNE) */
-          if (g->a_scaling == O_SCALE_TENSOR && g->b_scaling == O_SCALE_TENSOR) {
+          if (epi) {
             acc = acc + P;
           } else {
             float sab = sa * sb;
@@ -556,8 +602,9 @@ static void* gemm_worker(void* p) {
           }
         }
       }
-      if (g->a_scaling == O_SCALE_TENSOR && g->b_scaling == O_SCALE_TENSOR) {
-        float sa = g->a_sinv[0], sb = g->b_sinv[0];
+      if (epi) {
+        float sa = scale_at(g->a_scaling, g->a_sinv, g->M, m, 0);
+        float sb = scale_at(g->b_scaling, g->b_sinv, g->N, n, 0);
         e_sum = e_sum * (long double)sa * (long double)sb;
         acc = acc * sa;
         acc = acc * sb;

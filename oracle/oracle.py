@@ -20,6 +20,7 @@ import numpy as np
 
 E4M3, E5M2 = 0, 1
 TENSOR, S1x128, S128x128 = 0, 1, 2
+ROW = 5
 ALGO_MAX, ALGO_MOST_RECENT = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +88,9 @@ def lib():
         L.o_cast_transpose.restype = None
         L.o_cast_transpose.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_float, C.c_int,
                                        C.c_void_p, C.c_void_p]
+        L.o_cast_rowwise.restype = None
+        L.o_cast_rowwise.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int,
+                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
         for nm in ("o_cast_block", "o_cast_block_pow2"):
             getattr(L, nm).restype = None
             getattr(L, nm).argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int, C.c_int,
@@ -310,6 +314,26 @@ def cast_block(x_bf16, fmt: int, tile: int, want_y=True, want_t=False, plain=Fal
         out["y_t"], out["sinv_t"] = yt, sinvt
     if tile == S128x128:
         out["sinv"], out["sinv_t"] = sinv, sinvt
+    return out
+
+
+def cast_rowwise(x_bf16, fmt: int, want_y=True, want_t=False):
+    """Row-wise cast: y with one scale per row, y_t [cols][rows] with one
+    scale per column of x.  Returns dict with y, sinv, y_t, sinv_t."""
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    out = {}
+    y = np.empty((rows, cols), np.uint8) if want_y else None
+    s = np.empty(rows, np.float32) if want_y else None
+    yt = np.empty((cols, rows), np.uint8) if want_t else None
+    st = np.empty(cols, np.float32) if want_t else None
+    lib().o_cast_rowwise(_p(x), rows, cols, fmt, _p(y) if y is not None else None,
+                         _p(s) if s is not None else None, _p(yt) if yt is not None else None,
+                         _p(st) if st is not None else None)
+    if want_y:
+        out["y"], out["sinv"] = y, s
+    if want_t:
+        out["y_t"], out["sinv_t"] = yt, st
     return out
 
 
