@@ -16,7 +16,9 @@ Also reported (same JSON line):
                    HIP events around R launches captured in a HIP graph, on
                    the stream the kernels run on;
   kernels       -- per-kernel throughput (GEMM TFLOP/s, cast GB/s of
-                   algorithmic bytes) for this workload;
+                   algorithmic bytes) for this workload, plus the forward
+                   GEMM with its output quantised in the epilogue (E4M3,
+                   transposed copy, amax) beside the unfused GEMM + cast;
   blockwise     -- the block-wise path on 8192 tokens x 4096 in x 14336 out:
                    forward (1x128 activation tiles, 128x128 weight blocks)
                    and backward (dgrad, wgrad with token-axis tiles), with
@@ -162,6 +164,13 @@ def main():
     k["gemm_fwd_tensor"] = time_launch(lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y), R)
     k["gemm_dgrad_tensor"] = time_launch(lambda: L.fp8_scaled_gemm(dyq, 1, 0, sinv[2:3], wq, 0, 0, sinv[1:2], dx), R)
     k["gemm_wgrad_tensor"] = time_launch(lambda: L.fp8_scaled_gemm(xtq, 0, 0, sinv[0:1], dytq, 1, 0, sinv[2:3], dw), R)
+    # the forward GEMM with its output quantised in the epilogue (E4M3 codes,
+    # transposed copy, amax): the next layer's cast+transpose+amax fused in
+    y8, y8t = torch.empty((T, DO), **u8), torch.empty((DO, T), **u8)
+    am8 = torch.zeros(1, dtype=torch.float32, device=dev)
+    k["gemm_fwd_tensor_fp8out"] = time_launch(
+        lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y8, d_amax=am8,
+                                  d_scale=scale[0:1], d_fmt=0, D_t=y8t), R)
     k["cast_transpose_amax_e4m3"] = time_launch(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq, y_t=xtq, amax_out=amax[0:1]), R)
     k["cast_transpose_amax_e5m2"] = time_launch(lambda: L.fp8_cast_e5m2(dy0, scale[2:3], y=dyq, y_t=dytq, amax_out=amax[2:3]), R)
     k["cast_e4m3"] = time_launch(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq), R)
@@ -172,6 +181,9 @@ def main():
         "gemm_fwd_tensor": {"tflops": 2.0 * T * DI * DO / k["gemm_fwd_tensor"] / 1e12, "us": k["gemm_fwd_tensor"] * 1e6},
         "gemm_dgrad_tensor": {"tflops": 2.0 * T * DI * DO / k["gemm_dgrad_tensor"] / 1e12, "us": k["gemm_dgrad_tensor"] * 1e6},
         "gemm_wgrad_tensor": {"tflops": 2.0 * T * DI * DO / k["gemm_wgrad_tensor"] / 1e12, "us": k["gemm_wgrad_tensor"] * 1e6},
+        "gemm_fwd_tensor_fp8out": {"tflops": 2.0 * T * DI * DO / k["gemm_fwd_tensor_fp8out"] / 1e12,
+                                   "us": k["gemm_fwd_tensor_fp8out"] * 1e6,
+                                   "us_unfused_equivalent": (k["gemm_fwd_tensor"] + k["cast_transpose_amax_e4m3"]) * 1e6},
         "cast_transpose_amax_e4m3": {"gbs": 4.0 * nel / k["cast_transpose_amax_e4m3"] / 1e9, "us": k["cast_transpose_amax_e4m3"] * 1e6},
         "cast_transpose_amax_e5m2": {"gbs": 4.0 * nel / k["cast_transpose_amax_e5m2"] / 1e9, "us": k["cast_transpose_amax_e5m2"] * 1e6},
         "cast_e4m3": {"gbs": 3.0 * nel / k["cast_e4m3"] / 1e9, "us": k["cast_e4m3"] * 1e6},
