@@ -13,8 +13,9 @@ inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3
 inline bool fmt_ok(int f) { return f == FP8_E4M3 || f == FP8_E5M2; }
 inline bool scaling_ok(int s) {
   return s == FP8_SCALE_TENSOR || s == FP8_SCALE_1x128 || s == FP8_SCALE_128x128 ||
-         s == FP8_SCALE_1x128_POW2 || s == FP8_SCALE_128x128_POW2;
+         s == FP8_SCALE_1x128_POW2 || s == FP8_SCALE_128x128_POW2 || s == FP8_SCALE_ROW;
 }
+inline bool is_block(int s) { return s != FP8_SCALE_TENSOR && s != FP8_SCALE_ROW; }
 inline fp8_status launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
 
 fp8_status cast_common(const void* x, int64_t rows, int64_t cols, const float* scale, uint8_t* y,
@@ -153,6 +154,22 @@ fp8_status fp8_cast_block_pow2(const void* x_bf16, int64_t rows, int64_t cols, f
                            stream);
 }
 
+fp8_status fp8_cast_rowwise(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                            uint8_t* y, float* scale_inv, uint8_t* y_t, float* scale_inv_t,
+                            hipStream_t stream) {
+  if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
+  if (!fmt_ok(fmt)) return FP8_ERR_ARG;
+  if (rows == 0 || cols == 0) return FP8_OK;  // nothing to quantise
+  if ((y == nullptr) != (scale_inv == nullptr) || (y_t == nullptr) != (scale_inv_t == nullptr))
+    return FP8_ERR_NULL;
+  if (y == nullptr && y_t == nullptr) return FP8_ERR_NULL;
+  if (x_bf16 == nullptr) return FP8_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(y) || !aligned16(y_t)) return FP8_ERR_ALIGN;
+  if (!aligned4(scale_inv) || !aligned4(scale_inv_t)) return FP8_ERR_ALIGN;
+  return launched(launch_cast_rowwise(static_cast<const uint16_t*>(x_bf16), rows, cols, fmt, y,
+                                      scale_inv, y_t, scale_inv_t, stream));
+}
+
 fp8_status fp8_scaled_gemm(const fp8_gemm_args* a, hipStream_t stream) {
   if (a == nullptr) return FP8_ERR_NULL;
   if (a->M < 0 || a->N < 0 || a->K < 0) return FP8_ERR_SHAPE;
@@ -165,7 +182,10 @@ fp8_status fp8_scaled_gemm(const fp8_gemm_args* a, hipStream_t stream) {
   if (a->accumulate != 0 && a->accumulate != 1) return FP8_ERR_ARG;
   if (a->accumulate && a->d_dtype != FP8_OUT_F32) return FP8_ERR_UNSUPPORTED;
   if (!fp8_out && a->D_t != nullptr) return FP8_ERR_ARG;
-  const bool block = !(a->a_scaling == FP8_SCALE_TENSOR && a->b_scaling == FP8_SCALE_TENSOR);
+  const bool block = is_block(a->a_scaling) || is_block(a->b_scaling);
+  // per-row scales are applied after the K sum: not with block operands
+  if (block && (a->a_scaling == FP8_SCALE_ROW || a->b_scaling == FP8_SCALE_ROW))
+    return FP8_ERR_UNSUPPORTED;
   if (a->K % (block ? 128 : 16) != 0) return FP8_ERR_SHAPE;
   if (a->M > 0 && a->N > 0) {
     if (a->D == nullptr) return FP8_ERR_NULL;

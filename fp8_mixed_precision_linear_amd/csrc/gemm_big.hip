@@ -125,6 +125,9 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int row, int g) {
 // BLOCK : block-mode promotion per 128-wide K block;
 // SA_ROWS: A has 1x128 scales (one per row and K block), else one per wave;
 // SB_COL : B has 1x128 scales (one per column and K block), else one per wave.
+// Without BLOCK, SA_ROWS && SB_COL selects per-row scales applied in the
+// epilogue: A's inverse scale per row m (a_scaling 5) and B's per row n
+// (b_scaling 5), either of them possibly per tensor.
 template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL, bool MX>
 __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
@@ -338,6 +341,30 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     if (p.b_scaling == 0) sb = p.b_sinv[0];
   }
   constexpr bool EPI_SCALE = !BLOCK || MX;
+  constexpr bool ROWS = !BLOCK && SA_ROWS && SB_COL;
+  // per-row scales of this lane's outputs (rows clamped into D for edge tiles)
+  float rsa[ROWS ? TI : 1], rsb[ROWS ? TJ : 1][4];
+  if constexpr (ROWS) {
+    const int64_t astr = p.a_scaling == 5 ? 1 : 0, bstr = p.b_scaling == 5 ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int64_t m = m0 + wm * WTM + 16 * i + l16;
+      rsa[i] = p.a_sinv[(m < M ? m : M - 1) * astr];
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + wn * WTN + 16 * j + 4 * g + q;
+        rsb[j][q] = p.b_sinv[(n < N ? n : N - 1) * bstr];
+      }
+  }
+  // dequantised value of accumulator entry (i, j, q)
+  auto deq = [&](int i, int j, int q, float a) -> float {
+    if constexpr (ROWS) return (a * rsa[i]) * rsb[j][q];
+    else if constexpr (EPI_SCALE) return (a * sa) * sb;
+    else return a;
+  };
   const int esz = p.d_fp8 ? 1 : (p.d_f32 ? 4 : 2);
   const bool staged = (m0 + BM <= M) && (n0 + BN <= N) && ((p.ldd * esz) % 16 == 0) &&
                       ((reinterpret_cast<uintptr_t>(p.D) & 15u) == 0) &&
@@ -362,7 +389,7 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
           float v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            v[q] = EPI_SCALE ? (acc[i][j][q] * sa) * sb : acc[i][j][q];
+            v[q] = deq(i, j, q, acc[i][j][q]);
             const uint32_t b = __float_as_uint(v[q]) & 0x7FFFFFFFu;
             amax_bits = b > amax_bits ? b : amax_bits;
           }
@@ -423,7 +450,7 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
           for (int j = 0; j < TJ; ++j) {
             float v[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = EPI_SCALE ? (acc[i][j][q] * sa) * sb : acc[i][j][q];
+            for (int q = 0; q < 4; ++q) v[q] = deq(i, j, q, acc[i][j][q]);
             const int byte = (16 * j + 4 * g) * ES;
             uint8_t* dst = wl + r * ROW_BYTES + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
             if constexpr (F32) {
@@ -477,7 +504,7 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (n + r >= N) continue;
-          float x = EPI_SCALE ? (acc[i][j][r] * sa) * sb : acc[i][j][r];
+          float x = deq(i, j, r, acc[i][j][r]);
           if (p.d_fp8) {
             const float xs = x * p.d_scale[0];
             const uint8_t c = (uint8_t)((p.d_fp8 == 1 ? cvt4<0>(xs, 0.f, 0.f, 0.f)
@@ -534,14 +561,18 @@ hipError_t launch_block(const GemmParams& p, hipStream_t s) {
 }
 
 // Scaling codes: 0 per-tensor, 1 / 2 block (1x128 / 128x128) with any
-// binary32 scales, 3 / 4 the same blocks with power-of-two scales.  When
+// binary32 scales, 3 / 4 the same blocks with power-of-two scales, 5 one
+// scale per row (with per-tensor or per-row operands only).  When
 // every block-scaled operand has power-of-two scales the block scales go
 // into the matrix instruction; otherwise they are promoted in FP32 (a
 // power of two is a binary32 scale like any other).
 template <int AF, int BF>
 hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
-  const bool block = !(p.a_scaling == 0 && p.b_scaling == 0);
-  if (!block) return launch_one<AF, BF, false, false, false, false>(p, s);
+  const bool row_a = p.a_scaling == 5, row_b = p.b_scaling == 5;
+  const bool block = !((p.a_scaling == 0 || row_a) && (p.b_scaling == 0 || row_b));
+  if (!block)
+    return row_a || row_b ? launch_one<AF, BF, false, true, true, false>(p, s)
+                          : launch_one<AF, BF, false, false, false, false>(p, s);
   const bool mx = (p.a_scaling == 0 || p.a_scaling >= 3) && (p.b_scaling == 0 || p.b_scaling >= 3);
   return mx ? launch_block<AF, BF, true>(p, s) : launch_block<AF, BF, false>(p, s);
 }

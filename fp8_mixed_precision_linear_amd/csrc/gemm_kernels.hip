@@ -3,6 +3,9 @@
 // D[m][n] = sum_k A[m][k] B[n][k], A and B FP8 (E4M3 or E5M2, mixed allowed),
 // both K-contiguous, FP32 accumulation, dequantisation by inverse scales:
 //   tensor x tensor : D = (sum_k a b) * sa * sb, applied in the epilogue;
+//   per-row scales  : the same with sa = sa(m), sb = sb(n) ("Per-row vs
+//                     per-tensor scaling": one scale per row of an operand
+//                     factors out of the sum over k);
 //   block modes     : each 128-wide K block is one v_mfma_f32_16x16x128
 //                     per 16x16 output tile, accumulated from zero and
 //                     promoted into the FP32 accumulator as
@@ -179,12 +182,9 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmParams p) {
     __syncthreads();
   }
 
-  // ---- epilogue: dequantise (tensor mode), round, store, output amax
-  float sa = 1.0f, sb = 1.0f;
-  if constexpr (!BLOCK) {
-    sa = p.a_sinv[0];
-    sb = p.b_sinv[0];
-  }
+  // ---- epilogue: dequantise (per-tensor or per-row scales), round, store,
+  // output amax
+  const int64_t astr = p.a_scaling == 5 ? 1 : 0, bstr = p.b_scaling == 5 ? 1 : 0;
   uint32_t amax_bits = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(kThreads) k_gemm(GemmParams p) {
         const int64_t m = mrow0 + 16 * i + r, n = ncol0 + 16 * j;
         if (m >= M || n >= N) continue;
         float v = acc[i][j][r];
-        if constexpr (!BLOCK) v = (v * sa) * sb;
+        if constexpr (!BLOCK) v = (v * p.a_sinv[m * astr]) * p.b_sinv[n * bstr];
         if (p.d_f32) {
           float* d = reinterpret_cast<float*>(p.D) + m * p.ldd + n;
           if (p.accumulate) v = *d + v;
@@ -245,7 +245,8 @@ __global__ void k_zero_out(GemmParams p) {
 template <int AF, int BF>
 hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
   dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
-  const bool block = !(p.a_scaling == 0 && p.b_scaling == 0);
+  const bool block = !((p.a_scaling == 0 || p.a_scaling == 5) &&
+                       (p.b_scaling == 0 || p.b_scaling == 5));
   const bool sb_col = p.b_scaling == 1;
   if (!block)
     hipLaunchKernelGGL((k_gemm<AF, BF, false, false>), grid, dim3(kThreads), 0, s, p);
@@ -274,8 +275,8 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
   // this kernel promotes every block scale in FP32: power-of-two block
   // scales (codes 3, 4) are binary32 scales of the same layouts (1, 2)
   GemmParams q = p;
-  if (q.a_scaling >= 3) q.a_scaling -= 2;
-  if (q.b_scaling >= 3) q.b_scaling -= 2;
+  if (q.a_scaling == 3 || q.a_scaling == 4) q.a_scaling -= 2;
+  if (q.b_scaling == 3 || q.b_scaling == 4) q.b_scaling -= 2;
   if (q.a_fmt == 0 && q.b_fmt == 0) return launch_fmt<0, 0>(q, s);
   if (q.a_fmt == 1 && q.b_fmt == 0) return launch_fmt<1, 0>(q, s);
   if (q.a_fmt == 0 && q.b_fmt == 1) return launch_fmt<0, 1>(q, s);

@@ -35,6 +35,11 @@ hipError_t launch_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int 
                              int pow2, uint8_t* y, float* sinv, uint8_t* y_t, float* sinv_t,
                              hipStream_t s);
 
+// Row-wise cast: per-row scales for y, per-column scales for y_t (either
+// output pair may be absent).
+hipError_t launch_cast_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint8_t* y,
+                               float* sinv, uint8_t* y_t, float* sinv_t, hipStream_t s);
+
 struct GemmParams {
   int64_t M, N, K, lda, ldb, ldd;
   const uint8_t* A;

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
 E4M3, E5M2 = 0, 1
 SCALE_TENSOR, SCALE_1x128, SCALE_128x128 = 0, 1, 2
 SCALE_1x128_POW2, SCALE_128x128_POW2 = 3, 4
+SCALE_ROW = 5
 OUT_BF16, OUT_F32, OUT_E4M3, OUT_E5M2 = 0, 1, 2, 3
 AMAX_MAX, AMAX_MOST_RECENT = 0, 1
 
@@ -62,6 +63,7 @@ def _load():
         "fp8_cast_e5m2": (i32, [vp, i64, i64, vp, vp, vp, vp, vp]),
         "fp8_cast_block": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
         "fp8_cast_block_pow2": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
+        "fp8_cast_rowwise": (i32, [vp, i64, i64, i32, vp, vp, vp, vp, vp]),
         "fp8_scaled_gemm": (i32, [C.POINTER(GemmArgs), vp]),
     }
     for name, (res, args) in sig.items():
@@ -194,6 +196,14 @@ def fp8_cast_block(x, fmt, tile, y=None, scale_inv=None, y_t=None, scale_inv_t=N
 def fp8_cast_block_pow2(x, fmt, tile, y=None, scale_inv=None, y_t=None, scale_inv_t=None,
                         stream=None):
     _cast_block(_L.fp8_cast_block_pow2, x, fmt, tile, y, scale_inv, y_t, scale_inv_t, stream)
+
+
+def fp8_cast_rowwise(x, fmt, y=None, scale_inv=None, y_t=None, scale_inv_t=None, stream=None):
+    rows, cols = _rc(x)
+    _check("fp8_cast_rowwise",
+           _L.fp8_cast_rowwise(_ptr(x, _BF16, "x"), rows, cols, fmt, _ptr(y, _U8, "y"),
+                               _ptr(scale_inv, _F32, "scale_inv"), _ptr(y_t, _U8, "y_t"),
+                               _ptr(scale_inv_t, _F32, "scale_inv_t"), _stream(stream)))
 
 
 def fp8_scaled_gemm(A, a_fmt, a_scaling, a_scale_inv, B, b_fmt, b_scaling, b_scale_inv, D,

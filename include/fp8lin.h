@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 2
+#define FP8LIN_ABI_VERSION 3
 
 /* [MPG] "The precision formats", "FP8 E4M3", "FP8 E5M2": E4M3 = 4 exponent
  * and 3 mantissa bits, range about 2^-9..448; E5M2 = 5 and 2, range about
@@ -68,13 +68,17 @@ typedef enum { FP8_AMAX_MAX = 0, FP8_AMAX_MOST_RECENT = 1 } fp8_amax_algo;
  * per 128-element segment of a row (1x128), or per 128x128 block.
  * The *_POW2 codes (GEMM operands only) are the same block layouts whose
  * inverse scales are exact powers of two 2^e, |e| <= 126, as produced by
- * fp8_cast_block_pow2 ([P3] exponent-bias scaling). */
+ * fp8_cast_block_pow2 ([P3] exponent-bias scaling).
+ * FP8_SCALE_ROW (GEMM operands only): one scale per row of a K-contiguous
+ * operand, i.e. per token or per output channel, as produced by
+ * fp8_cast_rowwise ("Per-row vs per-tensor scaling"). */
 typedef enum {
   FP8_SCALE_TENSOR = 0,
   FP8_SCALE_1x128 = 1,
   FP8_SCALE_128x128 = 2,
   FP8_SCALE_1x128_POW2 = 3,
-  FP8_SCALE_128x128_POW2 = 4
+  FP8_SCALE_128x128_POW2 = 4,
+  FP8_SCALE_ROW = 5
 } fp8_scaling;
 
 /* GEMM output: BF16, FP32, or FP8 codes quantised in the epilogue (the
@@ -226,6 +230,30 @@ fp8_status fp8_cast_block_pow2(const void* x_bf16, int64_t rows, int64_t cols, f
                                float* scale_inv_t, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_cast_rowwise -- row-wise (per-channel) cast with scales computed on
+ * the fly.  [MPG] "Per-row vs per-tensor scaling": one scale per row of the
+ * matrix rather than one per tensor, so an outlier row or column only
+ * coarsens its own scale (torchao's row-wise recipe).
+ *   x_bf16       [rows][cols] bf16, 16-byte aligned.
+ *   y            [rows][cols]: row r quantised with s_r = fl32(fmax / amax_r),
+ *                amax_r = max_c |x[r][c]| (s_r = 1 for an all-zero or
+ *                non-finite row), codes as fp8_cast_e4m3 / e5m2;
+ *   scale_inv    [rows]: fl32(1 / s_r)  (an FP8_SCALE_ROW GEMM operand);
+ *   y_t          [cols][rows]: y_t[c][r] quantised with the scale of column
+ *                c, s_c = fl32(fmax / max_r |x[r][c]|) (same fallback) -- the
+ *                K-contiguous operand of the GEMMs that reduce over rows;
+ *   scale_inv_t  [cols]: fl32(1 / s_c).
+ *   Each of (y, scale_inv) and (y_t, scale_inv_t) is either both given or
+ *   both NULL, and at least one pair is given (an empty tensor needs no
+ *   pointers and enqueues nothing).  y, y_t 16-byte aligned; scale_inv_t
+ *   also serves as the column-maxima workspace while the call runs.
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_ARG (fmt).
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_cast_rowwise(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                            uint8_t* y, float* scale_inv, uint8_t* y_t, float* scale_inv_t,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fp8_scaled_gemm -- D[m][n] = sum_k A[m][k] * B[n][k] with FP8 operands,
  * FP32 accumulation and dequantisation.
  * [MPG] "Per-tensor scaling" (multiply the matmul result by the inverse
@@ -249,8 +277,11 @@ fp8_status fp8_cast_block_pow2(const void* x_bf16, int64_t rows, int64_t cols, f
  *   inside the matrix instruction (exact power-of-two scaling of each
  *   128-wide K block) and a per-tensor operand's scale in the epilogue;
  *   mixed with a plain block operand, all block scales are promoted in
- *   FP32 as for FP8_SCALE_1x128 / FP8_SCALE_128x128.
- * Result: tensor x tensor: D = (sum_k a b) * sa * sb; any block scaling:
+ *   FP32 as for FP8_SCALE_1x128 / FP8_SCALE_128x128;
+ *   FP8_SCALE_ROW     : [rows] (one per row of the operand; combines with
+ *   FP8_SCALE_TENSOR or FP8_SCALE_ROW only, else FP8_ERR_UNSUPPORTED).
+ * Result: tensor or row x tensor or row: D = ((sum_k a b) * sa(m)) * sb(n),
+ * one FP32 sum over all of K scaled in the epilogue; any block scaling:
  * D = sum_kb (sum_{k in kb} a b) * sa(m,kb) * sb(n,kb), each 128-wide K
  * block promoted into the FP32 accumulator.  D is [M][ldd], BF16 (round
  * to nearest even) or FP32.  accumulate = 1 (FP32 output only) adds the
@@ -264,14 +295,15 @@ fp8_status fp8_cast_block_pow2(const void* x_bf16, int64_t rows, int64_t cols, f
  * the same codes transposed (the next layer's wgrad operand); d_amax is
  * max |v| (the amax of the quantised tensor, for its delayed scaling).
  * accumulate must be 0; requires ldt >= M when D_t is given.
- * Shape rules: M, N, K >= 0; K % 16 == 0 (tensor x tensor) or K % 128 == 0
- * (block modes); lda, ldb >= K and multiples of 16; ldd >= N; A, B 16-byte
+ * Shape rules: M, N, K >= 0; K % 16 == 0 (tensor and row modes) or
+ * K % 128 == 0 (block modes); lda, ldb >= K and multiples of 16; ldd >= N; A, B 16-byte
  * aligned; D 4-byte aligned.  K == 0 gives D = 0 (or D unchanged when
  * accumulating).
  * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_ARG (also
  * D_t with a non-FP8 output), FP8_ERR_UNSUPPORTED (accumulate with a BF16
  * or FP8 output; FP8 output with lda or ldb beyond the large-tile kernel's
- * 32-bit panel offsets, i.e. 256 * ld >= 2^31).
+ * 32-bit panel offsets, i.e. 256 * ld >= 2^31; FP8_SCALE_ROW with a block
+ * operand).
  * ---------------------------------------------------------------------- */
 typedef struct {
   int64_t M, N, K;

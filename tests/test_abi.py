@@ -28,7 +28,7 @@ def test_header_declares_the_layer_calls():
     for f in ["fp8_amax", "fp8_compute_scale", "fp8_amax_history_update", "fp8_cast_e4m3",
               "fp8_cast_e5m2", "fp8_cast_block", "fp8_scaled_gemm", "fp8_abi_version",
               "fp8_status_string", "fp8_compute_scale_pow2", "fp8_amax_history_update_pow2",
-              "fp8_cast_block_pow2"]:
+              "fp8_cast_block_pow2", "fp8_cast_rowwise"]:
         assert f in fns
 
 
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.abi_version() == 2
+    assert L.abi_version() == 3
     for s in range(7):
         assert isinstance(L.status_string(s), str) and L.status_string(s)
     assert L.status_string(99) == "unknown status"
@@ -74,6 +74,17 @@ def test_host_validation_before_launch(L):
                             C.c_void_p(0x3000), None, None, None) == 6
     assert f.fp8_cast_block(C.c_void_p(0x1000), 4, 4, 0, 1, C.c_void_p(0x2000), None, None,
                             None, None) == 1
+    # row-wise cast: bad format, unpaired or missing outputs, misalignment, sizes
+    x, y, s = C.c_void_p(0x1000), C.c_void_p(0x2000), C.c_void_p(0x3000)
+    assert f.fp8_cast_rowwise(x, 4, 4, 2, y, s, None, None, None) == 6
+    assert f.fp8_cast_rowwise(x, 4, 4, 0, y, None, None, None, None) == 1
+    assert f.fp8_cast_rowwise(x, 4, 4, 0, None, None, y, None, None) == 1
+    assert f.fp8_cast_rowwise(x, 4, 4, 0, None, None, None, None, None) == 1
+    assert f.fp8_cast_rowwise(None, 4, 4, 0, y, s, None, None, None) == 1
+    assert f.fp8_cast_rowwise(x, 4, 4, 0, C.c_void_p(0x2008), s, None, None, None) == 3
+    assert f.fp8_cast_rowwise(x, 4, 4, 0, y, C.c_void_p(0x3002), None, None, None) == 3
+    assert f.fp8_cast_rowwise(x, -1, 4, 0, y, s, None, None, None) == 2
+    assert f.fp8_cast_rowwise(None, 0, 4, 0, None, None, None, None, None) == 0   # empty: no-op
 
 
 def _gemm(L, **kw):
@@ -92,7 +103,11 @@ def test_gemm_validation(L):
     assert _gemm(L, lda=264, K=256) == 3              # lda % 16
     assert _gemm(L, A=0x1008) == 3                    # A alignment
     assert _gemm(L, a_fmt=3) == 6
-    assert _gemm(L, b_scaling=5) == 6
+    assert _gemm(L, b_scaling=6) == 6
+    # per-row scales: with per-tensor or per-row operands only, K % 16
+    assert _gemm(L, a_scaling=5, b_scaling=1) == 4
+    assert _gemm(L, a_scaling=4, b_scaling=5) == 4
+    assert _gemm(L, K=100, a_scaling=5, b_scaling=5) == 2
     assert _gemm(L, K=272, b_scaling=4) == 2          # power-of-two block modes: K % 128 too
     assert _gemm(L, accumulate=1) == 4                # accumulate needs FP32 output
     assert _gemm(L, D=None) == 1
