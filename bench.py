@@ -19,10 +19,14 @@ Also reported (same JSON line):
                    algorithmic bytes) for this workload, plus the forward
                    GEMM with its output quantised in the epilogue (E4M3,
                    transposed copy, amax) beside the unfused GEMM + cast;
+  rowwise       -- per-row (per-channel) scaling on the same shapes and data:
+                   row-wise casts into both orientations and the three GEMMs
+                   with per-row scales;
   blockwise     -- the block-wise path on 8192 tokens x 4096 in x 14336 out:
                    forward (1x128 activation tiles, 128x128 weight blocks)
                    and backward (dgrad, wgrad with token-axis tiles), with
-                   binary32 block scales and with power-of-two ones;
+                   binary32 block scales and with power-of-two ones, and
+                   the row-wise path on the same shapes;
   cpu_baseline  -- the plain CPU oracle timed on a bounded sample of the
                    same step (rank 0, N = 1 only).
 
@@ -190,6 +194,21 @@ def main():
         "amax": {"gbs": 2.0 * nel / k["amax"] / 1e9, "us": k["amax"] * 1e6},
         "history_update": {"us": k["history_update"] * 1e6},
     }
+    # ---- row-wise (per-channel) scaling on the same shapes: each operand
+    # cast once into both orientations (row scales, column scales), the
+    # three GEMMs with per-row scales applied in the epilogue
+    f32 = dict(dtype=torch.float32, device=dev)
+    sxr, sxc = torch.empty(T, **f32), torch.empty(DI, **f32)
+    swr, swc = torch.empty(DI, **f32), torch.empty(DO, **f32)
+    sdr, sdc = torch.empty(T, **f32), torch.empty(DO, **f32)
+    k["cast_rowwise_x"] = time_launch(lambda: L.fp8_cast_rowwise(x0, 0, xq, sxr, xtq, sxc), R)
+    k["cast_rowwise_w"] = time_launch(lambda: L.fp8_cast_rowwise(w0, 0, wq, swr, wtq, swc), R)
+    k["cast_rowwise_dy"] = time_launch(lambda: L.fp8_cast_rowwise(dy0, 1, dyq, sdr, dytq, sdc), R)
+    k["gemm_fwd_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(xq, 0, 5, sxr, wtq, 0, 5, swc, y), R)
+    k["gemm_dgrad_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(dyq, 1, 5, sdr, wq, 0, 5, swr, dx), R)
+    k["gemm_wgrad_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(xtq, 0, 5, sxc, dytq, 1, 5, sdc, dw), R)
+    rowwise = rowwise_summary(k, T, DI, DO, "row-wise fwd+dgrad+wgrad, tokens 4096, in 4096, out 4096 "
+                                           "(delayed-scaling workload data, step 0)")
     g_avg = (k["gemm_fwd_tensor"] + k["gemm_dgrad_tensor"] + k["gemm_wgrad_tensor"]) / 3
     g_ach = 2.0 * T * DI * DO / g_avg / 1e12
     roofline = {"bound": "mfma",
@@ -218,6 +237,7 @@ def main():
         "roofline": roofline,
         "kernels": {n: {kk: round(vv, 2) for kk, vv in d.items()} for n, d in kernels.items()},
     }
+    result["rowwise"] = rowwise
     if blockwise is not None:
         result["blockwise"] = blockwise
     if not args.no_cpu:
@@ -283,6 +303,39 @@ def bench_blockwise(torch, L, datagen, dev, stream, d_bf16, time_launch, R):
             + k["gemm_wgrad_block_pow2"])
     out["fwd_bwd_tflops_incl_casts_pow2"] = round(3 * fl / tot2 / 1e12, 2)
     out["fwd_bwd_ms_pow2"] = round(tot2 * 1e3, 3)
+    # row-wise scaling on the same shapes and data
+    sxr, sxc = torch.empty(T, **f32), torch.empty(DI, **f32)
+    swr, swc = torch.empty(DI, **f32), torch.empty(DO, **f32)
+    sdr, sdc = torch.empty(T, **f32), torch.empty(DO, **f32)
+    r = {}
+    r["cast_rowwise_x"] = time_launch(lambda: L.fp8_cast_rowwise(x, 0, xq, sxr, xtq, sxc), R)
+    r["cast_rowwise_w"] = time_launch(lambda: L.fp8_cast_rowwise(w, 0, wq, swr, wtq, swc), R)
+    r["cast_rowwise_dy"] = time_launch(lambda: L.fp8_cast_rowwise(dy, 1, dyq, sdr, dytq, sdc), R)
+    r["gemm_fwd_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(xq, 0, 5, sxr, wtq, 0, 5, swc, y), R)
+    r["gemm_dgrad_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(dyq, 1, 5, sdr, wq, 0, 5, swr, dx), R)
+    r["gemm_wgrad_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(xtq, 0, 5, sxc, dytq, 1, 5, sdc, dw), R)
+    out["rowwise"] = rowwise_summary(r, T, DI, DO, "row-wise on the same shapes and data")
+    return out
+
+
+def rowwise_summary(k, T, DI, DO, workload):
+    """Row-wise path: GEMM TFLOP/s, cast GB/s of algorithmic bytes (bf16 read
+    once, both FP8 orientations written once, row and column scales), and
+    the whole fwd+bwd including the three casts."""
+    fl = 2.0 * T * DI * DO
+    out = {"workload": workload}
+    for n in ("gemm_fwd_rowwise", "gemm_dgrad_rowwise", "gemm_wgrad_rowwise"):
+        out[n] = {"tflops": round(fl / k[n] / 1e12, 2), "us": round(k[n] * 1e6, 1),
+                  "pct_fp8_peak": round(100 * fl / k[n] / 1e12 / FP8_PEAK_TFLOPS, 2)}
+    shapes = {"cast_rowwise_x": (T, DI), "cast_rowwise_w": (DI, DO), "cast_rowwise_dy": (T, DO)}
+    for n, (a, b) in shapes.items():
+        by = a * b * 4.0 + 4.0 * (a + b)
+        out[n] = {"gbs": round(by / k[n] / 1e9, 1), "us": round(k[n] * 1e6, 1),
+                  "pct_hbm_peak": round(100 * by / k[n] / 1e9 / HBM_PEAK_GBS, 2)}
+    tot = sum(k[n] for n in list(shapes) + ["gemm_fwd_rowwise", "gemm_dgrad_rowwise",
+                                            "gemm_wgrad_rowwise"])
+    out["fwd_bwd_tflops_incl_casts"] = round(3 * fl / tot / 1e12, 2)
+    out["fwd_bwd_ms"] = round(tot * 1e3, 3)
     return out
 
 

@@ -11,16 +11,19 @@
 //       operand of the GEMMs that reduce over rows (weight gradient).
 // Codes as in the per-tensor cast (saturating RNE, NaN -> 0x7F | sign).
 //
-// Fast path (cols % 8 == 0 and cols <= 32768; with y_t also rows % 16 == 0
-// and cols % 16 == 0), HBM-bound, x read twice when y_t is wanted:
-//   1. the column maxima are zeroed (binary32 patterns kept in scale_inv_t);
-//   2. row kernel: each group of NT threads owns whole rows (G groups per
+// Fast path (cols % 8 == 0 and cols <= 32768; with y_t also rows >= 64,
+// rows % 16 == 0 and cols % 16 == 0), HBM-bound, x read twice when y_t is
+// wanted:
+//   1. row kernel: each group of NT threads owns whole rows (G groups per
 //      workgroup, a persistent grid walks the rows), holds a row in
 //      registers (8 bf16 per thread per chunk of 8*NT columns): row amax,
 //      scale, cast, 8-byte stores.  Each thread keeps running maxima of its
 //      columns over the rows it visits; at the end they are combined across
-//      the groups in LDS and leave as one filtered device atomic per column
-//      per workgroup;
+//      the groups in LDS and stored as the workgroup's partial column maxima
+//      (16-bit |bf16| patterns, one row of [grid][cols]) in the memory of
+//      y_t, which is written only later (grid <= rows / 2, so they fit);
+//   2. the partial maxima are reduced per column into scale_inv_t (binary32
+//      patterns of the column amax) -- no device atomics anywhere;
 //   3. cast + transpose with per-column scales: 128 x 128 tiles through LDS
 //      (the per-tensor kernel's layout), scales from the column maxima;
 //   4. the column maxima become scale_inv_t in place.
@@ -69,7 +72,7 @@ __device__ __forceinline__ void st_nt8(uint2 v, void* p) {
 template <int FMT, int NT, int G, int NCH, bool WANT_Y, bool COLS>
 __global__ void __launch_bounds__(NT * G)
     k_rw_rows(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t iters,
-              uint8_t* __restrict__ y, float* __restrict__ sinv, float* __restrict__ colmax) {
+              uint8_t* __restrict__ y, float* __restrict__ sinv, uint32_t* __restrict__ part) {
   constexpr int NW = NT / 64;
   constexpr int CH = 8 * NT;
   __shared__ uint32_t red[2][G][NW];
@@ -122,9 +125,10 @@ __global__ void __launch_bounds__(NT * G)
   }
 
   if constexpr (COLS) {
-    // combine the groups' column maxima in LDS, one chunk at a time, then
-    // one filtered atomic per column (consecutive lanes, consecutive columns)
+    // combine the groups' column maxima in LDS, one chunk at a time; the
+    // workgroup's row of partials: packed pairs, part[blockIdx.x][cols / 2]
     __shared__ uint32_t cmx[G][4 * NT];
+    uint32_t* prow = part + (int64_t)blockIdx.x * (cols >> 1);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if ((int64_t)c * CH >= cols) break;   // uniform
@@ -137,11 +141,7 @@ __global__ void __launch_bounds__(NT * G)
 #pragma unroll
         for (int g2 = 1; g2 < G; ++g2) pk = absmax_pk(pk, cmx[g2][d]);
         const int64_t col = (int64_t)c * CH + 2 * d;
-        if (col < cols) {
-          const uint32_t lo = (pk & 0xFFFFu) << 16, hi = pk & 0xFFFF0000u;
-          if (lo) atomic_max_bits(colmax + col, lo);
-          if (hi) atomic_max_bits(colmax + col + 1, hi);
-        }
+        if (col < cols) prow[col >> 1] = pk;
       }
     }
   }
@@ -235,6 +235,29 @@ __global__ void __launch_bounds__(1024)
   }
 }
 
+// Partial column maxima [nparts][cols / 2] (packed pairs) -> binary32
+// patterns of the column amax in colmax.  Block (16 pairs: 64 contiguous
+// bytes per partial row) x (64 slices of the partial rows), combined in
+// LDS: many small blocks, so the reads are spread over the whole chip.
+__global__ void __launch_bounds__(1024)
+    k_rw_colmax(const uint32_t* __restrict__ part, int64_t nparts, int64_t cols,
+                float* __restrict__ colmax) {
+  __shared__ uint32_t red[64][17];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t pairs = cols >> 1;
+  const int64_t pr = (int64_t)blockIdx.x * 16 + tx;
+  uint32_t m = 0;
+  if (pr < pairs)
+    for (int64_t b = ty; b < nparts; b += 64) m = absmax_pk(m, part[b * pairs + pr]);
+  red[ty][tx] = m;
+  __syncthreads();
+  if (ty == 0 && pr < pairs) {
+    for (int k = 1; k < 64; ++k) m = absmax_pk(m, red[k][tx]);
+    colmax[2 * pr] = __uint_as_float((m & 0xFFFFu) << 16);
+    colmax[2 * pr + 1] = __uint_as_float(m & 0xFFFF0000u);
+  }
+}
+
 // Column maxima -> scale_inv_t, in place.
 template <int FMT>
 __global__ void k_rw_finalize(float* __restrict__ colmax, int64_t cols) {
@@ -299,25 +322,41 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Launches the row kernel; with part != nullptr the workgroups' partial
+// column maxima go to part ([grid][cols / 2] dwords, grid <= rows / 2 so
+// that they fit in y_t's rows * cols bytes).  Returns the grid in *grid_out.
 template <int FMT, int NT, int G, int NCH>
 hipError_t launch_rows(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* y, float* sinv,
-                       float* colmax, int per_cu, hipStream_t s) {
+                       uint32_t* part, int per_cu, int64_t* grid_out, hipStream_t s) {
   const int64_t groups = (rows + G - 1) / G;
   int64_t grid = device_cu_count() * per_cu;
   if (grid > groups) grid = groups;
+  if (part && grid > rows / 2) grid = rows / 2;
   if (grid < 1) grid = 1;
+  *grid_out = grid;
   const int64_t iters = (groups + grid - 1) / grid;
   dim3 g((unsigned)grid), b(NT * G);
-  if (y && colmax)
+  if (y && part)
     hipLaunchKernelGGL((k_rw_rows<FMT, NT, G, NCH, true, true>), g, b, 0, s, x, rows, cols, iters,
-                       y, sinv, colmax);
+                       y, sinv, part);
   else if (y)
     hipLaunchKernelGGL((k_rw_rows<FMT, NT, G, NCH, true, false>), g, b, 0, s, x, rows, cols, iters,
-                       y, sinv, colmax);
+                       y, sinv, part);
   else
     hipLaunchKernelGGL((k_rw_rows<FMT, NT, G, NCH, false, true>), g, b, 0, s, x, rows, cols, iters,
-                       y, sinv, colmax);
+                       y, sinv, part);
   return hipGetLastError();
+}
+
+// Row kernel for one of the row lengths <= 4096, 8192, 16384, 32768
+// columns (8 * NT * NCH); part as in launch_rows.
+template <int FMT>
+hipError_t launch_rows_any(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* y, float* sinv,
+                           uint32_t* part, int64_t* grid, hipStream_t s) {
+  if (cols <= 4096) return launch_rows<FMT, 256, 4, 2>(x, rows, cols, y, sinv, part, 2, grid, s);
+  if (cols <= 8192) return launch_rows<FMT, 256, 4, 4>(x, rows, cols, y, sinv, part, 1, grid, s);
+  if (cols <= 16384) return launch_rows<FMT, 256, 2, 8>(x, rows, cols, y, sinv, part, 1, grid, s);
+  return launch_rows<FMT, 512, 1, 8>(x, rows, cols, y, sinv, part, 1, grid, s);
 }
 
 template <int FMT>
@@ -325,49 +364,44 @@ hipError_t launch_rw(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* y, 
                      uint8_t* yt, float* sinv_t, hipStream_t s) {
   const int64_t cus = device_cu_count();
   const bool fast_rows = cols % 8 == 0 && cols <= 32768;
-  const bool fast_t = yt == nullptr ||
-                      (rows % 16 == 0 && cols % 16 == 0 &&
-                       (rows + 127) / 128 * ((cols + 127) / 128) < (1LL << 30));
-  if (!(fast_rows && fast_t)) {
-    hipError_t e = hipSuccess;
-    if (y) {
-      int64_t grid = rows < cus * 8 ? rows : cus * 8;
+  const bool fast_t = rows >= 64 && rows % 16 == 0 && cols % 16 == 0 &&
+                      (rows + 127) / 128 * ((cols + 127) / 128) < (1LL << 30);
+  hipError_t e = hipSuccess;
+  int64_t grid = 0;
+  if (!yt || !(fast_rows && fast_t)) {
+    if (y && fast_rows) {
+      e = launch_rows_any<FMT>(x, rows, cols, y, sinv, nullptr, &grid, s);
+    } else if (y) {
+      grid = rows < cus * 8 ? rows : cus * 8;
       hipLaunchKernelGGL((k_rw_rows_generic<FMT>), dim3((unsigned)grid), dim3(256), 0, s, x, rows,
                          cols, y, sinv);
       e = hipGetLastError();
-      if (e != hipSuccess) return e;
     }
-    if (yt) {
-      int64_t grid = (cols + 255) / 256;
-      if (grid > cus * 8) grid = cus * 8;
-      hipLaunchKernelGGL((k_rw_cols_generic<FMT>), dim3((unsigned)grid), dim3(256), 0, s, x, rows,
-                         cols, yt, sinv_t);
-      e = hipGetLastError();
-    }
-    return e;
+    if (e != hipSuccess || !yt) return e;
+    grid = (cols + 255) / 256;
+    if (grid > cus * 8) grid = cus * 8;
+    hipLaunchKernelGGL((k_rw_cols_generic<FMT>), dim3((unsigned)grid), dim3(256), 0, s, x, rows,
+                       cols, yt, sinv_t);
+    return hipGetLastError();
   }
-  float* colmax = yt ? sinv_t : nullptr;
-  if (colmax) {
-    hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(colmax), cols, 0u, s);
-    if (e != hipSuccess) return e;
-  }
-  // row lengths: <= 4096, 8192, 16384, 32768 columns (8 * NT * NCH)
-  hipError_t e;
-  if (cols <= 4096) e = launch_rows<FMT, 256, 4, 2>(x, rows, cols, y, sinv, colmax, 2, s);
-  else if (cols <= 8192) e = launch_rows<FMT, 256, 4, 4>(x, rows, cols, y, sinv, colmax, 1, s);
-  else if (cols <= 16384) e = launch_rows<FMT, 256, 2, 8>(x, rows, cols, y, sinv, colmax, 1, s);
-  else e = launch_rows<FMT, 512, 1, 8>(x, rows, cols, y, sinv, colmax, 1, s);
-  if (e != hipSuccess || !yt) return e;
+  // y_t wanted on the fast path: partial column maxima in y_t's memory
+  uint32_t* part = reinterpret_cast<uint32_t*>(yt);
+  e = launch_rows_any<FMT>(x, rows, cols, y, sinv, part, &grid, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_rw_colmax, dim3((unsigned)((cols / 2 + 15) / 16)), dim3(1024), 0, s, part,
+                     grid, cols, sinv_t);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int tiles_c = (int)((cols + 127) / 128);
   const int ntiles = (int)((rows + 127) / 128) * tiles_c;
   int64_t blocks = (ntiles + 3) / 4;
   if (blocks > cus) blocks = cus;
   hipLaunchKernelGGL((k_rw_transpose<FMT>), dim3((unsigned)blocks), dim3(1024), 0, s, x, rows,
-                     cols, colmax, yt, tiles_c, ntiles);
+                     cols, sinv_t, yt, tiles_c, ntiles);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_rw_finalize<FMT>), dim3((unsigned)((cols + 255) / 256)), dim3(256), 0, s,
-                     colmax, cols);
+                     sinv_t, cols);
   return hipGetLastError();
 }
 

@@ -132,6 +132,10 @@ template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL, bool MX>
 __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
   __shared__ float su_tab[NWAVES][MAX_KB];
+  constexpr bool ROWS = !BLOCK && SA_ROWS && SB_COL;
+  // per-row scales of the tile's 256 D rows and 256 D columns, staged once
+  // (rows clamped into D for edge tiles); read in the epilogue
+  __shared__ float rs_tab[ROWS ? BM + BN : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -157,6 +161,15 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   // DMA: wave w fills rows 32w .. 32w+31 of A and of B, 8 rows per
   // instruction; lane p lands in row 8*it + (p >> 3), stored chunk p & 7
   const int lrow = 32 * wave + (lane >> 3);
+
+  if constexpr (ROWS) {   // thread t < BM: A's scale of D row m0 + t; else B's of column n0 + t - BM
+    static_assert(THREADS == BM + BN, "one row scale per thread");
+    const bool is_a = tid < BM;
+    const int64_t r = is_a ? m0 + tid : n0 + (tid - BM);
+    const int64_t lim = is_a ? M : N;
+    const int row_mode = is_a ? p.a_scaling == 5 : p.b_scaling == 5;
+    rs_tab[tid] = (is_a ? p.a_sinv : p.b_sinv)[row_mode ? (r < lim ? r : lim - 1) : 0];
+  }
 
   // ---- per-wavefront table of the uniform part of each K block's scale
   if constexpr (BLOCK && !(SA_ROWS && SB_COL)) {
@@ -341,27 +354,11 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     if (p.b_scaling == 0) sb = p.b_sinv[0];
   }
   constexpr bool EPI_SCALE = !BLOCK || MX;
-  constexpr bool ROWS = !BLOCK && SA_ROWS && SB_COL;
-  // per-row scales of this lane's outputs (rows clamped into D for edge tiles)
-  float rsa[ROWS ? TI : 1], rsb[ROWS ? TJ : 1][4];
-  if constexpr (ROWS) {
-    const int64_t astr = p.a_scaling == 5 ? 1 : 0, bstr = p.b_scaling == 5 ? 1 : 0;
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int64_t m = m0 + wm * WTM + 16 * i + l16;
-      rsa[i] = p.a_sinv[(m < M ? m : M - 1) * astr];
-    }
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * WTN + 16 * j + 4 * g + q;
-        rsb[j][q] = p.b_sinv[(n < N ? n : N - 1) * bstr];
-      }
-  }
+  if constexpr (ROWS) __syncthreads();   // the tile's row scales are in rs_tab
   // dequantised value of accumulator entry (i, j, q)
   auto deq = [&](int i, int j, int q, float a) -> float {
-    if constexpr (ROWS) return (a * rsa[i]) * rsb[j][q];
+    if constexpr (ROWS)
+      return (a * rs_tab[wm * WTM + 16 * i + l16]) * rs_tab[BM + wn * WTN + 16 * j + 4 * g + q];
     else if constexpr (EPI_SCALE) return (a * sa) * sb;
     else return a;
   };

@@ -245,8 +245,10 @@ fp8_status fp8_cast_block_pow2(const void* x_bf16, int64_t rows, int64_t cols, f
  *   scale_inv_t  [cols]: fl32(1 / s_c).
  *   Each of (y, scale_inv) and (y_t, scale_inv_t) is either both given or
  *   both NULL, and at least one pair is given (an empty tensor needs no
- *   pointers and enqueues nothing).  y, y_t 16-byte aligned; scale_inv_t
- *   also serves as the column-maxima workspace while the call runs.
+ *   pointers and enqueues nothing).  y, y_t 16-byte aligned.  The memory
+ *   of y_t and scale_inv_t also serves as workspace while the call runs
+ *   (column maxima); both hold their final values once the call's work
+ *   has completed in stream order.
  * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_ARG (fmt).
  * ---------------------------------------------------------------------- */
 fp8_status fp8_cast_rowwise(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,

@@ -45,8 +45,8 @@ def special_input(rng, rows, cols):
     return x
 
 
-CAST_SHAPES = [(64, 384), (200, 4096), (128, 8192), (48, 16384), (32, 32768), (16, 40000),
-               (33, 100), (1, 8), (4096, 16), (4112, 256)]
+CAST_SHAPES = [(64, 384), (200, 4096), (128, 8192), (48, 16384), (80, 16384), (64, 32768),
+               (32, 32768), (16, 40000), (33, 100), (1, 8), (4096, 16), (4112, 256)]
 
 
 @pytest.mark.parametrize("shape", CAST_SHAPES)
@@ -77,8 +77,8 @@ def test_cast_rowwise(O, L, shape, fmt, want):
 
 
 def test_cast_rowwise_repeated_calls(O, L):
-    """The column maxima live in scale_inv_t during the call: a second call
-    on new data into the same buffers starts from zero again."""
+    """Partial column maxima live in y_t and scale_inv_t during the call: a
+    second call on new data into the same buffers starts afresh."""
     rows, cols = 256, 512
     outs = (torch.empty((rows, cols), dtype=torch.uint8, device="cuda"),
             torch.empty(rows, device="cuda"),
