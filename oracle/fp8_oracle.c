@@ -439,6 +439,119 @@ void o_cast_rowwise(const uint16_t* x, int64_t rows, int64_t cols, int fmt, uint
 }
 
 /* ------------------------------------------------------------------ */
+/* Stochastic rounding.                                                */
+/* [MPG] "Stochastic rounding": instead of rounding to nearest, round  */
+/* up or down at random according to the remainder, which makes the   */
+/* rounded value unbiased.  [TALK] outline: "rounding techniques".     */
+/*                                                                     */
+/* Random words: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel  */
+/* random numbers: as easy as 1, 2, 3", SC 2011), a counter-based      */
+/* generator: ten rounds of two 32x32->64 multiplications whose halves */
+/* are mixed with the other words and the round key; the key advances  */
+/* by the two Weyl constants after each round.                          */
+/* ------------------------------------------------------------------ */
+void o_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int round = 0; round < 10; ++round) {
+    uint64_t p0 = (uint64_t)0xD2511F53u * c0;   /* the two multipliers of Philox4x32 */
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    uint32_t n1 = (uint32_t)p1;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    uint32_t n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    k0 += 0x9E3779B9u;                          /* golden ratio */
+    k1 += 0xBB67AE85u;                          /* sqrt(3) - 1 */
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The random word of element i of a tensor (row-major index) under
+ * (seed, offset): word i % 4 of Philox4x32-10 with counter
+ * (i / 4, offset) as four little-endian 32-bit words and key seed. */
+uint32_t o_sr_word(uint64_t seed, uint64_t offset, uint64_t i) {
+  uint64_t g = i >> 2;
+  uint32_t ctr[4] = {(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)offset, (uint32_t)(offset >> 32)};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  o_philox4x32_10(ctr, key, out);
+  return out[i & 3];
+}
+
+/* Stochastic rounding of a binary32 value to an FP8 code with the random
+ * word r.  |v| >= fmax and +-Inf saturate to +-fmax, NaN gives 0x7F|sign
+ * (as the round-to-nearest encoder).  Otherwise, with lo the largest FP8
+ * magnitude <= |v| and hi the next one, the magnitude becomes hi when
+ * r < (|v| - lo) / (hi - lo) * 2^32 (probability (|v| - lo) / (hi - lo)
+ * for a uniform r, exactly when that ratio is a multiple of 2^-32), else
+ * lo; the sign of v is kept.  lo is found by a search over the codes. */
+uint8_t o_fp8_encode_sr(float v, int fmt, uint32_t r) {
+  uint32_t sign = (b_of(v) >> 31) ? 0x80u : 0x00u;
+  double a = fabs((double)v);
+  double fmax = o_fp8_max(fmt);
+  if (isnan(v)) return (uint8_t)(0x7F | sign);
+  int top = fmt == O_E4M3 ? 0x7E : 0x7B;          /* largest finite magnitude code */
+  if (a >= fmax) return (uint8_t)(top | sign);
+  int lo = 0, hi = top;                            /* decode(lo) <= a < decode(hi) */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (o_fp8_decode((uint8_t)mid, fmt) <= a) lo = mid; else hi = mid;
+  }
+  double dlo = o_fp8_decode((uint8_t)lo, fmt), dhi = o_fp8_decode((uint8_t)(lo + 1), fmt);
+  double q = (a - dlo) / (dhi - dlo);              /* exact: a has 24 bits, dhi - dlo = 2^k */
+  int up = (double)r < ldexp(q, 32);
+  return (uint8_t)((up ? lo + 1 : lo) | (int)sign);
+}
+
+/* Per-tensor cast with stochastic rounding: y[i] = sr(fl32(x[i] * s), word i)
+ * and, when y_t is given, y_t[c][r] = y[r][c] (the same word per element). */
+void o_cast_sr(const uint16_t* x, int64_t rows, int64_t cols, float s, int fmt, uint64_t seed,
+               uint64_t offset, uint8_t* y, uint8_t* y_t) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      int64_t i = r * cols + c;
+      float v = o_bf16_to_f32(x[i]) * s;
+      uint8_t q = o_fp8_encode_sr(v, fmt, o_sr_word(seed, offset, (uint64_t)i));
+      if (y) y[i] = q;
+      if (y_t) y_t[c * rows + r] = q;
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Exponentially weighted amax for delayed scaling.                    */
+/* [MPG] "Delayed scaling (the default recipe)": the scale used at step */
+/* t is the one right for step t-1, or an exponentially weighted        */
+/* average of recent steps.  Reading: the average is taken of the amax  */
+/* and the scale follows from it by the current-scaling rule:          */
+/*   amax_new == 0 or non-finite: nothing changes;                      */
+/*   ewma == 0 (no step seen yet): ewma = amax_new;                     */
+/*   otherwise ewma = fl32(fl32(beta * ewma) + fl32(fl32(1 - beta) *    */
+/*   amax_new));                                                        */
+/*   then scale, scale_inv from ewma with the margin (kept on failure). */
+/* ------------------------------------------------------------------ */
+void o_amax_ewma_update(float* ewma, int64_t n, const float* amax_new, float beta, int fmt,
+                        int margin, float* scale, float* scale_inv) {
+  float omb = 1.0f - beta;
+  for (int64_t i = 0; i < n; ++i) {
+    float a = amax_new[i];
+    if (!(a > 0.0f) || isinf(a)) continue;
+    if (ewma[i] == 0.0f) {
+      ewma[i] = a;
+    } else {
+      float t0 = beta * ewma[i];
+      float t1 = omb * a;
+      ewma[i] = t0 + t1;
+    }
+    float sc, si;
+    if (o_compute_scale(ewma[i], fmt, margin, 0.0f, &sc, &si)) {
+      scale[i] = sc;
+      scale_inv[i] = si;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
 /* bf16 rounding of a binary32 value (round to nearest even; a NaN     */
 /* stays a quiet NaN).  Used to state the GEMM's BF16 output.          */
 /* [MPG] "Mixed-precision accumulation": the FP32 accumulation is cast */

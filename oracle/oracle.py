@@ -95,6 +95,18 @@ def lib():
             getattr(L, nm).restype = None
             getattr(L, nm).argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int, C.c_int,
                                        C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+        L.o_philox4x32_10.restype = None
+        L.o_philox4x32_10.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p]
+        L.o_sr_word.restype = C.c_uint32
+        L.o_sr_word.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64]
+        L.o_fp8_encode_sr.restype = C.c_uint8
+        L.o_fp8_encode_sr.argtypes = [C.c_float, C.c_int, C.c_uint32]
+        L.o_cast_sr.restype = None
+        L.o_cast_sr.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_float, C.c_int, C.c_uint64,
+                                C.c_uint64, C.c_void_p, C.c_void_p]
+        L.o_amax_ewma_update.restype = None
+        L.o_amax_ewma_update.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_float, C.c_int,
+                                         C.c_int, C.c_void_p, C.c_void_p]
         L.o_f32_to_bf16.restype = C.c_uint16
         L.o_f32_to_bf16.argtypes = [C.c_float]
         L.o_encode_array.restype = None
@@ -218,6 +230,45 @@ def history_update(history: np.ndarray, amax_new, fmt: int, margin: int, algo: i
     n, ln = history.shape
     fn = lib().o_history_update_pow2 if pow2 else lib().o_history_update
     fn(_p(history), n, ln, _p(a), fmt, margin, algo, _p(scale), _p(scale_inv))
+
+
+def amax_ewma_update(ewma: np.ndarray, amax_new, beta: float, fmt: int, margin: int,
+                     scale: np.ndarray, scale_inv: np.ndarray):
+    """In-place on ewma [n], scale [n], scale_inv [n] (float32)."""
+    for a in (ewma, scale, scale_inv):
+        assert a.dtype == np.float32 and a.flags.c_contiguous
+    am = _c(amax_new, np.float32)
+    lib().o_amax_ewma_update(_p(ewma), ewma.size, _p(am), float(beta), fmt, margin, _p(scale),
+                             _p(scale_inv))
+
+
+# -------------------------------------------------- stochastic rounding ---
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = _c(np.asarray(ctr, np.uint32), np.uint32)
+    k = _c(np.asarray(key, np.uint32), np.uint32)
+    out = np.empty(4, np.uint32)
+    lib().o_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def sr_word(seed: int, offset: int, i: int) -> int:
+    return int(lib().o_sr_word(seed, offset, i))
+
+
+def encode_sr(v: float, fmt: int, r: int) -> int:
+    return int(lib().o_fp8_encode_sr(float(np.float32(v)), fmt, int(r)))
+
+
+def cast_sr(x_bf16, s: float, fmt: int, seed: int, offset: int = 0, want_y=True, want_t=False):
+    """Per-tensor cast with stochastic rounding; returns (y, y_t) (None where
+    not wanted)."""
+    x = _c(x_bf16, np.uint16)
+    rows, cols = x.shape
+    y = np.empty((rows, cols), np.uint8) if want_y else None
+    yt = np.empty((cols, rows), np.uint8) if want_t else None
+    lib().o_cast_sr(_p(x), rows, cols, float(np.float32(s)), fmt, seed, offset,
+                    _p(y) if y is not None else None, _p(yt) if yt is not None else None)
+    return y, yt
 
 
 # -------------------------------------------------------------- casts ---
