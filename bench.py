@@ -16,7 +16,8 @@ Also reported (same JSON line):
                    HIP events around R launches captured in a HIP graph, on
                    the stream the kernels run on;
   kernels       -- per-kernel throughput (GEMM TFLOP/s, cast GB/s of
-                   algorithmic bytes) for this workload, plus the forward
+                   algorithmic bytes) for this workload (also dY's cast with
+                   stochastic rounding and the EWMA scale update), plus the forward
                    GEMM with its output quantised in the epilogue (E4M3,
                    transposed copy, amax) beside the unfused GEMM + cast;
   rowwise       -- per-row (per-channel) scaling on the same shapes and data:
@@ -177,9 +178,13 @@ def main():
                                   d_scale=scale[0:1], d_fmt=0, D_t=y8t), R)
     k["cast_transpose_amax_e4m3"] = time_launch(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq, y_t=xtq, amax_out=amax[0:1]), R)
     k["cast_transpose_amax_e5m2"] = time_launch(lambda: L.fp8_cast_e5m2(dy0, scale[2:3], y=dyq, y_t=dytq, amax_out=amax[2:3]), R)
+    k["cast_transpose_amax_e5m2_sr"] = time_launch(
+        lambda: L.fp8_cast_sr(dy0, 1, scale[2:3], 1234, 0, y=dyq, y_t=dytq, amax_out=amax[2:3]), R)
     k["cast_e4m3"] = time_launch(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq), R)
     k["amax"] = time_launch(lambda: L.fp8_amax(x0, amax[0:1]), R)
     k["history_update"] = time_launch(lambda: L.fp8_amax_history_update(hist[0:2], amax[0:2], 0, 0, 0, scale[0:2], sinv[0:2]), R)
+    ewma = torch.zeros(3, dtype=torch.float32, device=dev)
+    k["ewma_update"] = time_launch(lambda: L.fp8_amax_ewma_update(ewma, amax, 0.9, 0, 0, scale, sinv), R)
     nel = T * DI
     kernels = {
         "gemm_fwd_tensor": {"tflops": 2.0 * T * DI * DO / k["gemm_fwd_tensor"] / 1e12, "us": k["gemm_fwd_tensor"] * 1e6},
@@ -190,9 +195,12 @@ def main():
                                    "us_unfused_equivalent": (k["gemm_fwd_tensor"] + k["cast_transpose_amax_e4m3"]) * 1e6},
         "cast_transpose_amax_e4m3": {"gbs": 4.0 * nel / k["cast_transpose_amax_e4m3"] / 1e9, "us": k["cast_transpose_amax_e4m3"] * 1e6},
         "cast_transpose_amax_e5m2": {"gbs": 4.0 * nel / k["cast_transpose_amax_e5m2"] / 1e9, "us": k["cast_transpose_amax_e5m2"] * 1e6},
+        "cast_transpose_amax_e5m2_sr": {"gbs": 4.0 * nel / k["cast_transpose_amax_e5m2_sr"] / 1e9,
+                                        "us": k["cast_transpose_amax_e5m2_sr"] * 1e6},
         "cast_e4m3": {"gbs": 3.0 * nel / k["cast_e4m3"] / 1e9, "us": k["cast_e4m3"] * 1e6},
         "amax": {"gbs": 2.0 * nel / k["amax"] / 1e9, "us": k["amax"] * 1e6},
         "history_update": {"us": k["history_update"] * 1e6},
+        "ewma_update": {"us": k["ewma_update"] * 1e6},
     }
     # ---- row-wise (per-channel) scaling on the same shapes: each operand
     # cast once into both orientations (row scales, column scales), the

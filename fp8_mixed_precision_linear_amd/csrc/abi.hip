@@ -19,7 +19,8 @@ inline bool is_block(int s) { return s != FP8_SCALE_TENSOR && s != FP8_SCALE_ROW
 inline fp8_status launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH; }
 
 fp8_status cast_common(const void* x, int64_t rows, int64_t cols, const float* scale, uint8_t* y,
-                       uint8_t* y_t, float* amax_out, int fmt, hipStream_t stream) {
+                       uint8_t* y_t, float* amax_out, int fmt, int sr, uint64_t seed,
+                       uint64_t offset, hipStream_t stream) {
   if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
   const bool empty = rows == 0 || cols == 0;
   if (!empty && (x == nullptr || scale == nullptr || (y == nullptr && y_t == nullptr)))
@@ -27,7 +28,7 @@ fp8_status cast_common(const void* x, int64_t rows, int64_t cols, const float* s
   if (!aligned16(x) || !aligned16(y) || !aligned16(y_t)) return FP8_ERR_ALIGN;
   if (amax_out && !aligned4(amax_out)) return FP8_ERR_ALIGN;
   return launched(launch_cast(static_cast<const uint16_t*>(x), rows, cols, scale, fmt, y, y_t,
-                              amax_out, stream));
+                              amax_out, sr, seed, offset, stream));
 }
 
 }  // namespace
@@ -132,12 +133,34 @@ fp8_status fp8_amax_history_update_pow2(float* history, int64_t n, int64_t len,
 
 fp8_status fp8_cast_e4m3(const void* x_bf16, int64_t rows, int64_t cols, const float* scale,
                          uint8_t* y, uint8_t* y_t, float* amax_out, hipStream_t stream) {
-  return cast_common(x_bf16, rows, cols, scale, y, y_t, amax_out, FP8_E4M3, stream);
+  return cast_common(x_bf16, rows, cols, scale, y, y_t, amax_out, FP8_E4M3, 0, 0, 0, stream);
 }
 
 fp8_status fp8_cast_e5m2(const void* x_bf16, int64_t rows, int64_t cols, const float* scale,
                          uint8_t* y, uint8_t* y_t, float* amax_out, hipStream_t stream) {
-  return cast_common(x_bf16, rows, cols, scale, y, y_t, amax_out, FP8_E5M2, stream);
+  return cast_common(x_bf16, rows, cols, scale, y, y_t, amax_out, FP8_E5M2, 0, 0, 0, stream);
+}
+
+fp8_status fp8_cast_sr(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                       const float* scale, uint64_t seed, uint64_t offset, uint8_t* y,
+                       uint8_t* y_t, float* amax_out, hipStream_t stream) {
+  if (!fmt_ok(fmt)) return FP8_ERR_ARG;
+  return cast_common(x_bf16, rows, cols, scale, y, y_t, amax_out, fmt, 1, seed, offset, stream);
+}
+
+fp8_status fp8_amax_ewma_update(float* ewma, int64_t n, const float* amax_new, float beta,
+                                fp8_format fmt, int margin, float* scale, float* scale_inv,
+                                hipStream_t stream) {
+  if (n < 0) return FP8_ERR_SHAPE;
+  if (!fmt_ok(fmt) || margin < 0 || margin > 64 || !(beta >= 0.0f && beta <= 1.0f))
+    return FP8_ERR_ARG;
+  if (n > 0 && (ewma == nullptr || amax_new == nullptr || scale == nullptr ||
+                scale_inv == nullptr))
+    return FP8_ERR_NULL;
+  if (!aligned4(ewma) || !aligned4(amax_new) || !aligned4(scale) || !aligned4(scale_inv))
+    return FP8_ERR_ALIGN;
+  return launched(launch_ewma_update(ewma, n, amax_new, beta, fmt, margin, scale, scale_inv,
+                                     stream));
 }
 
 fp8_status fp8_cast_block(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,

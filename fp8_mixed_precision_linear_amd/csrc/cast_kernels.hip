@@ -7,6 +7,11 @@
 // [TALK] = PyData Amsterdam 2026 "FP8 for pretraining", outline 05:00-15:00:
 //   E4M3 for forward activations and weights, E5M2 for gradients.
 //
+// With SR the rounding is stochastic ([MPG] "Stochastic rounding"): each
+// element draws its word of a Philox4x32-10 block (fp8_device.h) from its
+// row-major index, the seed and the offset; the transposed copy holds the
+// same codes.
+//
 // Memory-bound kernels: every byte is read or written once, with 16-byte
 // accesses.  The transposed copy goes through LDS as dwords that each hold
 // 4 codes of one column (a 4x4 byte transpose in registers), with a 16-byte
@@ -45,10 +50,11 @@ __device__ __forceinline__ void block_amax_to(float* out, uint32_t v) {
 // loads, one 16-byte store).  Any n; the last n % 16 values are handled by
 // the first threads of block 0.
 // ---------------------------------------------------------------------
-template <int FMT, bool AMAX>
+template <int FMT, bool AMAX, bool SR>
 __global__ void __launch_bounds__(kBig)
     k_cast_flat(const uint16_t* __restrict__ x, int64_t n, const float* __restrict__ scale,
-                uint8_t* __restrict__ y, float* __restrict__ amax) {
+                uint8_t* __restrict__ y, float* __restrict__ amax, uint64_t seed,
+                uint64_t offset) {
   const float s = *scale;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint4* yv = reinterpret_cast<uint4*>(y);
@@ -62,8 +68,15 @@ __global__ void __launch_bounds__(kBig)
       m = absmax_pk(m, a.x); m = absmax_pk(m, a.y); m = absmax_pk(m, a.z); m = absmax_pk(m, a.w);
       m = absmax_pk(m, b.x); m = absmax_pk(m, b.y); m = absmax_pk(m, b.z); m = absmax_pk(m, b.w);
     }
-    uint2 qa = cvt8_bf16<FMT>(a, s);
-    uint2 qb = cvt8_bf16<FMT>(b, s);
+    uint2 qa, qb;
+    if constexpr (SR) {   // elements 16u .. 16u+15: blocks 4u .. 4u+3
+      qa = cvt8_bf16_sr<FMT>(a, s, sr_block(4 * u, seed, offset), sr_block(4 * u + 1, seed, offset));
+      qb = cvt8_bf16_sr<FMT>(b, s, sr_block(4 * u + 2, seed, offset),
+                             sr_block(4 * u + 3, seed, offset));
+    } else {
+      qa = cvt8_bf16<FMT>(a, s);
+      qb = cvt8_bf16<FMT>(b, s);
+    }
     st_nt16(make_uint4(qa.x, qa.y, qb.x, qb.y), yv + u);
   }
   uint32_t mb = AMAX ? absmax_fold(m) : 0u;
@@ -71,6 +84,7 @@ __global__ void __launch_bounds__(kBig)
     int64_t i = (nu << 4) + threadIdx.x;
     uint16_t h = x[i];
     float v = __uint_as_float((uint32_t)h << 16) * s;
+    if constexpr (SR) v = sr_target<FMT>(v, sr_word(i, seed, offset));
     y[i] = (uint8_t)(cvt4<FMT>(v, 0.f, 0.f, 0.f) & 0xFFu);
     if (AMAX) {
       uint32_t t = (uint32_t)(h & 0x7FFFu) << 16;
@@ -104,12 +118,12 @@ __device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t 
   t3 = __builtin_amdgcn_perm(a23_hi, a01_hi, 0x07060302u);       // c3
 }
 
-template <int FMT, bool AMAX, bool WANT_Y>
+template <int FMT, bool AMAX, bool WANT_Y, bool SR>
 __global__ void __launch_bounds__(kBig)
     k_cast_transpose(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                      const float* __restrict__ scale, uint8_t* __restrict__ y,
                      uint8_t* __restrict__ yt, float* __restrict__ amax, int tiles_c,
-                     int ntiles) {
+                     int ntiles, uint64_t seed, uint64_t offset) {
   // four 256-thread groups, each on its own tile and 16 KB of LDS; the grid
   // walks the tiles row-major, four per workgroup per pass
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][128 * 128];
@@ -141,8 +155,15 @@ __global__ void __launch_bounds__(kBig)
         m = absmax_pk(m, a.x); m = absmax_pk(m, a.y); m = absmax_pk(m, a.z); m = absmax_pk(m, a.w);
         m = absmax_pk(m, b.x); m = absmax_pk(m, b.y); m = absmax_pk(m, b.z); m = absmax_pk(m, b.w);
       }
-      uint2 qa = cvt8_bf16<FMT>(a, s);
-      uint2 qb = cvt8_bf16<FMT>(b, s);
+      uint2 qa, qb;
+      if constexpr (SR) {   // 16 elements from r * cols + cbase (a multiple of 16)
+        const uint64_t g = (uint64_t)(r * cols + cbase) >> 2;
+        qa = cvt8_bf16_sr<FMT>(a, s, sr_block(g, seed, offset), sr_block(g + 1, seed, offset));
+        qb = cvt8_bf16_sr<FMT>(b, s, sr_block(g + 2, seed, offset), sr_block(g + 3, seed, offset));
+      } else {
+        qa = cvt8_bf16<FMT>(a, s);
+        qb = cvt8_bf16<FMT>(b, s);
+      }
       w[i][0] = qa.x; w[i][1] = qa.y; w[i][2] = qb.x; w[i][3] = qb.y;
       if (WANT_Y && col_ok && r < rows)
         st_nt16(make_uint4(qa.x, qa.y, qb.x, qb.y), reinterpret_cast<uint4*>(y + r * cols + cbase));
@@ -183,19 +204,21 @@ __global__ void __launch_bounds__(kBig)
 // Generic cast for shapes the tiled kernels do not take (rows or cols not
 // multiples of 16): one element per thread, same arithmetic.
 // ---------------------------------------------------------------------
-template <int FMT, bool AMAX>
+template <int FMT, bool AMAX, bool SR>
 __global__ void __launch_bounds__(kThreads)
     k_cast_generic(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                    const float* __restrict__ scale, uint8_t* __restrict__ y,
-                   uint8_t* __restrict__ yt, float* __restrict__ amax) {
+                   uint8_t* __restrict__ yt, float* __restrict__ amax, uint64_t seed,
+                   uint64_t offset) {
   const float s = *scale;
   const int64_t n = rows * cols;
   uint32_t m = 0;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
     const uint16_t h = x[i];
-    const uint8_t q = (uint8_t)(cvt4<FMT>(__uint_as_float((uint32_t)h << 16) * s, 0.f, 0.f, 0.f) &
-                                0xFFu);
+    float v = __uint_as_float((uint32_t)h << 16) * s;
+    if constexpr (SR) v = sr_target<FMT>(v, sr_word(i, seed, offset));
+    const uint8_t q = (uint8_t)(cvt4<FMT>(v, 0.f, 0.f, 0.f) & 0xFFu);
     const int64_t r = i / cols, c = i - r * cols;
     if (y) y[i] = q;
     if (yt) yt[c * rows + r] = q;
@@ -207,9 +230,10 @@ __global__ void __launch_bounds__(kThreads)
   if (AMAX) block_amax_to<kThreads>(amax, m);
 }
 
-template <int FMT, bool AMAX>
+template <int FMT, bool AMAX, bool SR>
 hipError_t launch_cast_t(const uint16_t* x, int64_t rows, int64_t cols, const float* scale,
-                         uint8_t* y, uint8_t* yt, float* amax, hipStream_t s) {
+                         uint8_t* y, uint8_t* yt, float* amax, uint64_t seed, uint64_t offset,
+                         hipStream_t s) {
   const int64_t n = rows * cols;
   const int64_t cus = device_cu_count();
   if (yt == nullptr) {
@@ -217,8 +241,8 @@ hipError_t launch_cast_t(const uint16_t* x, int64_t rows, int64_t cols, const fl
     int64_t blocks = (nu + kBig - 1) / kBig;
     if (blocks > cus) blocks = cus;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL((k_cast_flat<FMT, AMAX>), dim3((unsigned)blocks), dim3(kBig), 0, s, x,
-                       n, scale, y, amax);
+    hipLaunchKernelGGL((k_cast_flat<FMT, AMAX, SR>), dim3((unsigned)blocks), dim3(kBig), 0, s, x,
+                       n, scale, y, amax, seed, offset);
     return hipGetLastError();
   }
   if (rows % 16 == 0 && cols % 16 == 0 && (rows + 127) / 128 * ((cols + 127) / 128) < (1LL << 30)) {
@@ -227,34 +251,43 @@ hipError_t launch_cast_t(const uint16_t* x, int64_t rows, int64_t cols, const fl
     int64_t blocks = (ntiles + 3) / 4;
     if (blocks > cus) blocks = cus;
     if (y)
-      hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, true>), dim3((unsigned)blocks), dim3(kBig), 0,
-                         s, x, rows, cols, scale, y, yt, amax, tiles_c, ntiles);
+      hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, true, SR>), dim3((unsigned)blocks),
+                         dim3(kBig), 0, s, x, rows, cols, scale, y, yt, amax, tiles_c, ntiles,
+                         seed, offset);
     else
-      hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, false>), dim3((unsigned)blocks), dim3(kBig),
-                         0, s, x, rows, cols, scale, y, yt, amax, tiles_c, ntiles);
+      hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, false, SR>), dim3((unsigned)blocks),
+                         dim3(kBig), 0, s, x, rows, cols, scale, y, yt, amax, tiles_c, ntiles,
+                         seed, offset);
     return hipGetLastError();
   }
   int64_t blocks = (n + kThreads - 1) / kThreads;
   if (blocks > cus) blocks = cus;
-  hipLaunchKernelGGL((k_cast_generic<FMT, AMAX>), dim3((unsigned)blocks), dim3(kThreads), 0, s, x,
-                     rows, cols, scale, y, yt, amax);
+  hipLaunchKernelGGL((k_cast_generic<FMT, AMAX, SR>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                     x, rows, cols, scale, y, yt, amax, seed, offset);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, const float* scale, int fmt,
-                       uint8_t* y, uint8_t* y_t, float* amax, hipStream_t s) {
+                       uint8_t* y, uint8_t* y_t, float* amax, int sr, uint64_t seed,
+                       uint64_t offset, hipStream_t s) {
   if (amax) {
     hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 1, 0u, s);
     if (e != hipSuccess) return e;
   }
   if (rows == 0 || cols == 0) return hipSuccess;
-  if (fmt == 0)
-    return amax ? launch_cast_t<0, true>(x, rows, cols, scale, y, y_t, amax, s)
-                : launch_cast_t<0, false>(x, rows, cols, scale, y, y_t, amax, s);
-  return amax ? launch_cast_t<1, true>(x, rows, cols, scale, y, y_t, amax, s)
-              : launch_cast_t<1, false>(x, rows, cols, scale, y, y_t, amax, s);
+  const int key = fmt * 4 + (amax ? 2 : 0) + (sr ? 1 : 0);
+  switch (key) {
+    case 0: return launch_cast_t<0, false, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
+    case 1: return launch_cast_t<0, false, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
+    case 2: return launch_cast_t<0, true, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
+    case 3: return launch_cast_t<0, true, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
+    case 4: return launch_cast_t<1, false, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
+    case 5: return launch_cast_t<1, false, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
+    case 6: return launch_cast_t<1, true, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
+    default: return launch_cast_t<1, true, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
+  }
 }
 
 }  // namespace fp8lin

@@ -94,6 +94,83 @@ __device__ __forceinline__ uint2 cvt8_bf16(uint4 v, float s) {
   return r;
 }
 
+// ---------------------------------------------------------------------
+// Stochastic rounding ([MPG] "Stochastic rounding": round up or down at
+// random according to the remainder, so the rounded value is unbiased).
+//
+// Random words: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011).  Element i of a tensor (row-major
+// index) takes word i % 4 of the block with counter (i / 4, offset) as four
+// little-endian 32-bit words and key seed.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// The four words of block g (elements 4g .. 4g+3).
+__device__ __forceinline__ uint4 sr_block(uint64_t g, uint64_t seed, uint64_t offset) {
+  return philox4x32_10(make_uint4((uint32_t)g, (uint32_t)(g >> 32), (uint32_t)offset,
+                                  (uint32_t)(offset >> 32)),
+                       (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+// Word i % 4 of block i / 4 (one element on its own).
+__device__ __forceinline__ uint32_t sr_word(int64_t i, uint64_t seed, uint64_t offset) {
+  const uint4 w = sr_block((uint64_t)i >> 2, seed, offset);
+  const int k = (int)(i & 3);
+  return k == 0 ? w.x : (k == 1 ? w.y : (k == 2 ? w.z : w.w));
+}
+
+// The FP8 value (as an exactly representable binary32) that v rounds to
+// with the word r: with lo <= |v| < hi the neighbouring FP8 magnitudes, hi
+// when r < (|v| - lo) / (hi - lo) * 2^32, else lo; sign kept.  |v| >= fmax,
+// Inf and NaN are returned as they are (the conversion saturates them and
+// patches NaN).  In the FP8 normal range the remainder is the low 23 - M
+// mantissa bits of |v|; below it, |v| is scaled by the inverse subnormal
+// step (exact) and the remainder compared in binary64.
+template <int FMT>
+__device__ __forceinline__ float sr_target(float v, uint32_t r) {
+  constexpr int MB = FMT == 0 ? 3 : 2;           // mantissa bits
+  constexpr int EMIN = FMT == 0 ? -6 : -14;      // exponent of the smallest normal
+  constexpr int D = 23 - MB;
+  const float a = __builtin_fabsf(v);
+  if (!(a < Fmt<FMT>::max)) return v;
+  const uint32_t sgn = __float_as_uint(v) & 0x80000000u;
+  const uint32_t b = __float_as_uint(a);
+  uint32_t t;
+  if (b >= (uint32_t)(EMIN + 127) << 23) {
+    const uint32_t frac = b & ((1u << D) - 1u);
+    const bool up = (r >> (32 - D)) < frac;
+    t = (b & ~((1u << D) - 1u)) + (up ? (1u << D) : 0u);
+  } else {
+    const float x = __builtin_ldexpf(a, MB - EMIN);          // a / subnormal step, exact
+    const float k = __builtin_floorf(x);
+    const double frac = (double)(x - k);                     // exact
+    const bool up = (double)r < frac * 4294967296.0;
+    t = __float_as_uint(__builtin_ldexpf(k + (up ? 1.0f : 0.0f), EMIN - MB));
+  }
+  return __uint_as_float(t | sgn);
+}
+
+// Eight bf16 (one 16-byte load) times s -> 8 codes, stochastically rounded
+// with the words w[0..7].
+template <int FMT>
+__device__ __forceinline__ uint2 cvt8_bf16_sr(uint4 v, float s, uint4 w0, uint4 w1) {
+  uint2 q;
+  q.x = cvt4<FMT>(sr_target<FMT>(bf16_lo(v.x) * s, w0.x), sr_target<FMT>(bf16_hi(v.x) * s, w0.y),
+                  sr_target<FMT>(bf16_lo(v.y) * s, w0.z), sr_target<FMT>(bf16_hi(v.y) * s, w0.w));
+  q.y = cvt4<FMT>(sr_target<FMT>(bf16_lo(v.z) * s, w1.x), sr_target<FMT>(bf16_hi(v.z) * s, w1.y),
+                  sr_target<FMT>(bf16_lo(v.w) * s, w1.z), sr_target<FMT>(bf16_hi(v.w) * s, w1.w));
+  return q;
+}
+
 // max |x| over the bf16 halves of a dword, as a packed pair of 15-bit
 // magnitudes: clearing the sign bits leaves patterns whose unsigned order
 // is the order of |x| (NaN above Inf), so a packed u16 max is exact.

@@ -25,10 +25,15 @@ hipError_t launch_history_update(float* history, int64_t n, int64_t len, const f
                                  int fmt, int margin, int algo, int pow2, float* scale,
                                  float* scale_inv, hipStream_t s);
 
-// Per-tensor cast with optional transpose and amax (amax must be zeroed by
-// the caller first when given).
+// Exponentially weighted amax and its scale, n tensors.
+hipError_t launch_ewma_update(float* ewma, int64_t n, const float* amax_new, float beta, int fmt,
+                              int margin, float* scale, float* scale_inv, hipStream_t s);
+
+// Per-tensor cast with optional transpose and amax (zeroed here first when
+// given); sr != 0: stochastic rounding with Philox words from (seed, offset).
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, const float* scale, int fmt,
-                       uint8_t* y, uint8_t* y_t, float* amax, hipStream_t s);
+                       uint8_t* y, uint8_t* y_t, float* amax, int sr, uint64_t seed,
+                       uint64_t offset, hipStream_t s);
 
 // Block-wise cast (tile: 1 = 1x128, 2 = 128x128; pow2: power-of-two scales).
 hipError_t launch_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int tile,

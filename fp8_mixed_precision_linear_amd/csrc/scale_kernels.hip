@@ -81,6 +81,37 @@ __global__ void k_compute_scale(const float* __restrict__ amax, int64_t n, float
   scale_inv[i] = si;
 }
 
+// Delayed scaling with an exponentially weighted amax ([MPG] "Delayed
+// scaling (the default recipe)": an exponentially weighted average of
+// recent steps), one thread per tensor.  A zero or non-finite new amax
+// changes nothing; the first one seeds the average; afterwards
+// ewma = fl32(fl32(beta * ewma) + fl32(fl32(1 - beta) * amax)), every
+// operation rounded on its own (no contraction); the scale follows by the
+// current-scaling rule and is kept when that rule fails.
+__global__ void k_ewma_update(float* __restrict__ ewma, int64_t n, const float* __restrict__ amax_new,
+                              float beta, float fmax, int margin, float* __restrict__ scale,
+                              float* __restrict__ scale_inv) {
+#pragma clang fp contract(off)
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float a = amax_new[i];
+  if (!(a > 0.0f) || __builtin_isinf(a)) return;
+  float e = ewma[i];
+  if (e == 0.0f) {
+    e = a;
+  } else {
+    const float t0 = beta * e;             // no fused multiply-add: each product
+    const float t1 = (1.0f - beta) * a;    // and the sum round on their own
+    e = t0 + t1;
+  }
+  ewma[i] = e;
+  float sc, si;
+  if (scale_from_amax(e, fmax, margin, sc, si)) {
+    scale[i] = sc;
+    scale_inv[i] = si;
+  }
+}
+
 // Delayed scaling: one wavefront per tensor shifts its history (newest
 // first), inserts the new amax, takes the window maximum (NaN propagates:
 // compared as bit patterns of non-negative values) or the newest entry, and
@@ -182,6 +213,14 @@ hipError_t launch_history_update(float* history, int64_t n, int64_t len, const f
   if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_history_update, dim3((unsigned)n), dim3(64), 0, s, history, n, len,
                      amax_new, fmax_of(fmt), margin, algo, pow2, scale, scale_inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_ewma_update(float* ewma, int64_t n, const float* amax_new, float beta, int fmt,
+                              int margin, float* scale, float* scale_inv, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_ewma_update, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ewma, n,
+                     amax_new, beta, fmax_of(fmt), margin, scale, scale_inv);
   return hipGetLastError();
 }
 

@@ -64,6 +64,8 @@ def _load():
         "fp8_cast_block": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
         "fp8_cast_block_pow2": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
         "fp8_cast_rowwise": (i32, [vp, i64, i64, i32, vp, vp, vp, vp, vp]),
+        "fp8_cast_sr": (i32, [vp, i64, i64, i32, vp, C.c_uint64, C.c_uint64, vp, vp, vp, vp]),
+        "fp8_amax_ewma_update": (i32, [vp, i64, vp, C.c_float, i32, i32, vp, vp, vp]),
         "fp8_scaled_gemm": (i32, [C.POINTER(GemmArgs), vp]),
     }
     for name, (res, args) in sig.items():
@@ -171,6 +173,25 @@ def _cast(fn, x, scale, y, y_t, amax_out, stream):
     _check(fn.__name__, fn(_ptr(x, _BF16, "x"), rows, cols, _ptr(scale, _F32, "scale"),
                            _ptr(y, _U8, "y"), _ptr(y_t, _U8, "y_t"),
                            _ptr(amax_out, _F32, "amax_out"), _stream(stream)))
+
+
+def fp8_cast_sr(x, fmt, scale, seed, offset=0, y=None, y_t=None, amax_out=None, stream=None):
+    rows, cols = _rc(x)
+    _check("fp8_cast_sr",
+           _L.fp8_cast_sr(_ptr(x, _BF16, "x"), rows, cols, fmt, _ptr(scale, _F32, "scale"),
+                          int(seed), int(offset), _ptr(y, _U8, "y"), _ptr(y_t, _U8, "y_t"),
+                          _ptr(amax_out, _F32, "amax_out"), _stream(stream)))
+
+
+def fp8_amax_ewma_update(ewma, amax_new, beta, fmt, margin, scale, scale_inv, stream=None):
+    n = ewma.numel()
+    for name, t in (("amax_new", amax_new), ("scale", scale), ("scale_inv", scale_inv)):
+        if t.numel() != n:
+            raise ValueError(f"{name} must hold {n} floats")
+    _check("fp8_amax_ewma_update",
+           _L.fp8_amax_ewma_update(_ptr(ewma, _F32, "ewma"), n, _ptr(amax_new, _F32, "amax_new"),
+                                   float(beta), fmt, margin, _ptr(scale, _F32, "scale"),
+                                   _ptr(scale_inv, _F32, "scale_inv"), _stream(stream)))
 
 
 def fp8_cast_e4m3(x, scale, y=None, y_t=None, amax_out=None, stream=None):

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 3
+#define FP8LIN_ABI_VERSION 4
 
 /* [MPG] "The precision formats", "FP8 E4M3", "FP8 E5M2": E4M3 = 4 exponent
  * and 3 mantissa bits, range about 2^-9..448; E5M2 = 5 and 2, range about
@@ -171,6 +171,26 @@ fp8_status fp8_amax_history_update_pow2(float* history, int64_t n, int64_t len,
                                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_amax_ewma_update -- delayed scaling from an exponentially weighted
+ * amax.  [MPG] "Delayed scaling (the default recipe)": the scale used at
+ * step t is the one right for step t-1, or an exponentially weighted
+ * average of recent steps (read as an average of the amax, from which the
+ * scale follows).  For each tensor i < n, with a = amax_new[i]:
+ *   a == 0 or non-finite: nothing changes;
+ *   ewma[i] == 0 (no step seen yet): ewma[i] = a;
+ *   else ewma[i] = fl32(fl32(beta * ewma[i]) + fl32(fl32(1 - beta) * a));
+ *   then scale[i] = fl32(fmax / ewma[i]) * 2^-margin, scale_inv[i] =
+ *   fl32(1 / scale[i]) (overflow clamped to FLT_MAX).
+ *   ewma       [n] floats, in place (initialise to 0, scale = scale_inv = 1).
+ *   beta       weight of the past, 0 <= beta <= 1 (0: the newest amax).
+ * Errors: FP8_ERR_NULL, FP8_ERR_SHAPE (n < 0), FP8_ERR_ALIGN, FP8_ERR_ARG
+ * (fmt, margin outside 0..64, beta outside [0, 1] or NaN).
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_amax_ewma_update(float* ewma, int64_t n, const float* amax_new, float beta,
+                                fp8_format fmt, int margin, float* scale, float* scale_inv,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fp8_cast_e4m3 / fp8_cast_e5m2 -- per-tensor saturating RNE cast,
  * q = encode(fl32(x * scale)), with optional fused transpose and amax.
  * [MPG] "Per-tensor scaling" (multiply by the scale before quantising);
@@ -189,6 +209,29 @@ fp8_status fp8_cast_e4m3(const void* x_bf16, int64_t rows, int64_t cols, const f
                          uint8_t* y, uint8_t* y_t, float* amax_out, hipStream_t stream);
 fp8_status fp8_cast_e5m2(const void* x_bf16, int64_t rows, int64_t cols, const float* scale,
                          uint8_t* y, uint8_t* y_t, float* amax_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_cast_sr -- per-tensor cast with stochastic rounding.
+ * [MPG] "Stochastic rounding": round up or down at random according to the
+ * remainder, which keeps the rounded value unbiased (used for gradients);
+ * [TALK] outline: "rounding techniques".
+ * With v = fl32(x * scale) and lo <= |v| < hi the two neighbouring FP8
+ * magnitudes, the code is hi when r < (|v| - lo) / (hi - lo) * 2^32, else
+ * lo (sign kept), where r is the element's random word; |v| >= fmax and
+ * +-Inf saturate to +-fmax, NaN gives 0x7F | sign.  The word of element i
+ * (row-major index) is word i % 4 of Philox4x32-10 (Salmon et al., SC 2011)
+ * with counter (i / 4 low, i / 4 high, offset low, offset high) and key
+ * (seed low, seed high); y_t holds the same codes transposed.  Calls with the
+ * same (seed, offset) repeat the same draw: advance offset by at least
+ * ceil(rows * cols / 4) per call for fresh words (the values are baked into
+ * a captured graph).
+ *   fmt        FP8_E4M3 or FP8_E5M2.
+ *   Other arguments, layouts and errors as fp8_cast_e4m3, plus FP8_ERR_ARG
+ *   (fmt).
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_cast_sr(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                       const float* scale, uint64_t seed, uint64_t offset, uint8_t* y,
+                       uint8_t* y_t, float* amax_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * fp8_cast_block -- block-wise cast with per-tile scales computed on the fly.

@@ -28,7 +28,7 @@ def test_header_declares_the_layer_calls():
     for f in ["fp8_amax", "fp8_compute_scale", "fp8_amax_history_update", "fp8_cast_e4m3",
               "fp8_cast_e5m2", "fp8_cast_block", "fp8_scaled_gemm", "fp8_abi_version",
               "fp8_status_string", "fp8_compute_scale_pow2", "fp8_amax_history_update_pow2",
-              "fp8_cast_block_pow2", "fp8_cast_rowwise"]:
+              "fp8_cast_block_pow2", "fp8_cast_rowwise", "fp8_cast_sr", "fp8_amax_ewma_update"]:
         assert f in fns
 
 
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.abi_version() == 3
+    assert L.abi_version() == 4
     for s in range(7):
         assert isinstance(L.status_string(s), str) and L.status_string(s)
     assert L.status_string(99) == "unknown status"
@@ -85,6 +85,22 @@ def test_host_validation_before_launch(L):
     assert f.fp8_cast_rowwise(x, 4, 4, 0, y, C.c_void_p(0x3002), None, None, None) == 3
     assert f.fp8_cast_rowwise(x, -1, 4, 0, y, s, None, None, None) == 2
     assert f.fp8_cast_rowwise(None, 0, 4, 0, None, None, None, None, None) == 0   # empty: no-op
+    # stochastic-rounding cast: bad format, missing outputs, misalignment
+    assert f.fp8_cast_sr(x, 4, 4, 2, s, 1, 0, y, None, None, None) == 6
+    assert f.fp8_cast_sr(x, 4, 4, 0, s, 1, 0, None, None, None, None) == 1
+    assert f.fp8_cast_sr(x, 4, 4, 1, s, 1, 0, C.c_void_p(0x2004), None, None, None) == 3
+    assert f.fp8_cast_sr(x, -4, 4, 1, s, 1, 0, y, None, None, None) == 2
+    # EWMA update: beta outside [0, 1] or NaN, margin, sizes, pointers
+    e, a = C.c_void_p(0x4000), C.c_void_p(0x5000)
+    assert f.fp8_amax_ewma_update(e, 1, a, 1.5, 0, 0, s, s, None) == 6
+    assert f.fp8_amax_ewma_update(e, 1, a, -0.1, 0, 0, s, s, None) == 6
+    assert f.fp8_amax_ewma_update(e, 1, a, float("nan"), 0, 0, s, s, None) == 6
+    assert f.fp8_amax_ewma_update(e, 1, a, 0.5, 0, 65, s, s, None) == 6
+    assert f.fp8_amax_ewma_update(e, 1, a, 0.5, 2, 0, s, s, None) == 6
+    assert f.fp8_amax_ewma_update(e, -1, a, 0.5, 0, 0, s, s, None) == 2
+    assert f.fp8_amax_ewma_update(e, 1, None, 0.5, 0, 0, s, s, None) == 1
+    assert f.fp8_amax_ewma_update(C.c_void_p(0x4002), 1, a, 0.5, 0, 0, s, s, None) == 3
+    assert f.fp8_amax_ewma_update(None, 0, None, 0.5, 0, 0, None, None, None) == 0   # n = 0: no-op
 
 
 def _gemm(L, **kw):
