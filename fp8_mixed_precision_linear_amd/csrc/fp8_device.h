@@ -105,8 +105,10 @@ __device__ __forceinline__ uint2 cvt8_bf16(uint4 v, float s) {
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    // one 32x32 -> 64-bit multiply gives both halves
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
@@ -133,8 +135,20 @@ __device__ __forceinline__ uint32_t sr_word(int64_t i, uint64_t seed, uint64_t o
 // when r < (|v| - lo) / (hi - lo) * 2^32, else lo; sign kept.  |v| >= fmax,
 // Inf and NaN are returned as they are (the conversion saturates them and
 // patches NaN).  In the FP8 normal range the remainder is the low 23 - M
-// mantissa bits of |v|; below it, |v| is scaled by the inverse subnormal
-// step (exact) and the remainder compared in binary64.
+// mantissa bits of |v|; below it (rare: a branch), |v| is scaled by the
+// inverse subnormal step (exact), and r < F with F = remainder * 2^32 (an
+// exact binary32 below 2^32) is decided as r < ceil(F) in 64-bit integers.
+template <int FMT>
+__device__ __noinline__ uint32_t sr_subnormal(float a, uint32_t r) {
+  constexpr int MB = FMT == 0 ? 3 : 2;
+  constexpr int EMIN = FMT == 0 ? -6 : -14;
+  const float x = __builtin_ldexpf(a, MB - EMIN);            // a / subnormal step, exact
+  const float k = __builtin_floorf(x);
+  const float F = __builtin_ldexpf(x - k, 32);               // exact, < 2^32
+  const bool up = (uint64_t)r < (uint64_t)__builtin_ceilf(F);
+  return __float_as_uint(__builtin_ldexpf(k + (up ? 1.0f : 0.0f), EMIN - MB));
+}
+
 template <int FMT>
 __device__ __forceinline__ float sr_target(float v, uint32_t r) {
   constexpr int MB = FMT == 0 ? 3 : 2;           // mantissa bits
@@ -145,16 +159,12 @@ __device__ __forceinline__ float sr_target(float v, uint32_t r) {
   const uint32_t sgn = __float_as_uint(v) & 0x80000000u;
   const uint32_t b = __float_as_uint(a);
   uint32_t t;
-  if (b >= (uint32_t)(EMIN + 127) << 23) {
+  if (__builtin_expect(b >= (uint32_t)(EMIN + 127) << 23, 1)) {
     const uint32_t frac = b & ((1u << D) - 1u);
     const bool up = (r >> (32 - D)) < frac;
     t = (b & ~((1u << D) - 1u)) + (up ? (1u << D) : 0u);
   } else {
-    const float x = __builtin_ldexpf(a, MB - EMIN);          // a / subnormal step, exact
-    const float k = __builtin_floorf(x);
-    const double frac = (double)(x - k);                     // exact
-    const bool up = (double)r < frac * 4294967296.0;
-    t = __float_as_uint(__builtin_ldexpf(k + (up ? 1.0f : 0.0f), EMIN - MB));
+    t = sr_subnormal<FMT>(a, r);   // out of line: keeps the common path short
   }
   return __uint_as_float(t | sgn);
 }
