@@ -238,13 +238,19 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
 
   for (int kb = 0; kb < nk; ++kb) {
     const int stage = kb & 1;
-    if (kb + 1 < nk) load_stage(kb + 1, lds[stage ^ 1]);
     const uint8_t* As = lds[stage];
     const uint8_t* Bs = As + A_BYTES;
 
+    // fragment reads first (A row-tile 0 with B column-tile 0 ahead of the
+    // rest, so the first MFMA can start early), then the next stage's DMA:
+    // after the barrier every wavefront wants its fragments at once, and
+    // DMA instructions issued ahead of them delay them (measured: 2-4%
+    // faster than issuing the DMA first)
+    const v8i a_first = frag(As, wm * WTM + l16, g);
     v8i bfr[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) bfr[j] = frag(Bs, wn * WTN + 16 * j + l16, g);
+    if (kb + 1 < nk) load_stage(kb + 1, lds[stage ^ 1]);
 
     // The MFMA takes B as its first operand, so each 16x16 result tile is
     // the transpose of the D tile: lane (g, l16) holds D row 16*i + l16,
@@ -264,14 +270,17 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
         else
           eb[j] = (int)((eu >> 8) & 0xFFu);
       }
+      v8i a_cur = a_first;
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const v8i afr = frag(As, wm * WTM + 16 * i + l16, g);
+        v8i a_nxt = a_cur;
+        if (i + 1 < TI) a_nxt = frag(As, wm * WTM + 16 * (i + 1) + l16, g);
         int ea = (int)(eu & 0xFFu);
         if constexpr (SA_ROWS)
           ea = e8m0_of(reinterpret_cast<const float*>(As + SA_OFF)[wm * WTM + 16 * i + l16]);
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_mx<BF, AF>(bfr[j], afr, acc[i][j], eb[j], ea);
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_mx<BF, AF>(bfr[j], a_cur, acc[i][j], eb[j], ea);
+        a_cur = a_nxt;
       }
     } else if constexpr (BLOCK) {
       float scol[TJ][4];
@@ -301,7 +310,7 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
               acc[i][j][r] = __builtin_fmaf(pp[j][r], sr, acc[i][j][r]);
           }
       };
-      v8i a_cur = frag(As, wm * WTM + l16, g);
+      v8i a_cur = a_first;
       v4f pprev[TJ];
       float sprev = 0.0f;
 #pragma unroll
@@ -325,11 +334,14 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
       }
       promote(TI - 1, pprev, sprev);
     } else {
+      v8i a_cur = a_first;
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const v8i afr = frag(As, wm * WTM + 16 * i + l16, g);
+        v8i a_nxt = a_cur;
+        if (i + 1 < TI) a_nxt = frag(As, wm * WTM + 16 * (i + 1) + l16, g);
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma<BF, AF>(bfr[j], afr, acc[i][j]);
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma<BF, AF>(bfr[j], a_cur, acc[i][j]);
+        a_cur = a_nxt;
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
