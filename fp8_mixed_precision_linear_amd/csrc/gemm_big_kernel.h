@@ -1,0 +1,606 @@
+// gemm_big_kernel.h -- the large-tile FP8 scaled GEMM for gfx950 (the main
+// path): kernel and launch templates, instantiated by gemm_big.hip (BF16 /
+// FP32 output) and gemm_big_fp8out.hip (FP8 output), two translation units
+// compiled in parallel.
+//
+// Same contract as k_gemm in gemm_kernels.hip (see there and the C ABI):
+// D = A . B^T, K-contiguous FP8 operands, FP32 accumulation; tensor scales
+// in the epilogue, block scales promoted per 128-wide K block.
+// [MPG] = "Mixed Precision LLM Training: The Complete Guide",
+//   "Skipping the BAcc accumulator promotion", "DeepSeek FP8 training recipe
+//   in detail > Block-wise scaling at 128 granularity" and "> Mixed-precision
+//   accumulation".
+//
+// Layout of one workgroup (512 threads, 8 wavefronts):
+//   output tile 256 x 256; wavefront w owns rows 128*(w/4).., columns
+//   64*(w%4).. (8 x 4 MFMA tiles of 16x16, one v_mfma_f32_16x16x128 per tile
+//   per 128-wide K block);
+//   K loop in 128-byte steps through two LDS stages of 66 KB (A 32 KB, B
+//   32 KB, 1 KB of row scales for each 1x128 operand);
+//   operands move global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+//   staging), one instruction per 8 rows x 128 bytes of a tile, so every
+//   global read covers whole 128-byte lines.  Tiles are row-major in LDS
+//   with 16-byte chunk c of row r stored at chunk c ^ swz(r); a lane's DMA
+//   slot is fixed, so the swizzle is applied by choosing which global chunk
+//   each lane fetches.  An MFMA operand lane l takes row l % 16 and the K
+//   chunks g and g + 4 (g = l / 16); A and B use the same assignment, so
+//   every product pairs equal k and each group of 8 consecutive register
+//   bytes holds 8 consecutive k.  With this assignment and swz(r) =
+//   ((r >> 1) & 7) ^ ((r & 1) << 2) the 16-row ds_read_b128 pattern ran
+//   about 1.6x faster than with chunk pairs {2g, 2g+1} (measured on gfx950).
+//   Buffer loads past the end of an operand return zeros, which covers the
+//   M / N / K tails without branches.
+//   The prefetch is issued from inline assembly: the compiler then neither
+//   waits for it before reading the other stage nor keeps it ordered with
+//   anything else; each step ends with an explicit vmcnt(0) and a barrier.
+//   Inside the loop there is no other vector-memory access: per-K-block
+//   scales come from LDS (1x128 rows arrive with the operands; per-tensor and
+//   128x128 scales sit in a per-wavefront table filled before the loop).
+// Workgroup order: the hardware hands consecutive workgroups to the 8 XCDs in
+// turn; ids are remapped so each XCD gets a contiguous run of tiles, taken
+// 8 tile-rows at a time, so the A and B panels a tile needs sit in that
+// XCD's L2.
+#pragma once
+
+#include <type_traits>
+
+#include "fp8_device.h"
+#include "launch.h"
+
+namespace fp8lin {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int THREADS = 512, NWAVES = 8;
+constexpr int WTM = 128, WTN = 64;       // wavefront tile
+constexpr int TI = WTM / 16, TJ = WTN / 16;
+constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+constexpr int SA_OFF = A_BYTES + B_BYTES;
+constexpr int SB_OFF = SA_OFF + BM * 4;
+constexpr int STAGE = SB_OFF + BN * 4;
+constexpr int MAX_KB = 512;              // per-wavefront scale table: K <= 65536
+constexpr int GROUP_M = 8;
+constexpr uint32_t kOOB = 0x7FFFFFF0u;   // a buffer offset past any operand
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <int AF, int BF>
+__device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, 0, 0, 0);
+}
+
+// The same instruction with per-lane E8M0 block scales: lane l of operand
+// `a` holds one row and applies 2^(sa - 127) to it, likewise for `b`.
+template <int AF, int BF>
+__device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, sa, 0, sb);
+}
+
+// E8M0 code of a power of two 2^e (|e| <= 126): its binary32 exponent field.
+__device__ __forceinline__ int e8m0_of(float pow2) { return (int)(__float_as_uint(pow2) >> 23) & 0xFF; }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// Raw buffer resource (wave-uniform): base, no stride, `bytes` records.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(a & 0xFFFFFFFFu));
+  r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = kRsrcWord3;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)p));
+}
+
+// 16 bytes per lane from buffer offset `off` into LDS at m0 + 16 * lane.
+__device__ __forceinline__ void dma16(uint32_t m0, uint32_t off, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(off), "s"(rsrc) : "memory", "m0");
+}
+// 4 bytes per lane into LDS at m0 + 4 * lane.
+__device__ __forceinline__ void dma4(uint32_t m0, uint32_t off, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(off), "s"(rsrc) : "memory", "m0");
+}
+
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
+
+// MFMA operand fragment of tile row `row` for lane group g: chunks g, g + 4.
+__device__ __forceinline__ v8i frag(const uint8_t* tile, int row, int g) {
+  const int sw = swz(row);
+  const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * BK + ((g ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * BK + (((g + 4) ^ sw) << 4));
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// BLOCK : block-mode promotion per 128-wide K block;
+// SA_ROWS: A has 1x128 scales (one per row and K block), else one per wave;
+// SB_COL : B has 1x128 scales (one per column and K block), else one per wave.
+// Without BLOCK, SA_ROWS && SB_COL selects per-row scales applied in the
+// epilogue: A's inverse scale per row m (a_scaling 5) and B's per row n
+// (b_scaling 5), either of them possibly per tensor.
+template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL, bool MX, bool OUT8>
+__global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
+  __shared__ float su_tab[NWAVES][MAX_KB];
+  constexpr bool ROWS = !BLOCK && SA_ROWS && SB_COL;
+  // per-row scales of the tile's 256 D rows and 256 D columns, staged once
+  // (rows clamped into D for edge tiles); read in the epilogue
+  __shared__ float rs_tab[ROWS ? BM + BN : 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int nk = (int)((K + BK - 1) / BK);
+
+  // ---- tile id: contiguous runs per XCD, grouped by 8 tile-rows
+  const int nblk = tiles_m * tiles_n;
+  int bid = blockIdx.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int group = bid / (GROUP_M * tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gm = min(tiles_m - first_m, GROUP_M);
+  const int in_group = bid - group * GROUP_M * tiles_n;
+  const int tm = first_m + in_group % gm, tn = in_group / gm;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int64_t rows_a = min((int64_t)BM, M - m0), rows_b = min((int64_t)BN, N - n0);
+  const i32x4 ra = make_rsrc(p.A + m0 * p.lda, (uint32_t)(rows_a * p.lda));
+  const i32x4 rb = make_rsrc(p.B + n0 * p.ldb, (uint32_t)(rows_b * p.ldb));
+  const int lda = (int)p.lda, ldb = (int)p.ldb;
+  // DMA: wave w fills rows 32w .. 32w+31 of A and of B, 8 rows per
+  // instruction; lane p lands in row 8*it + (p >> 3), stored chunk p & 7
+  const int lrow = 32 * wave + (lane >> 3);
+
+  if constexpr (ROWS) {   // thread t < BM: A's scale of D row m0 + t; else B's of column n0 + t - BM
+    static_assert(THREADS == BM + BN, "one row scale per thread");
+    const bool is_a = tid < BM;
+    const int64_t r = is_a ? m0 + tid : n0 + (tid - BM);
+    const int64_t lim = is_a ? M : N;
+    const int row_mode = is_a ? p.a_scaling == 5 : p.b_scaling == 5;
+    rs_tab[tid] = (is_a ? p.a_sinv : p.b_sinv)[row_mode ? (r < lim ? r : lim - 1) : 0];
+  }
+
+  // ---- per-wavefront table of the uniform part of each K block's scale
+  if constexpr (BLOCK && !(SA_ROWS && SB_COL)) {
+    const int64_t mb = min((m0 + wm * WTM) / 128, (M + 127) / 128 - 1);
+    const int64_t nb = min((n0 + wn * WTN) / 128, (N + 127) / 128 - 1);
+    for (int kb = lane; kb < nk; kb += 64) {
+      if constexpr (MX) {
+        // E8M0 codes of the uniform block scales: A in bits 0-7, B in 8-15
+        // (127 = 1.0 for a per-tensor operand, whose scale goes to the
+        // epilogue)
+        int ea = 127, eb = 127;
+        if constexpr (!SA_ROWS)
+          if (p.a_scaling != 0) ea = e8m0_of(p.a_sinv[kb * ((M + 127) / 128) + mb]);
+        if constexpr (!SB_COL)
+          if (p.b_scaling != 0) eb = e8m0_of(p.b_sinv[kb * ((N + 127) / 128) + nb]);
+        su_tab[wave][kb] = __uint_as_float((uint32_t)ea | ((uint32_t)eb << 8));
+      } else {
+        float s = 1.0f;
+        if constexpr (!SA_ROWS)
+          s = p.a_scaling == 0 ? p.a_sinv[0] : p.a_sinv[kb * ((M + 127) / 128) + mb];
+        if constexpr (!SB_COL)
+          s *= p.b_scaling == 0 ? p.b_sinv[0] : p.b_sinv[kb * ((N + 127) / 128) + nb];
+        su_tab[wave][kb] = s;
+      }
+    }
+  }
+
+  auto load_stage = [&](int kb, uint8_t* base) {
+    const int k0 = kb * BK;
+    const uint32_t lb = lds_addr(base);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = lrow + 8 * it;
+      const int kc = k0 + 16 * ((lane & 7) ^ swz(row));
+      const bool kin = kc < (int)K;
+      const uint32_t oa = kin ? (uint32_t)(row * lda + kc) : kOOB;
+      const uint32_t ob = kin ? (uint32_t)(row * ldb + kc) : kOOB;
+      dma16(lb + (32 * wave + 8 * it) * BK, oa, ra);
+      dma16(lb + A_BYTES + (32 * wave + 8 * it) * BK, ob, rb);
+    }
+    if constexpr (BLOCK && SA_ROWS) {
+      if (wave == 0) {   // 256 row scales of this K block
+        const i32x4 rs = make_rsrc(p.a_sinv + (int64_t)kb * M + m0, (uint32_t)(rows_a * 4));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dma4(lb + SA_OFF + q * 256, (uint32_t)(q * 256 + lane * 4), rs);
+      }
+    }
+    if constexpr (BLOCK && SB_COL) {
+      if (wave == 1) {   // 256 column scales of this K block
+        const i32x4 rs = make_rsrc(p.b_sinv + (int64_t)kb * N + n0, (uint32_t)(rows_b * 4));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dma4(lb + SB_OFF + q * 256, (uint32_t)(q * 256 + lane * 4), rs);
+      }
+    }
+  };
+
+  v4f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  load_stage(0, lds[0]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int kb = 0; kb < nk; ++kb) {
+    const int stage = kb & 1;
+    const uint8_t* As = lds[stage];
+    const uint8_t* Bs = As + A_BYTES;
+
+    // fragment reads first (A row-tile 0 with B column-tile 0 ahead of the
+    // rest, so the first MFMA can start early), then the next stage's DMA:
+    // after the barrier every wavefront wants its fragments at once, and
+    // DMA instructions issued ahead of them delay them (measured: 2-4%
+    // faster than issuing the DMA first)
+    const v8i a_first = frag(As, wm * WTM + l16, g);
+    v8i bfr[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) bfr[j] = frag(Bs, wn * WTN + 16 * j + l16, g);
+    if (kb + 1 < nk) load_stage(kb + 1, lds[stage ^ 1]);
+
+    // The MFMA takes B as its first operand, so each 16x16 result tile is
+    // the transpose of the D tile: lane (g, l16) holds D row 16*i + l16,
+    // columns 16*j + 4*g .. +3 -- four consecutive outputs of one row.
+    if constexpr (MX) {
+      // power-of-two block scales applied inside the matrix instruction
+      // (exact): lane l of the B fragment scales its row (a D column), lane
+      // l of the A fragment its row; no FP32 promotion, the accumulator
+      // stays in the instruction's C operand.
+      uint32_t eu = 0;
+      if constexpr (!(SA_ROWS && SB_COL)) eu = __float_as_uint(su_tab[wave][kb]);
+      int eb[TJ];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        if constexpr (SB_COL)
+          eb[j] = e8m0_of(reinterpret_cast<const float*>(As + SB_OFF)[wn * WTN + 16 * j + l16]);
+        else
+          eb[j] = (int)((eu >> 8) & 0xFFu);
+      }
+      v8i a_cur = a_first;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        v8i a_nxt = a_cur;
+        if (i + 1 < TI) a_nxt = frag(As, wm * WTM + 16 * (i + 1) + l16, g);
+        int ea = (int)(eu & 0xFFu);
+        if constexpr (SA_ROWS)
+          ea = e8m0_of(reinterpret_cast<const float*>(As + SA_OFF)[wm * WTM + 16 * i + l16]);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_mx<BF, AF>(bfr[j], a_cur, acc[i][j], eb[j], ea);
+        a_cur = a_nxt;
+      }
+    } else if constexpr (BLOCK) {
+      float scol[TJ][4];
+      if constexpr (SB_COL) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const float4 sv =
+              *reinterpret_cast<const float4*>(As + SB_OFF + (wn * WTN + 16 * j + 4 * g) * 4);
+          scol[j][0] = sv.x; scol[j][1] = sv.y; scol[j][2] = sv.z; scol[j][3] = sv.w;
+        }
+      }
+      float suni = 1.0f;
+      if constexpr (!(SA_ROWS && SB_COL)) suni = su_tab[wave][kb];
+      // one row-tile at a time: the next A fragment is read while this
+      // tile's MFMAs run, and the block partials of the previous row-tile
+      // are promoted while this row's MFMAs execute (their results are
+      // long ready by then); the last row is promoted after the loop.  The
+      // scheduling barrier keeps each row's MFMAs ahead of the promotion.
+      auto promote = [&](int i, const v4f (&pp)[TJ], float sr) {
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (SB_COL)
+              acc[i][j][r] = __builtin_fmaf(pp[j][r] * sr, scol[j][r], acc[i][j][r]);
+            else
+              acc[i][j][r] = __builtin_fmaf(pp[j][r], sr, acc[i][j][r]);
+          }
+      };
+      v8i a_cur = a_first;
+      v4f pprev[TJ];
+      float sprev = 0.0f;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        v8i a_nxt = a_cur;
+        if (i + 1 < TI) a_nxt = frag(As, wm * WTM + 16 * (i + 1) + l16, g);
+        float srow = suni;
+        if constexpr (SA_ROWS) {
+          srow = reinterpret_cast<const float*>(As + SA_OFF)[wm * WTM + 16 * i + l16];
+          if constexpr (!SB_COL) srow *= suni;
+        }
+        v4f pcur[TJ];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) pcur[j] = mfma<BF, AF>(bfr[j], a_cur, v4f{0.f, 0.f, 0.f, 0.f});
+        if (i > 0) promote(i - 1, pprev, sprev);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) pprev[j] = pcur[j];
+        sprev = srow;
+        a_cur = a_nxt;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      promote(TI - 1, pprev, sprev);
+    } else {
+      v8i a_cur = a_first;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        v8i a_nxt = a_cur;
+        if (i + 1 < TI) a_nxt = frag(As, wm * WTM + 16 * (i + 1) + l16, g);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma<BF, AF>(bfr[j], a_cur, acc[i][j]);
+        a_cur = a_nxt;
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---- epilogue.  Lane (g, l16) holds, for each (i, j), D row 16*i + l16,
+  // columns 16*j + 4*g .. +3 of the wavefront's 128 x 64 tile.  Tiles wholly
+  // inside D with 16-byte-aligned rows are staged through LDS (each
+  // wavefront owns 16 KB of the freed operand stages: 16-byte chunk c of
+  // tile row r sits at chunk c ^ (r & 7)) and leave as whole rows, 16 bytes
+  // per lane: one 128-byte line per tile row for BF16, two for FP32 (FP32
+  // goes in two passes of 64 rows).  Other tiles store element by element
+  // with bounds checks.
+  float sa = 1.0f, sb = 1.0f;
+  if constexpr (!BLOCK) {
+    sa = p.a_sinv[0];
+    sb = p.b_sinv[0];
+  }
+  if constexpr (MX) {   // a per-tensor operand's scale is applied here
+    if (p.a_scaling == 0) sa = p.a_sinv[0];
+    if (p.b_scaling == 0) sb = p.b_sinv[0];
+  }
+  constexpr bool EPI_SCALE = !BLOCK || MX;
+  if constexpr (ROWS) __syncthreads();   // the tile's row scales are in rs_tab
+  // dequantised value of accumulator entry (i, j, q)
+  auto deq = [&](int i, int j, int q, float a) -> float {
+    if constexpr (ROWS)
+      return (a * rs_tab[wm * WTM + 16 * i + l16]) * rs_tab[BM + wn * WTN + 16 * j + 4 * g + q];
+    else if constexpr (EPI_SCALE) return (a * sa) * sb;
+    else return a;
+  };
+  const int esz = OUT8 ? 1 : (p.d_f32 ? 4 : 2);
+  const bool staged = (m0 + BM <= M) && (n0 + BN <= N) && ((p.ldd * esz) % 16 == 0) &&
+                      ((reinterpret_cast<uintptr_t>(p.D) & 15u) == 0) &&
+                      (p.D_t == nullptr || ((p.ldt % 16 == 0) &&
+                                            ((reinterpret_cast<uintptr_t>(p.D_t) & 15u) == 0)));
+  uint32_t amax_bits = 0;
+  if (OUT8 && staged) {
+    // FP8 output: codes encode(fl32(v * d_scale)) of the dequantised value
+    // v, amax of |v|.  Codes go through the wavefront's LDS region twice:
+    // row-major (64 bytes per tile row, 16-byte chunk c at c ^ (r & 3)),
+    // then, for the transposed copy, column-major (row stride 144 bytes).
+    __syncthreads();
+    uint8_t* wl = &lds[0][0] + wave * 16384;
+    const float so = p.d_scale[0];
+    auto epi8 = [&](auto fmttag) {
+      constexpr int F = decltype(fmttag)::value;
+      uint32_t code[TI][TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[q] = deq(i, j, q, acc[i][j][q]);
+            const uint32_t b = __float_as_uint(v[q]) & 0x7FFFFFFFu;
+            amax_bits = b > amax_bits ? b : amax_bits;
+          }
+          code[i][j] = cvt4<F>(v[0] * so, v[1] * so, v[2] * so, v[3] * so);
+          const int r = 16 * i + l16;
+          *reinterpret_cast<uint32_t*>(wl + r * 64 + ((j ^ (r & 3)) << 4) + 4 * g) = code[i][j];
+        }
+      {
+        const int q = lane & 3, rr = lane >> 2;
+#pragma unroll
+        for (int t = 0; t < WTM / 16; ++t) {
+          const int r = 16 * t + rr;
+          const uint4 w = *reinterpret_cast<const uint4*>(wl + r * 64 + ((q ^ (r & 3)) << 4));
+          uint8_t* gp = reinterpret_cast<uint8_t*>(p.D) + (m0 + wm * WTM + r) * p.ldd + n0 +
+                        wn * WTN + q * 16;
+          *reinterpret_cast<uint4*>(gp) = w;
+        }
+      }
+      if (p.D_t) {
+        // same wavefront, LDS operations in order: the row-major reads above
+        // complete before these writes reuse the region
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              wl[(16 * j + 4 * g + q) * 144 + 16 * i + l16] = (uint8_t)(code[i][j] >> (8 * q));
+        const int c = lane & 7, rr = lane >> 3;
+#pragma unroll
+        for (int t = 0; t < WTN / 8; ++t) {
+          const int n = 8 * t + rr;
+          const uint4 w = *reinterpret_cast<const uint4*>(wl + n * 144 + 16 * c);
+          uint8_t* gp = p.D_t + (n0 + wn * WTN + n) * p.ldt + m0 + wm * WTM + 16 * c;
+          *reinterpret_cast<uint4*>(gp) = w;
+        }
+      }
+    };
+    if (p.d_fp8 == 1) epi8(std::integral_constant<int, 0>{});
+    else epi8(std::integral_constant<int, 1>{});
+  } else if (staged) {
+    __syncthreads();   // every wavefront is done reading both stages
+    uint8_t* wl = &lds[0][0] + wave * 16384;
+    auto epi = [&](auto f32tag) {
+      constexpr bool F32 = decltype(f32tag)::value;
+      constexpr int ES = F32 ? 4 : 2;
+      constexpr int ROWS_PASS = F32 ? 64 : 128;
+      constexpr int ROW_BYTES = WTN * ES;
+      constexpr int LANES_ROW = ROW_BYTES / 16;
+      constexpr int ROWS_INST = 64 / LANES_ROW;
+#pragma unroll
+      for (int pass = 0; pass < WTM / ROWS_PASS; ++pass) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          if ((16 * i) / ROWS_PASS != pass) continue;
+          const int r = 16 * i + l16 - pass * ROWS_PASS;
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = deq(i, j, q, acc[i][j][q]);
+            const int byte = (16 * j + 4 * g) * ES;
+            uint8_t* dst = wl + r * ROW_BYTES + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
+            if constexpr (F32) {
+              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+              const uint32_t h0 = f32_to_bf16_rne(v[0]), h1 = f32_to_bf16_rne(v[1]);
+              const uint32_t h2 = f32_to_bf16_rne(v[2]), h3 = f32_to_bf16_rne(v[3]);
+              *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+            }
+          }
+        }
+        // read back whole rows (same wavefront: LDS operations stay in order)
+        const int q = lane % LANES_ROW, rr = lane / LANES_ROW;
+#pragma unroll 4
+        for (int t = 0; t < ROWS_PASS / ROWS_INST; ++t) {
+          const int r = t * ROWS_INST + rr;
+          uint4 w = *reinterpret_cast<const uint4*>(wl + r * ROW_BYTES + ((q ^ (r & 7)) << 4));
+          const int64_t gm = m0 + wm * WTM + pass * ROWS_PASS + r;
+          uint8_t* gp = reinterpret_cast<uint8_t*>(p.D) + (gm * p.ldd + n0 + wn * WTN) * ES + q * 16;
+          if constexpr (F32) {
+            if (p.accumulate) {
+              const float4 o = *reinterpret_cast<const float4*>(gp);
+              w.x = __float_as_uint(o.x + __uint_as_float(w.x));
+              w.y = __float_as_uint(o.y + __uint_as_float(w.y));
+              w.z = __float_as_uint(o.z + __uint_as_float(w.z));
+              w.w = __float_as_uint(o.w + __uint_as_float(w.w));
+            }
+            const uint32_t m4[4] = {w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu, w.z & 0x7FFFFFFFu,
+                                    w.w & 0x7FFFFFFFu};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) amax_bits = m4[e] > amax_bits ? m4[e] : amax_bits;
+          } else {
+            const uint32_t m = absmax_fold(absmax_pk(absmax_pk(absmax_pk(absmax_pk(0u, w.x), w.y), w.z), w.w));
+            amax_bits = m > amax_bits ? m : amax_bits;
+          }
+          *reinterpret_cast<uint4*>(gp) = w;
+        }
+      }
+    };
+    if (p.d_f32) epi(std::true_type{});
+    else epi(std::false_type{});
+  } else {
+    const int64_t mr0 = m0 + wm * WTM + l16;
+    const int64_t nc0 = n0 + wn * WTN + 4 * g;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int64_t m = mr0 + 16 * i, n = nc0 + 16 * j;
+        if (m >= M) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (n + r >= N) continue;
+          float x = deq(i, j, r, acc[i][j][r]);
+          if (OUT8) {
+            const float xs = x * p.d_scale[0];
+            const uint8_t c = (uint8_t)((p.d_fp8 == 1 ? cvt4<0>(xs, 0.f, 0.f, 0.f)
+                                                      : cvt4<1>(xs, 0.f, 0.f, 0.f)) & 0xFFu);
+            reinterpret_cast<uint8_t*>(p.D)[m * p.ldd + n + r] = c;
+            if (p.D_t) p.D_t[(n + r) * p.ldt + m] = c;
+            const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;
+            amax_bits = b > amax_bits ? b : amax_bits;
+          } else if (p.d_f32) {
+            float* d = reinterpret_cast<float*>(p.D) + m * p.ldd + n + r;
+            if (p.accumulate) x = *d + x;
+            *d = x;
+            const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;
+            amax_bits = b > amax_bits ? b : amax_bits;
+          } else {
+            const uint16_t h = f32_to_bf16_rne(x);
+            reinterpret_cast<uint16_t*>(p.D)[m * p.ldd + n + r] = h;
+            const uint32_t b = (uint32_t)(h & 0x7FFFu) << 16;
+            amax_bits = b > amax_bits ? b : amax_bits;
+          }
+        }
+      }
+  }
+  if (p.d_amax) {   // one device atomic per workgroup
+    __shared__ uint32_t wmax[NWAVES];
+    amax_bits = wave_max_u32(amax_bits);
+    if (lane == 0) wmax[wave] = amax_bits;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int w = 0; w < NWAVES; ++w) m = wmax[w] > m ? wmax[w] : m;
+      if (m != 0u) atomic_max_bits(p.d_amax, m);
+    }
+  }
+}
+
+template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL, bool MX, bool OUT8>
+hipError_t launch_one(const GemmParams& p, hipStream_t s) {
+  auto kern = k_gemm_big<AF, BF, BLOCK, SA_ROWS, SB_COL, MX, OUT8>;
+  const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(THREADS), 0, s, p, tiles_m,
+                     tiles_n);
+  return hipGetLastError();
+}
+
+template <int AF, int BF, bool MX, bool OUT8>
+hipError_t launch_block(const GemmParams& p, hipStream_t s) {
+  const bool sa = p.a_scaling == 1 || p.a_scaling == 3, sb = p.b_scaling == 1 || p.b_scaling == 3;
+  if (sa && sb) return launch_one<AF, BF, true, true, true, MX, OUT8>(p, s);
+  if (sa) return launch_one<AF, BF, true, true, false, MX, OUT8>(p, s);
+  if (sb) return launch_one<AF, BF, true, false, true, MX, OUT8>(p, s);
+  return launch_one<AF, BF, true, false, false, MX, OUT8>(p, s);
+}
+
+// Scaling codes: 0 per-tensor, 1 / 2 block (1x128 / 128x128) with any
+// binary32 scales, 3 / 4 the same blocks with power-of-two scales, 5 one
+// scale per row (with per-tensor or per-row operands only).  When
+// every block-scaled operand has power-of-two scales the block scales go
+// into the matrix instruction; otherwise they are promoted in FP32 (a
+// power of two is a binary32 scale like any other).
+template <int AF, int BF, bool OUT8>
+hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
+  const bool row_a = p.a_scaling == 5, row_b = p.b_scaling == 5;
+  const bool block = !((p.a_scaling == 0 || row_a) && (p.b_scaling == 0 || row_b));
+  if (!block)
+    return row_a || row_b ? launch_one<AF, BF, false, true, true, false, OUT8>(p, s)
+                          : launch_one<AF, BF, false, false, false, false, OUT8>(p, s);
+  const bool mx = (p.a_scaling == 0 || p.a_scaling >= 3) && (p.b_scaling == 0 || p.b_scaling >= 3);
+  return mx ? launch_block<AF, BF, true, OUT8>(p, s) : launch_block<AF, BF, false, OUT8>(p, s);
+}
+
+// OUT8: FP8 output (its own instantiations, so that the BF16 / FP32 kernels
+// carry none of its registers).
+template <bool OUT8>
+hipError_t launch_gemm_big_out(const GemmParams& p, hipStream_t s) {
+  if (p.a_fmt == 0 && p.b_fmt == 0) return launch_fmt<0, 0, OUT8>(p, s);
+  if (p.a_fmt == 1 && p.b_fmt == 0) return launch_fmt<1, 0, OUT8>(p, s);
+  if (p.a_fmt == 0 && p.b_fmt == 1) return launch_fmt<0, 1, OUT8>(p, s);
+  return launch_fmt<1, 1, OUT8>(p, s);
+}
+
+}  // namespace
+
+}  // namespace fp8lin

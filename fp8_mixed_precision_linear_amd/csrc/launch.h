@@ -69,5 +69,6 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 // cover a 256-row panel of each operand).
 bool gemm_big_supported(const GemmParams& p);
 hipError_t launch_gemm_big(const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm_big_fp8out(const GemmParams& p, hipStream_t s);   // p.d_fp8 != 0
 
 }  // namespace fp8lin

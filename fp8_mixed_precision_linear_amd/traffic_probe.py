@@ -30,7 +30,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 256 << 20
 REPS = 3
-SOURCES = ("csrc/gemm_big.hip", "csrc/cast_kernels.hip", "csrc/fp8_device.h")
+SOURCES = ("csrc/gemm_big_kernel.h", "csrc/gemm_big.hip", "csrc/cast_kernels.hip",
+           "csrc/fp8_device.h")
 
 
 def sources_sha256() -> str:
@@ -89,9 +90,9 @@ def _classify(name: str):
         return "gemm_dgrad_tensor"
     if "k_gemm_big<0, 1, false" in name:
         return "gemm_wgrad_tensor"
-    if "k_cast_transpose<0, true, true>" in name:
+    if "k_cast_transpose<0, true, true, false>" in name:
         return "cast_transpose_amax_e4m3"
-    if "k_cast_transpose<1, true, true>" in name:
+    if "k_cast_transpose<1, true, true, false>" in name:
         return "cast_transpose_amax_e5m2"
     return None
 
