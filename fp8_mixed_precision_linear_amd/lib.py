@@ -118,6 +118,13 @@ _F32 = (torch.float32,)
 _U8 = (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2)
 
 
+def _need(t, n, name):
+    """Raise unless tensor t (if given) holds at least n elements: the C ABI
+    cannot see buffer sizes, so the binding checks them before any launch."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n}")
+
+
 def _rc(x):
     """(rows, cols) of a tensor viewed as [rows][cols] (1-D: one row)."""
     if x.dim() == 0:
@@ -132,11 +139,14 @@ def _rc(x):
 
 def fp8_amax(x, amax, stream=None):
     rows, cols = _rc(x)
+    _need(amax, 1, "amax")
     _check("fp8_amax", _L.fp8_amax(_ptr(x, _BF16, "x"), rows, cols, _ptr(amax, _F32, "amax"),
                                    _stream(stream)))
 
 
 def _compute_scale(fn, amax, fmt, margin, scale, scale_inv, stream):
+    _need(scale, amax.numel(), "scale")
+    _need(scale_inv, amax.numel(), "scale_inv")
     _check(fn.__name__,
            fn(_ptr(amax, _F32, "amax"), amax.numel(), fmt, margin,
               _ptr(scale, _F32, "scale"), _ptr(scale_inv, _F32, "scale_inv"), _stream(stream)))
@@ -152,6 +162,8 @@ def fp8_compute_scale_pow2(amax, fmt, margin, scale, scale_inv, stream=None):
 
 def _history(fn, history, amax_new, fmt, margin, algo, scale, scale_inv, stream):
     n, ln = history.shape
+    for name, t in (("amax_new", amax_new), ("scale", scale), ("scale_inv", scale_inv)):
+        _need(t, n, name)
     _check(fn.__name__,
            fn(_ptr(history, _F32, "history"), n, ln, _ptr(amax_new, _F32, "amax_new"), fmt, margin,
               algo, _ptr(scale, _F32, "scale"), _ptr(scale_inv, _F32, "scale_inv"), _stream(stream)))
@@ -168,15 +180,24 @@ def fp8_amax_history_update_pow2(history, amax_new, fmt, margin, algo, scale, sc
              scale_inv, stream)
 
 
-def _cast(fn, x, scale, y, y_t, amax_out, stream):
+def _cast_sizes(x, scale, y, y_t, amax_out):
     rows, cols = _rc(x)
+    _need(scale, 1, "scale")
+    _need(y, rows * cols, "y")
+    _need(y_t, rows * cols, "y_t")
+    _need(amax_out, 1, "amax_out")
+    return rows, cols
+
+
+def _cast(fn, x, scale, y, y_t, amax_out, stream):
+    rows, cols = _cast_sizes(x, scale, y, y_t, amax_out)
     _check(fn.__name__, fn(_ptr(x, _BF16, "x"), rows, cols, _ptr(scale, _F32, "scale"),
                            _ptr(y, _U8, "y"), _ptr(y_t, _U8, "y_t"),
                            _ptr(amax_out, _F32, "amax_out"), _stream(stream)))
 
 
 def fp8_cast_sr(x, fmt, scale, seed, offset=0, y=None, y_t=None, amax_out=None, stream=None):
-    rows, cols = _rc(x)
+    rows, cols = _cast_sizes(x, scale, y, y_t, amax_out)
     _check("fp8_cast_sr",
            _L.fp8_cast_sr(_ptr(x, _BF16, "x"), rows, cols, fmt, _ptr(scale, _F32, "scale"),
                           int(seed), int(offset), _ptr(y, _U8, "y"), _ptr(y_t, _U8, "y_t"),
@@ -204,6 +225,11 @@ def fp8_cast_e5m2(x, scale, y=None, y_t=None, amax_out=None, stream=None):
 
 def _cast_block(fn, x, fmt, tile, y, scale_inv, y_t, scale_inv_t, stream):
     rows, cols = _rc(x)
+    nrb, ncb = (rows + 127) // 128, (cols + 127) // 128
+    _need(y, rows * cols, "y")
+    _need(y_t, rows * cols, "y_t")
+    _need(scale_inv, ncb * (rows if tile == SCALE_1x128 else nrb), "scale_inv")
+    _need(scale_inv_t, nrb * (cols if tile == SCALE_1x128 else ncb), "scale_inv_t")
     _check(fn.__name__,
            fn(_ptr(x, _BF16, "x"), rows, cols, fmt, tile, _ptr(y, _U8, "y"),
               _ptr(scale_inv, _F32, "scale_inv"), _ptr(y_t, _U8, "y_t"),
@@ -221,6 +247,10 @@ def fp8_cast_block_pow2(x, fmt, tile, y=None, scale_inv=None, y_t=None, scale_in
 
 def fp8_cast_rowwise(x, fmt, y=None, scale_inv=None, y_t=None, scale_inv_t=None, stream=None):
     rows, cols = _rc(x)
+    _need(y, rows * cols, "y")
+    _need(scale_inv, rows, "scale_inv")
+    _need(y_t, rows * cols, "y_t")
+    _need(scale_inv_t, cols, "scale_inv_t")
     _check("fp8_cast_rowwise",
            _L.fp8_cast_rowwise(_ptr(x, _BF16, "x"), rows, cols, fmt, _ptr(y, _U8, "y"),
                                _ptr(scale_inv, _F32, "scale_inv"), _ptr(y_t, _U8, "y_t"),
@@ -244,6 +274,19 @@ def fp8_scaled_gemm(A, a_fmt, a_scaling, a_scale_inv, B, b_fmt, b_scaling, b_sca
             raise ValueError(f"D_t must be [{N}][{M}], got {tuple(D_t.shape)}")
     else:
         d_dtype = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32}[D.dtype]
+    nkb = (K + 127) // 128
+
+    def scales_needed(scaling, rows):
+        if scaling in (SCALE_1x128, SCALE_1x128_POW2):
+            return nkb * rows
+        if scaling in (SCALE_128x128, SCALE_128x128_POW2):
+            return nkb * ((rows + 127) // 128)
+        return rows if scaling == SCALE_ROW else 1
+    if K > 0 and M > 0 and N > 0:
+        _need(a_scale_inv, scales_needed(a_scaling, M), "a_scale_inv")
+        _need(b_scale_inv, scales_needed(b_scaling, N), "b_scale_inv")
+    _need(d_amax, 1, "d_amax")
+    _need(d_scale, 1, "d_scale")
     g = GemmArgs(M, N, K, K, K, N,
                  _ptr(A, _U8, "A"), a_fmt, a_scaling, _ptr(a_scale_inv, _F32, "a_scale_inv"),
                  _ptr(B, _U8, "B"), b_fmt, b_scaling, _ptr(b_scale_inv, _F32, "b_scale_inv"),

@@ -135,3 +135,27 @@ def test_gemm_validation(L):
     assert _gemm(L, d_dtype=3, d_scale=0x6000, accumulate=1) == 4
     assert _gemm(L, D_t=0x7000, ldt=64) == 6          # D_t with a BF16 output
     assert _gemm(L, d_dtype=2, d_scale=0x6000, D_t=0x7000, ldt=10) == 2
+
+
+def test_binding_checks_buffer_sizes(L):
+    """The C ABI cannot see buffer sizes: the binding refuses undersized
+    tensors before any launch (CPU tensors are never passed on)."""
+    import torch
+    x = torch.zeros((4, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="y holds 31"):
+        L.fp8_cast_e4m3(x, torch.ones(1), y=torch.empty(31, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="scale_inv holds 3"):
+        L.fp8_cast_rowwise(x, 0, y=torch.empty((4, 8), dtype=torch.uint8), scale_inv=torch.empty(3))
+    with pytest.raises(ValueError, match="scale_inv_t holds 1"):
+        L.fp8_cast_block(x, 0, 1, y_t=torch.empty((8, 4), dtype=torch.uint8),
+                         scale_inv_t=torch.empty(1))
+    with pytest.raises(ValueError, match="scale holds 1"):
+        L.fp8_amax_history_update(torch.zeros((2, 16)), torch.zeros(2), 0, 0, 0, torch.ones(1),
+                                  torch.ones(2))
+    A = torch.zeros((256, 384), dtype=torch.uint8)
+    B = torch.zeros((128, 384), dtype=torch.uint8)
+    D = torch.zeros((256, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="a_scale_inv holds 255"):
+        L.fp8_scaled_gemm(A, 0, L.SCALE_ROW, torch.ones(255), B, 0, 0, torch.ones(1), D)
+    with pytest.raises(ValueError, match="b_scale_inv holds 2"):
+        L.fp8_scaled_gemm(A, 0, 0, torch.ones(1), B, 0, L.SCALE_1x128, torch.ones(2), D)
