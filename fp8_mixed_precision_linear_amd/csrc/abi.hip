@@ -50,13 +50,15 @@ const char* fp8_status_string(fp8_status status) {
   return "unknown status";
 }
 
-fp8_status fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, float* amax,
+fp8_status fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, float* amax,
                     hipStream_t stream) {
-  if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
+  if (rows < 0 || cols < 0 || ld < cols) return FP8_ERR_SHAPE;
   if (amax == nullptr) return FP8_ERR_NULL;
   if (rows > 0 && cols > 0 && x_bf16 == nullptr) return FP8_ERR_NULL;
   if (!aligned16(x_bf16) || !aligned4(amax)) return FP8_ERR_ALIGN;
-  return launched(launch_amax(static_cast<const uint16_t*>(x_bf16), rows * cols, amax, stream));
+  const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
+  if (ld == cols || rows <= 1) return launched(launch_amax(x, rows * cols, amax, stream));
+  return launched(launch_amax_rows(x, rows, cols, ld, amax, stream));
 }
 
 }  // extern "C"

@@ -158,6 +158,37 @@ __global__ void __launch_bounds__(64) k_history_update(float* __restrict__ histo
 
 inline float fmax_of(int fmt) { return fmt == 0 ? kMaxE4M3 : kMaxE5M2; }
 
+// max |x| over a [rows][cols] bf16 matrix with row stride ld (elements): a
+// persistent grid walks the rows; 16-byte loads when every row start is
+// 16-byte aligned (ld % 8 == 0), element loads otherwise and for the last
+// cols % 8 values of a row.
+__global__ void __launch_bounds__(kAmaxThreads) k_amax_rows(const uint16_t* __restrict__ x,
+                                                            int64_t rows, int64_t cols, int64_t ld,
+                                                            float* __restrict__ amax) {
+  uint32_t mp = 0, m = 0;
+  const bool vec = (ld & 7) == 0;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const uint16_t* xr = x + r * ld;
+    int64_t c0 = 0;
+    if (vec) {
+      const int64_t nv = cols >> 3;
+      for (int64_t i = threadIdx.x; i < nv; i += blockDim.x) {
+        const uint4 a = ld_nt16(xr + 8 * i);
+        mp = absmax_pk(mp, a.x); mp = absmax_pk(mp, a.y);
+        mp = absmax_pk(mp, a.z); mp = absmax_pk(mp, a.w);
+      }
+      c0 = nv << 3;
+    }
+    for (int64_t c = c0 + threadIdx.x; c < cols; c += blockDim.x) {
+      const uint32_t t = (uint32_t)(xr[c] & 0x7FFFu) << 16;
+      m = m > t ? m : t;
+    }
+  }
+  const uint32_t f = absmax_fold(mp);
+  block_max_to(amax, m > f ? m : f);
+}
+
+
 }  // namespace
 
 int64_t device_cu_count() {
@@ -180,6 +211,16 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
+                            hipStream_t s) {
+  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 1, 0u, s);
+  if (e != hipSuccess || rows == 0 || cols == 0) return e;
+  int64_t blocks = rows < device_cu_count() ? rows : device_cu_count();
+  hipLaunchKernelGGL(k_amax_rows, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, s, x, rows, cols,
+                     ld, amax);
   return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@ def _load():
     sig = {
         "fp8_abi_version": (i32, []),
         "fp8_status_string": (C.c_char_p, [i32]),
-        "fp8_amax": (i32, [vp, i64, i64, vp, vp]),
+        "fp8_amax": (i32, [vp, i64, i64, i64, vp, vp]),
         "fp8_compute_scale": (i32, [vp, i64, i32, i32, vp, vp, vp]),
         "fp8_compute_scale_pow2": (i32, [vp, i64, i32, i32, vp, vp, vp]),
         "fp8_amax_history_update": (i32, [vp, i64, i64, vp, i32, i32, i32, vp, vp, vp]),
@@ -138,10 +138,19 @@ def _rc(x):
 
 
 def fp8_amax(x, amax, stream=None):
-    rows, cols = _rc(x)
+    """amax of x: a contiguous tensor, or a 2-D view whose rows are strided
+    (row stride >= number of columns, unit column stride)."""
     _need(amax, 1, "amax")
-    _check("fp8_amax", _L.fp8_amax(_ptr(x, _BF16, "x"), rows, cols, _ptr(amax, _F32, "amax"),
-                                   _stream(stream)))
+    if x.dim() == 2 and not x.is_contiguous() and x.stride(1) == 1 and x.stride(0) >= x.shape[1]:
+        rows, cols, ld = x.shape[0], x.shape[1], x.stride(0)
+        if not x.is_cuda or x.dtype not in _BF16:
+            raise TypeError("x must be a bf16 GPU tensor")
+        xp = x.data_ptr() or None
+    else:
+        rows, cols = _rc(x)
+        ld = cols
+        xp = _ptr(x, _BF16, "x")
+    _check("fp8_amax", _L.fp8_amax(xp, rows, cols, ld, _ptr(amax, _F32, "amax"), _stream(stream)))
 
 
 def _compute_scale(fn, amax, fmt, margin, scale, scale_inv, stream):

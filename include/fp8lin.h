@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 4
+#define FP8LIN_ABI_VERSION 5
 
 /* [MPG] "The precision formats", "FP8 E4M3", "FP8 E5M2": E4M3 = 4 exponent
  * and 3 mantissa bits, range about 2^-9..448; E5M2 = 5 and 2, range about
@@ -95,14 +95,16 @@ const char* fp8_status_string(fp8_status status);
  * fp8_amax -- amax = max |x| over a bf16 tensor.
  * [MPG] "Transformer Engine internals > Per-tensor scaling": the scale is
  * set from the tensor's maximum absolute value.
- *   x_bf16  [rows][cols] bf16, 16-byte aligned.
+ *   x_bf16  [rows][ld] bf16 (the first cols of each row are read),
+ *           16-byte aligned; ld >= cols, in elements (ld == cols: a
+ *           contiguous tensor).
  *   amax    1 float, overwritten.  The maximum is exact (no rounding is
  *           involved); a NaN element makes the result NaN; an empty tensor
  *           gives 0.
  * Errors: FP8_ERR_NULL (x with rows*cols > 0, or amax NULL), FP8_ERR_SHAPE
- * (negative size), FP8_ERR_ALIGN (x not 16-byte aligned).
+ * (negative size, ld < cols), FP8_ERR_ALIGN (x not 16-byte aligned).
  * ---------------------------------------------------------------------- */
-fp8_status fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, float* amax,
+fp8_status fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, float* amax,
                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.abi_version() == 4
+    assert L.abi_version() == 5
     for s in range(7):
         assert isinstance(L.status_string(s), str) and L.status_string(s)
     assert L.status_string(99) == "unknown status"
@@ -48,11 +48,12 @@ def test_version_and_status_strings(L):
 def test_host_validation_before_launch(L):
     f = L._L
     # negative sizes
-    assert f.fp8_amax(None, -1, 4, None, None) == 2
+    assert f.fp8_amax(None, -1, 4, 4, None, None) == 2
+    assert f.fp8_amax(C.c_void_p(0x1000), 4, 8, 7, C.c_void_p(0x2000), None) == 2   # ld < cols
     # missing output
-    assert f.fp8_amax(None, 0, 0, None, None) == 1
+    assert f.fp8_amax(None, 0, 0, 0, None, None) == 1
     # misaligned input pointer (never dereferenced: rejected first)
-    assert f.fp8_amax(C.c_void_p(0x1002), 4, 4, C.c_void_p(0x2000), None) == 3
+    assert f.fp8_amax(C.c_void_p(0x1002), 4, 4, 4, C.c_void_p(0x2000), None) == 3
     # scale: bad format / margin / n
     assert f.fp8_compute_scale(None, 1, 7, 0, None, None, None) == 6
     assert f.fp8_compute_scale(None, 1, 0, 99, None, None, None) == 6

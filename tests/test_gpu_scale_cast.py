@@ -55,6 +55,28 @@ def test_amax_specials(O, L):
         assert bits(out.cpu().numpy())[0] == bits(O.amax(x)), hex(special)
 
 
+@pytest.mark.parametrize("shape,ld,c0", [((64, 300), 512, 8), ((33, 77), 101, 0), ((1000, 8), 16, 0),
+                                         ((5, 4096), 4104, 8), ((2, 1), 9, 0), ((3, 5), 11, 0)])
+def test_amax_strided_rows(O, L, shape, ld, c0):
+    """A [rows][cols] view of a wider buffer (row stride ld): 16-byte row
+    loads when ld % 8 == 0, element loads otherwise."""
+    rows, cols = shape
+    rng = np.random.default_rng(rows + ld)
+    big = datagen.normal(rng, (rows, ld), 1.0)
+    big[:, :c0] = datagen.bf16_bits(np.full((rows, c0), 1e4, np.float32))   # outside the view
+    big[:, c0 + cols:] = datagen.bf16_bits(np.full((rows, ld - c0 - cols), -2e4, np.float32))
+    view = np.ascontiguousarray(big[:, c0:c0 + cols])
+    view.reshape(-1)[rows * cols // 2] = datagen.bf16_bits(np.array([-77.0], np.float32))[0]
+    big[:, c0:c0 + cols] = view
+    d = dev_bf16(big)
+    x = d[:, c0:c0 + cols]
+    out = Guarded((1,), torch.float32)
+    L.fp8_amax(x, out.t)
+    torch.cuda.synchronize()
+    out.check()
+    assert bits(out.np())[0] == bits(O.amax(view))
+
+
 # ----------------------------------------------------------------- scale ---
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("margin", [0, 3])
