@@ -90,6 +90,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(b >> 16);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two binary32 values -> two bf16 (a in the low half), round to nearest even.
+// One v_cvt_pk_bf16_f32; that instruction does not round binary32
+// subnormal inputs to nearest (measured over all 2^32 inputs: every other
+// input, NaN included, matches f32_to_bf16_rne), so a pair holding a
+// subnormal takes the integer path.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  if (__builtin_expect(__builtin_isfpclass(a, 0x90) | __builtin_isfpclass(b, 0x90), 0))
+    return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // Raw buffer resource (wave-uniform): base, no stride, `bytes` records.
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -470,9 +485,7 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
             if constexpr (F32) {
               *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
             } else {
-              const uint32_t h0 = f32_to_bf16_rne(v[0]), h1 = f32_to_bf16_rne(v[1]);
-              const uint32_t h2 = f32_to_bf16_rne(v[2]), h3 = f32_to_bf16_rne(v[3]);
-              *reinterpret_cast<uint2*>(dst) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+              *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]));
             }
           }
         }
@@ -492,11 +505,13 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
               w.z = __float_as_uint(o.z + __uint_as_float(w.z));
               w.w = __float_as_uint(o.w + __uint_as_float(w.w));
             }
-            const uint32_t m4[4] = {w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu, w.z & 0x7FFFFFFFu,
-                                    w.w & 0x7FFFFFFFu};
+            if (p.d_amax) {
+              const uint32_t m4[4] = {w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu, w.z & 0x7FFFFFFFu,
+                                      w.w & 0x7FFFFFFFu};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) amax_bits = m4[e] > amax_bits ? m4[e] : amax_bits;
-          } else {
+              for (int e = 0; e < 4; ++e) amax_bits = m4[e] > amax_bits ? m4[e] : amax_bits;
+            }
+          } else if (p.d_amax) {
             const uint32_t m = absmax_fold(absmax_pk(absmax_pk(absmax_pk(absmax_pk(0u, w.x), w.y), w.z), w.w));
             amax_bits = m > amax_bits ? m : amax_bits;
           }

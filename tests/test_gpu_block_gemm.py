@@ -238,3 +238,24 @@ def test_gemm_quantised_data_vs_unquantised_reference(O, L, mode):
         R, Bd = O.gemm_ref_bound(A, 0, asc, sa, B, 0, bsc, sb, a16, b16)
         u_out = 2.0 ** -8 if not out_f32 else 0.0
         assert np.all(np.abs(G - R) <= Bd + u_out * np.abs(G))
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 256), (200, 136, 384)])
+def test_gemm_bf16_output_in_f32_subnormal_range(O, L, shape):
+    """Per-tensor scales 2^-70 x 2^-71 put every output in binary32's
+    subnormal range: the BF16 rounding there must still be to nearest even
+    (those pairs leave the hardware conversion for the integer path).  The
+    data is exactly summable, so the GPU's binary32 value equals the
+    oracle's F and the BF16 bits must match exactly."""
+    M, N, K = shape
+    say("gemm bf16 subnormal outputs", shape)
+    rng = np.random.default_rng(M + N + K)
+    A = narrow_codes(rng, (M, K), 0)
+    B = narrow_codes(rng, (N, K), 0)
+    sa = np.array([2.0 ** -70], np.float32)
+    sb = np.array([2.0 ** -71], np.float32)
+    G, raw, am = run_gemm(L, A, 0, 0, sa, B, 0, 0, sb, False)
+    F = O.gemm(A, 0, 0, sa, B, 0, 0, sb, want=("F",))["F"]
+    assert np.all(np.abs(F) < 2.0 ** -126) and np.count_nonzero(F) > F.size // 2   # the case under test
+    assert np.array_equal(raw, O.f32_to_bf16(F).reshape(F.shape))
+    assert bits(am) == bits(amax_of_output(raw, False))
