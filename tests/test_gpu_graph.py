@@ -133,3 +133,57 @@ def test_gemm_amax_and_block_cast_graph_replay(L):
         torch.cuda.synchronize()
         for i, (t, w) in enumerate(zip(outs, want)):
             assert torch.equal(t.view(torch.uint8), w.view(torch.uint8)), (r, i)
+
+
+def test_rowwise_sr_ewma_graph_replay(L):
+    """The row-wise cast (four kernels, partial column maxima kept in the
+    outputs while it runs), a per-row GEMM with an FP8 output, the
+    stochastic-rounding cast and the EWMA update, captured and replayed:
+    every replay equals the eager run (the EWMA state is reset first)."""
+    rng = np.random.default_rng(9)
+    R, Cc, N = 256, 384, 512
+    x = dev_bf16(datagen.student_t3(rng, (R, Cc), 1.0))
+    w = dev_bf16(datagen.normal(rng, (N, Cc), 0.02))
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    xq, sx, xtq, sxt = (torch.empty((R, Cc), **u8), torch.empty(R, device="cuda"),
+                        torch.empty((Cc, R), **u8), torch.empty(Cc, device="cuda"))
+    wq, sw = torch.empty((N, Cc), **u8), torch.empty(N, device="cuda")
+    y8, y8t = torch.empty((R, N), **u8), torch.empty((N, R), **u8)
+    yam = torch.empty(1, device="cuda")
+    so = torch.tensor([3.0], device="cuda")
+    sq, sqt, sam = torch.empty((R, Cc), **u8), torch.empty((Cc, R), **u8), torch.empty(1, device="cuda")
+    ewma, esc, esi = (torch.zeros(2, device="cuda"), torch.ones(2, device="cuda"),
+                      torch.ones(2, device="cuda"))
+    am2 = torch.tensor([3.0, 7.0], device="cuda")
+
+    def work():
+        L.fp8_cast_rowwise(x, 0, xq, sx, xtq, sxt)
+        L.fp8_cast_rowwise(w, 0, wq, sw)
+        L.fp8_scaled_gemm(xq, 0, L.SCALE_ROW, sx, wq, 0, L.SCALE_ROW, sw, y8, d_amax=yam,
+                          d_scale=so, d_fmt=0, D_t=y8t)
+        L.fp8_cast_sr(x, 1, so, 77, 5, y=sq, y_t=sqt, amax_out=sam)
+        L.fp8_amax_ewma_update(ewma, am2, 0.5, 0, 0, esc, esi)
+        L.fp8_amax_ewma_update(ewma, am2, 0.5, 0, 0, esc, esi)
+
+    outs = (xq, sx, xtq, sxt, wq, sw, y8, y8t, yam, sq, sqt, sam, ewma, esc, esi)
+
+    def clear():
+        for t in outs:
+            t.view(torch.uint8).fill_(0xC3)
+        ewma.zero_()
+        esc.fill_(1.0)
+        esi.fill_(1.0)
+
+    clear()
+    work()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outs]
+    g = _capture(work)
+    for r in range(3):
+        say("rowwise/sr/ewma graph replay", r)
+        clear()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (t, wnt) in enumerate(zip(outs, want)):
+            assert torch.equal(t.view(torch.uint8), wnt.view(torch.uint8)), (r, i)
