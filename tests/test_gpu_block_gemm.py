@@ -259,3 +259,53 @@ def test_gemm_bf16_output_in_f32_subnormal_range(O, L, shape):
     assert np.all(np.abs(F) < 2.0 ** -126) and np.count_nonzero(F) > F.size // 2   # the case under test
     assert np.array_equal(raw, O.f32_to_bf16(F).reshape(F.shape))
     assert bits(am) == bits(amax_of_output(raw, False))
+
+
+@pytest.mark.parametrize("mode", [(0, 0), (1, 2), (3, 4), (5, 5)])
+@pytest.mark.parametrize("out", ["bf16", "f32", "e4m3"])
+def test_gemm_leading_dimensions(L, mode, out):
+    """Operands and output inside wider buffers (lda > K, ldb > K, ldd > N,
+    ldt > M) through the C ABI: the result equals the contiguous call bit
+    for bit, and the padding is never written."""
+    import ctypes as C
+    M, N, K = 300, 264, 384
+    asc, bsc = mode
+    say("gemm leading dims", mode, out)
+    rng = np.random.default_rng(17 + asc + 3 * bsc)
+    A = rand_codes(rng, (M, K), 0)
+    B = rand_codes(rng, (N, K), 1)
+    nkb = K // 128
+    if asc == 5:
+        sa, sb = np.exp2(rng.uniform(-8, 2, M)).astype(np.float32), np.exp2(rng.uniform(-8, 2, N)).astype(np.float32)
+    elif asc == 0:
+        sa, sb = np.float32([0.5]), np.float32([0.25])
+    else:
+        sa = np.exp2(rng.integers(-8, 3, (nkb, M))).astype(np.float32)
+        sb = np.exp2(rng.integers(-8, 3, (nkb, (N + 127) // 128))).astype(np.float32)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "e4m3": torch.uint8}[out]
+    d_dtype = {"bf16": L.OUT_BF16, "f32": L.OUT_F32, "e4m3": L.OUT_E4M3}[out]
+    lda, ldb, ldd, ldt = K + 32, K + 64, N + 16, M + 20
+    Ad = torch.full((M, lda), 0x3C, dtype=torch.uint8, device="cuda")
+    Bd = torch.full((N, ldb), 0x3C, dtype=torch.uint8, device="cuda")
+    Ad[:, :K] = torch.from_numpy(A).cuda()
+    Bd[:, :K] = torch.from_numpy(B).cuda()
+    sad, sbd, dsc = dev(sa), dev(sb), torch.tensor([2.0], device="cuda")
+    Dw = torch.full((M, ldd), 0, dtype=dt, device="cuda").view(torch.uint8).fill_(0xA5).view(dt)
+    Dtw = torch.full((N, ldt), 0xA5, dtype=torch.uint8, device="cuda") if out == "e4m3" else None
+    g = L.GemmArgs(M, N, K, lda, ldb, ldd, Ad.data_ptr(), 0, asc, sad.data_ptr(), Bd.data_ptr(), 1,
+                   bsc, sbd.data_ptr(), Dw.data_ptr(), d_dtype, None, 0,
+                   dsc.data_ptr() if out == "e4m3" else None,
+                   Dtw.data_ptr() if Dtw is not None else None, ldt)
+    assert L._L.fp8_scaled_gemm(C.byref(g), C.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+    # the contiguous call through the binding
+    D = torch.empty((M, N), dtype=dt, device="cuda")
+    Dt = torch.empty((N, M), dtype=torch.uint8, device="cuda") if out == "e4m3" else None
+    L.fp8_scaled_gemm(dev(A), 0, asc, sad, dev(B), 1, bsc, sbd, D,
+                      d_scale=dsc if out == "e4m3" else None, d_fmt=0 if out == "e4m3" else None,
+                      D_t=Dt)
+    torch.cuda.synchronize()
+    assert torch.equal(Dw[:, :N].contiguous().view(torch.uint8), D.view(torch.uint8))
+    assert torch.all(Dw[:, N:].contiguous().view(torch.uint8) == 0xA5)
+    if out == "e4m3":
+        assert torch.equal(Dtw[:, :M].contiguous(), Dt)
+        assert torch.all(Dtw[:, M:] == 0xA5)
