@@ -93,14 +93,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Two binary32 values -> two bf16 (a in the low half), round to nearest even.
-// One v_cvt_pk_bf16_f32; that instruction does not round binary32
-// subnormal inputs to nearest (measured over all 2^32 inputs: every other
-// input, NaN included, matches f32_to_bf16_rne), so a pair holding a
-// subnormal takes the integer path.
-__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
-  if (__builtin_expect(__builtin_isfpclass(a, 0x90) | __builtin_isfpclass(b, 0x90), 0))
-    return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+// Two binary32 values -> two bf16 (a in the low half) with one
+// v_cvt_pk_bf16_f32: round to nearest even, except that the instruction does
+// not round binary32 subnormal inputs to nearest (measured over all 2^32
+// inputs: every other input, NaN included, matches f32_to_bf16_rne).  The
+// caller handles subnormals with f32_to_bf16_rne.
+__device__ __forceinline__ uint32_t bf16x2_hw(float a, float b) {
   const f32x2 v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
@@ -182,41 +180,6 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   // instruction; lane p lands in row 8*it + (p >> 3), stored chunk p & 7
   const int lrow = 32 * wave + (lane >> 3);
 
-  if constexpr (ROWS) {   // thread t < BM: A's scale of D row m0 + t; else B's of column n0 + t - BM
-    static_assert(THREADS == BM + BN, "one row scale per thread");
-    const bool is_a = tid < BM;
-    const int64_t r = is_a ? m0 + tid : n0 + (tid - BM);
-    const int64_t lim = is_a ? M : N;
-    const int row_mode = is_a ? p.a_scaling == 5 : p.b_scaling == 5;
-    rs_tab[tid] = (is_a ? p.a_sinv : p.b_sinv)[row_mode ? (r < lim ? r : lim - 1) : 0];
-  }
-
-  // ---- per-wavefront table of the uniform part of each K block's scale
-  if constexpr (BLOCK && !(SA_ROWS && SB_COL)) {
-    const int64_t mb = min((m0 + wm * WTM) / 128, (M + 127) / 128 - 1);
-    const int64_t nb = min((n0 + wn * WTN) / 128, (N + 127) / 128 - 1);
-    for (int kb = lane; kb < nk; kb += 64) {
-      if constexpr (MX) {
-        // E8M0 codes of the uniform block scales: A in bits 0-7, B in 8-15
-        // (127 = 1.0 for a per-tensor operand, whose scale goes to the
-        // epilogue)
-        int ea = 127, eb = 127;
-        if constexpr (!SA_ROWS)
-          if (p.a_scaling != 0) ea = e8m0_of(p.a_sinv[kb * ((M + 127) / 128) + mb]);
-        if constexpr (!SB_COL)
-          if (p.b_scaling != 0) eb = e8m0_of(p.b_sinv[kb * ((N + 127) / 128) + nb]);
-        su_tab[wave][kb] = __uint_as_float((uint32_t)ea | ((uint32_t)eb << 8));
-      } else {
-        float s = 1.0f;
-        if constexpr (!SA_ROWS)
-          s = p.a_scaling == 0 ? p.a_sinv[0] : p.a_sinv[kb * ((M + 127) / 128) + mb];
-        if constexpr (!SB_COL)
-          s *= p.b_scaling == 0 ? p.b_sinv[0] : p.b_sinv[kb * ((N + 127) / 128) + nb];
-        su_tab[wave][kb] = s;
-      }
-    }
-  }
-
   auto load_stage = [&](int kb, uint8_t* base) {
     const int k0 = kb * BK;
     const uint32_t lb = lds_addr(base);
@@ -252,8 +215,51 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // the first two stages go out together, so the second one's latency
+  // overlaps the first's; the loop's first step then issues no DMA
   load_stage(0, lds[0]);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (nk > 1) load_stage(1, lds[1]);
+
+  if constexpr (ROWS) {   // thread t < BM: A's scale of D row m0 + t; else B's of column n0 + t - BM
+    static_assert(THREADS == BM + BN, "one row scale per thread");
+    const bool is_a = tid < BM;
+    const int64_t r = is_a ? m0 + tid : n0 + (tid - BM);
+    const int64_t lim = is_a ? M : N;
+    const int row_mode = is_a ? p.a_scaling == 5 : p.b_scaling == 5;
+    rs_tab[tid] = (is_a ? p.a_sinv : p.b_sinv)[row_mode ? (r < lim ? r : lim - 1) : 0];
+  }
+
+  // ---- per-wavefront table of the uniform part of each K block's scale
+  if constexpr (BLOCK && !(SA_ROWS && SB_COL)) {
+    const int64_t mb = min((m0 + wm * WTM) / 128, (M + 127) / 128 - 1);
+    const int64_t nb = min((n0 + wn * WTN) / 128, (N + 127) / 128 - 1);
+    for (int kb = lane; kb < nk; kb += 64) {
+      if constexpr (MX) {
+        // E8M0 codes of the uniform block scales: A in bits 0-7, B in 8-15
+        // (127 = 1.0 for a per-tensor operand, whose scale goes to the
+        // epilogue)
+        int ea = 127, eb = 127;
+        if constexpr (!SA_ROWS)
+          if (p.a_scaling != 0) ea = e8m0_of(p.a_sinv[kb * ((M + 127) / 128) + mb]);
+        if constexpr (!SB_COL)
+          if (p.b_scaling != 0) eb = e8m0_of(p.b_sinv[kb * ((N + 127) / 128) + nb]);
+        su_tab[wave][kb] = __uint_as_float((uint32_t)ea | ((uint32_t)eb << 8));
+      } else {
+        float s = 1.0f;
+        if constexpr (!SA_ROWS)
+          s = p.a_scaling == 0 ? p.a_sinv[0] : p.a_sinv[kb * ((M + 127) / 128) + mb];
+        if constexpr (!SB_COL)
+          s *= p.b_scaling == 0 ? p.b_sinv[0] : p.b_sinv[kb * ((N + 127) / 128) + nb];
+        su_tab[wave][kb] = s;
+      }
+    }
+  }
+
+  // stage 0 only: at most 8 DMAs of stage 1 may remain (the wavefronts that
+  // also load scales have 12 in stage 1 and wait for 4 of them as well;
+  // loads count down in issue order)
+  if (nk > 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int kb = 0; kb < nk; ++kb) {
@@ -270,7 +276,7 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     v8i bfr[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) bfr[j] = frag(Bs, wn * WTN + 16 * j + l16, g);
-    if (kb + 1 < nk) load_stage(kb + 1, lds[stage ^ 1]);
+    if (kb > 0 && kb + 1 < nk) load_stage(kb + 1, lds[stage ^ 1]);
 
     // The MFMA takes B as its first operand, so each 16x16 result tile is
     // the transpose of the D tile: lane (g, l16) holds D row 16*i + l16,
@@ -350,6 +356,12 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
         for (int j = 0; j < TJ; ++j) pprev[j] = pcur[j];
         sprev = srow;
         a_cur = a_nxt;
+        // one matrix instruction, then its share of the promotion
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, SB_COL ? 8 : 4, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       promote(TI - 1, pprev, sprev);
@@ -471,23 +483,41 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
       constexpr int ROWS_INST = 64 / LANES_ROW;
 #pragma unroll
       for (int pass = 0; pass < WTM / ROWS_PASS; ++pass) {
+        // BF16: the hardware pair conversion, one row-tile at a time; a
+        // row-tile in which any lane holds a binary32 subnormal (which that
+        // instruction does not round to nearest) is written again with the
+        // integer rounding
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
           if ((16 * i) / ROWS_PASS != pass) continue;
           const int r = 16 * i + l16 - pass * ROWS_PASS;
+          auto put = [&](auto softtag) -> bool {
+            constexpr bool SOFT = decltype(softtag)::value;
+            bool sub = false;
 #pragma unroll
-          for (int j = 0; j < TJ; ++j) {
-            float v[4];
+            for (int j = 0; j < TJ; ++j) {
+              float v[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = deq(i, j, q, acc[i][j][q]);
-            const int byte = (16 * j + 4 * g) * ES;
-            uint8_t* dst = wl + r * ROW_BYTES + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
-            if constexpr (F32) {
-              *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-              *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]));
+              for (int q = 0; q < 4; ++q) v[q] = deq(i, j, q, acc[i][j][q]);
+              const int byte = (16 * j + 4 * g) * ES;
+              uint8_t* dst = wl + r * ROW_BYTES + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
+              if constexpr (F32) {
+                *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+              } else if constexpr (SOFT) {
+                *reinterpret_cast<uint2*>(dst) =
+                    make_uint2((uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
+                               (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16));
+              } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sub |= __builtin_isfpclass(v[q], 0x90);
+                *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2_hw(v[0], v[1]), bf16x2_hw(v[2], v[3]));
+              }
             }
-          }
+            return sub;
+          };
+          const bool sub = put(std::false_type{});
+          if constexpr (!F32)
+            if (__builtin_expect(__any(sub), 0)) put(std::true_type{});
         }
         // read back whole rows (same wavefront: LDS operations stay in order)
         const int q = lane % LANES_ROW, rr = lane / LANES_ROW;
