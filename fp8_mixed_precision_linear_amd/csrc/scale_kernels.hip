@@ -37,29 +37,32 @@ __device__ __forceinline__ void block_max_to(float* out, uint32_t v) {
 }
 
 // max |x| over n bf16 values: 16-byte loads (8 values) on a grid-stride
-// loop, two loads in flight per thread, packed 16-bit max, then a
-// wavefront / block reduction and one atomic per block.
+// loop with up to kAmaxUnroll loads in flight per thread (issued together,
+// then reduced), packed 16-bit max, then a wavefront / block reduction and one
+// atomic per block.  With 2 loads per round trip the 4096 x 4096 case took
+// four dependent trips through memory; with 8 a grid of one workgroup per
+// CU covers it in one.
+constexpr int kAmaxUnroll = 8;
 __global__ void __launch_bounds__(kAmaxThreads) k_amax(const uint16_t* __restrict__ x, int64_t n,
                                                        float* __restrict__ amax) {
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   const int64_t nv = n >> 3;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  uint32_t m0 = 0, m1 = 0;
-  for (; i + stride < nv; i += 2 * stride) {
-    uint4 a = ld_nt16(xv + i);
-    uint4 b = ld_nt16(xv + i + stride);
-    m0 = absmax_pk(m0, a.x); m0 = absmax_pk(m0, a.y);
-    m0 = absmax_pk(m0, a.z); m0 = absmax_pk(m0, a.w);
-    m1 = absmax_pk(m1, b.x); m1 = absmax_pk(m1, b.y);
-    m1 = absmax_pk(m1, b.z); m1 = absmax_pk(m1, b.w);
+  uint32_t mu[4] = {0u, 0u, 0u, 0u};
+  for (; i < nv; i += kAmaxUnroll * stride) {
+    uint4 v[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u)
+      v[u] = i + u * stride < nv ? ld_nt16(xv + i + u * stride) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      uint32_t& m = mu[u & 3];
+      m = absmax_pk(m, v[u].x); m = absmax_pk(m, v[u].y);
+      m = absmax_pk(m, v[u].z); m = absmax_pk(m, v[u].w);
+    }
   }
-  if (i < nv) {
-    uint4 a = ld_nt16(xv + i);
-    m0 = absmax_pk(m0, a.x); m0 = absmax_pk(m0, a.y);
-    m0 = absmax_pk(m0, a.z); m0 = absmax_pk(m0, a.w);
-  }
-  uint32_t m = absmax_fold(absmax_pk(m0, m1));
+  uint32_t m = absmax_fold(absmax_pk(absmax_pk(mu[0], mu[1]), absmax_pk(mu[2], mu[3])));
   // tail: the last n % 8 values
   if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
     uint32_t t = (uint32_t)(x[(nv << 3) + threadIdx.x] & 0x7FFFu) << 16;
