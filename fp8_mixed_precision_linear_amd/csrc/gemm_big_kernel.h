@@ -398,6 +398,18 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     if (p.b_scaling == 0) sb = p.b_sinv[0];
   }
   constexpr bool EPI_SCALE = !BLOCK || MX;
+  // Can a dequantised output be a binary32 subnormal?  With per-tensor
+  // scales every nonzero accumulator is a multiple of 2^-(qa+qb), the
+  // product of the two formats' smallest subnormal steps (2^-9 for E4M3,
+  // 2^-16 for E5M2), so at least that in magnitude; rounding is monotone,
+  // so if that minimum, dequantised by the same two products, is a normal
+  // binary32, every nonzero output is.  Other modes always check.
+  bool may_sub = true;
+  if constexpr (!BLOCK && !ROWS) {
+    constexpr int QAB = (AF == 0 ? 9 : 16) + (BF == 0 ? 9 : 16);
+    const float lo = (__builtin_ldexpf(1.0f, -QAB) * __builtin_fabsf(sa)) * __builtin_fabsf(sb);
+    may_sub = !(lo >= 1.17549435e-38f);   // NaN scales: check
+  }
   if constexpr (ROWS) __syncthreads();   // the tile's row scales are in rs_tab
   // dequantised value of accumulator entry (i, j, q)
   auto deq = [&](int i, int j, int q, float a) -> float {
@@ -486,39 +498,48 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
         // BF16: the hardware pair conversion, one row-tile at a time; a
         // row-tile in which any lane holds a binary32 subnormal (which that
         // instruction does not round to nearest) is written again with the
-        // integer rounding
+        // integer rounding.  CHK = false: no output can be subnormal, the
+        // per-value check is left out.
+        auto row_tiles = [&](auto chktag) {
+          constexpr bool CHK = decltype(chktag)::value;
 #pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          if ((16 * i) / ROWS_PASS != pass) continue;
-          const int r = 16 * i + l16 - pass * ROWS_PASS;
-          auto put = [&](auto softtag) -> bool {
-            constexpr bool SOFT = decltype(softtag)::value;
-            bool sub = false;
+          for (int i = 0; i < TI; ++i) {
+            if ((16 * i) / ROWS_PASS != pass) continue;
+            const int r = 16 * i + l16 - pass * ROWS_PASS;
+            auto put = [&](auto softtag) -> bool {
+              constexpr bool SOFT = decltype(softtag)::value;
+              bool sub = false;
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) {
-              float v[4];
+              for (int j = 0; j < TJ; ++j) {
+                float v[4];
 #pragma unroll
-              for (int q = 0; q < 4; ++q) v[q] = deq(i, j, q, acc[i][j][q]);
-              const int byte = (16 * j + 4 * g) * ES;
-              uint8_t* dst = wl + r * ROW_BYTES + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
-              if constexpr (F32) {
-                *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-              } else if constexpr (SOFT) {
-                *reinterpret_cast<uint2*>(dst) =
-                    make_uint2((uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
-                               (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16));
-              } else {
+                for (int q = 0; q < 4; ++q) v[q] = deq(i, j, q, acc[i][j][q]);
+                const int byte = (16 * j + 4 * g) * ES;
+                uint8_t* dst = wl + r * ROW_BYTES + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
+                if constexpr (F32) {
+                  *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                } else if constexpr (SOFT) {
+                  *reinterpret_cast<uint2*>(dst) = make_uint2(
+                      (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
+                      (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16));
+                } else {
+                  if constexpr (CHK) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) sub |= __builtin_isfpclass(v[q], 0x90);
-                *reinterpret_cast<uint2*>(dst) = make_uint2(bf16x2_hw(v[0], v[1]), bf16x2_hw(v[2], v[3]));
+                    for (int q = 0; q < 4; ++q) sub |= __builtin_isfpclass(v[q], 0x90);
+                  }
+                  *reinterpret_cast<uint2*>(dst) =
+                      make_uint2(bf16x2_hw(v[0], v[1]), bf16x2_hw(v[2], v[3]));
+                }
               }
-            }
-            return sub;
-          };
-          const bool sub = put(std::false_type{});
-          if constexpr (!F32)
-            if (__builtin_expect(__any(sub), 0)) put(std::true_type{});
-        }
+              return sub;
+            };
+            const bool sub = put(std::false_type{});
+            if constexpr (!F32 && CHK)
+              if (__builtin_expect(__any(sub), 0)) put(std::true_type{});
+          }
+        };
+        if (F32 || !may_sub) row_tiles(std::false_type{});
+        else row_tiles(std::true_type{});
         // read back whole rows (same wavefront: LDS operations stay in order)
         const int q = lane % LANES_ROW, rr = lane / LANES_ROW;
 #pragma unroll 4

@@ -261,6 +261,43 @@ def test_gemm_bf16_output_in_f32_subnormal_range(O, L, shape):
     assert bits(am) == bits(amax_of_output(raw, False))
 
 
+@pytest.mark.parametrize("fmts", [(0, 0), (1, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("below", [False, True])
+def test_gemm_bf16_output_at_the_normal_boundary(O, L, fmts, below):
+    """Operands of FP8 subnormal codes only, so every accumulator is a small
+    multiple of the product of the formats' smallest steps, 2^-(qa+qb)
+    (q = 9 for E4M3, 16 for E5M2), and the sums are exact.  Per-tensor
+    scales put that smallest step at exactly 2^-126 after dequantisation
+    (every output normal), or one binade lower (below=True: outputs of one
+    step are binary32 subnormals).  The BF16 bits must equal the oracle's
+    F rounded to nearest even on both sides of the boundary."""
+    af, bf = fmts
+    M, N, K = 256, 512, 256
+    say("gemm bf16 normal boundary", fmts, below)
+    rng = np.random.default_rng(7 + 2 * af + bf + 4 * below)
+    # subnormal codes 1..3 (E4M3) or 1 (E5M2) with random signs, 3 in 4 zero
+    def sub_codes(shape, fmt):
+        top = 3 if fmt == 0 else 1
+        c = rng.integers(1, top + 1, shape).astype(np.uint8)
+        c[rng.random(shape) < 0.75] = 0
+        return c | (rng.integers(0, 2, shape).astype(np.uint8) << 7)
+    A, B = sub_codes((M, K), af), sub_codes((N, K), bf)
+    qab = (9 if af == 0 else 16) + (9 if bf == 0 else 16)
+    ea = (126 - qab) // 2
+    eb = 126 - qab - ea + (1 if below else 0)
+    sa, sb = np.array([2.0 ** -ea], np.float32), np.array([2.0 ** -eb], np.float32)
+    G, raw, am = run_gemm(L, A, af, 0, sa, B, bf, 0, sb, False)
+    F = O.gemm(A, af, 0, sa, B, bf, 0, sb, want=("F",))["F"]
+    nz = np.abs(F[F != 0])
+    assert nz.size > F.size // 4
+    if below:
+        assert np.any(nz < 2.0 ** -126)       # subnormal outputs present
+    else:
+        assert nz.min() == 2.0 ** -126        # the smallest step lands on the boundary
+    assert np.array_equal(raw, O.f32_to_bf16(F).reshape(F.shape))
+    assert bits(am) == bits(amax_of_output(raw, False))
+
+
 @pytest.mark.parametrize("mode", [(0, 0), (1, 2), (3, 4), (5, 5)])
 @pytest.mark.parametrize("out", ["bf16", "f32", "e4m3"])
 def test_gemm_leading_dimensions(L, mode, out):
