@@ -37,6 +37,13 @@ __device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t 
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
+// Halfwise unsigned 16-bit maximum of two packed pairs.
+__device__ __forceinline__ uint32_t pk_umax(uint32_t a, uint32_t b) {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(us2, a),
+                                                                __builtin_bit_cast(us2, b)));
+}
+
 // Binary32 pattern of max |x| over the two bf16 halves of a dword.
 __device__ __forceinline__ uint32_t absmax2(uint32_t w) {
   uint32_t lo = (w & 0x7FFFu) << 16, hi = (w & 0x7FFF0000u);
@@ -179,31 +186,32 @@ __global__ void __launch_bounds__(kThreads)
     }
     // ---- 1x128 along columns (token axis) for the transposed copy
     if constexpr (WANT_T) {
-      uint32_t cm[16];
+      // column maxima as packed 16-bit pairs: dword j holds |x| of columns
+      // 2j (low half) and 2j+1 (high half); bf16 magnitudes order like
+      // their bit patterns, so one packed max per row and dword
+      uint32_t cp[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        uint32_t lo = 0, hi = 0;
+        uint32_t m = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t d = (&v[i][0].x)[j];  // dword j of the 16 columns
-          lo = umax(lo, (d & 0x7FFFu) << 16);
-          hi = umax(hi, d & 0x7FFF0000u);
-        }
-        cm[2 * j] = lo;
-        cm[2 * j + 1] = hi;
+        for (int i = 0; i < 4; ++i) m = absmax_pk(m, (&v[i][0].x)[j]);
+        cp[j] = m;
       }
       // across the 8 row groups of this wavefront (lanes with equal cg)
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        uint32_t mb = cm[k];
-        mb = umax(mb, __shfl_xor(mb, 8, 64));
-        mb = umax(mb, __shfl_xor(mb, 16, 64));
-        mb = umax(mb, __shfl_xor(mb, 32, 64));
-        cm[k] = mb;
+      for (int j = 0; j < 8; ++j) {
+        uint32_t m = cp[j];
+        m = pk_umax(m, __shfl_xor(m, 8, 64));
+        m = pk_umax(m, __shfl_xor(m, 16, 64));
+        m = pk_umax(m, __shfl_xor(m, 32, 64));
+        cp[j] = m;
       }
-      if (lane < 8) {
+      if (lane < 8) {   // unpacked: binary32 patterns of the bf16 maxima
 #pragma unroll
-        for (int k = 0; k < 16; ++k) red[wave][16 * cg + k] = cm[k];
+        for (int j = 0; j < 8; ++j) {
+          red[wave][16 * cg + 2 * j] = (cp[j] & 0xFFFFu) << 16;
+          red[wave][16 * cg + 2 * j + 1] = cp[j] & 0xFFFF0000u;
+        }
       }
       __syncthreads();
       if (t < 128) {
