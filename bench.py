@@ -9,7 +9,11 @@ resident in HBM before timing.  One step = the whole hot path:
   dX), WGRAD GEMM (fp32 dW), amax-history update (len 16, max) for X, W, dY.
 `value` = GEMM FLOPs of the step (3 x 2*4096^3) / measured step time, with
 the K timed steps captured once into a HIP graph and replayed (the eager
-per-call time is reported beside it as ms_per_step_eager).
+per-call time is reported beside it as ms_per_step_eager).  The casts
+max-accumulate their amax into slots that the history update clears after
+reading them (fp8_cast_amax_acc, fp8_amax_history_update_reset); the same
+step with overwriting casts, each zeroing its slot with a fill kernel
+first, is reported as ms_per_step_overwrite_casts.
 
 Also reported (same JSON line):
   roofline      -- the dominant kernel (the GEMMs), per-launch duration from
@@ -105,7 +109,24 @@ def main():
     sinv = torch.ones(3, dtype=torch.float32, device=dev)
     amax = torch.zeros(3, dtype=torch.float32, device=dev)
 
+    # The casts max-accumulate their amax into the slots that the history
+    # update reads and then clears (amax starts at 0), so a step needs no
+    # zeroing kernel: 3 casts, 3 GEMMs, 2 history updates.
     def step(t):
+        x, w, dyt = data[t % NSTEPS_DATA]
+        L.fp8_cast_amax_acc(x, 0, scale[0:1], amax[0:1], y=xq, y_t=xtq)
+        L.fp8_cast_amax_acc(w, 0, scale[1:2], amax[1:2], y=wq, y_t=wtq)
+        L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y)
+        L.fp8_cast_amax_acc(dyt, 1, scale[2:3], amax[2:3], y=dyq, y_t=dytq)
+        L.fp8_scaled_gemm(dyq, 1, 0, sinv[2:3], wq, 0, 0, sinv[1:2], dx)
+        L.fp8_scaled_gemm(xtq, 0, 0, sinv[0:1], dytq, 1, 0, sinv[2:3], dw)
+        L.fp8_amax_history_update_reset(hist[0:2], amax[0:2], 0, 0, 0, scale[0:2], sinv[0:2])
+        L.fp8_amax_history_update_reset(hist[2:3], amax[2:3], 1, 0, 0, scale[2:3], sinv[2:3])
+
+    # the same step with overwriting casts (each zeroes its amax slot with a
+    # fill kernel first) and the plain history update, for comparison; timed
+    # after the accumulating step's graph (it leaves the slots nonzero)
+    def step_overwrite(t):
         x, w, dyt = data[t % NSTEPS_DATA]
         L.fp8_cast_e4m3(x, scale[0:1], y=xq, y_t=xtq, amax_out=amax[0:1])
         L.fp8_cast_e4m3(w, scale[1:2], y=wq, y_t=wtq, amax_out=amax[1:2])
@@ -132,6 +153,7 @@ def main():
     # graph: the same K steps captured once into a HIP graph and replayed
     # (no host launch cost; the GPU runs the identical kernel sequence)
     ms_step_graph = None
+    ms_step_overwrite = None
     wall = None
     if not args.no_graph:
         g = capture(torch, lambda: [step(args.warmup + t) for t in range(args.steps)])
@@ -144,6 +166,15 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         ms_step_graph = ev0.elapsed_time(ev1) / args.steps
+        del g
+        g = capture(torch, lambda: [step_overwrite(args.warmup + t) for t in range(args.steps)])
+        g.replay()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_step_overwrite = ev0.elapsed_time(ev1) / args.steps
         del g
     ms_step = ms_step_graph if ms_step_graph is not None else ms_step_eager
     gemm_flops = 3 * 2.0 * T * DI * DO
@@ -177,6 +208,7 @@ def main():
         lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y8, d_amax=am8,
                                   d_scale=scale[0:1], d_fmt=0, D_t=y8t), R)
     k["cast_transpose_amax_e4m3"] = time_launch(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq, y_t=xtq, amax_out=amax[0:1]), R)
+    k["cast_transpose_amax_acc_e4m3"] = time_launch(lambda: L.fp8_cast_amax_acc(x0, 0, scale[0:1], amax[0:1], y=xq, y_t=xtq), R)
     k["cast_transpose_amax_e5m2"] = time_launch(lambda: L.fp8_cast_e5m2(dy0, scale[2:3], y=dyq, y_t=dytq, amax_out=amax[2:3]), R)
     k["cast_transpose_amax_e5m2_sr"] = time_launch(
         lambda: L.fp8_cast_sr(dy0, 1, scale[2:3], 1234, 0, y=dyq, y_t=dytq, amax_out=amax[2:3]), R)
@@ -194,6 +226,8 @@ def main():
                                    "us": k["gemm_fwd_tensor_fp8out"] * 1e6,
                                    "us_unfused_equivalent": (k["gemm_fwd_tensor"] + k["cast_transpose_amax_e4m3"]) * 1e6},
         "cast_transpose_amax_e4m3": {"gbs": 4.0 * nel / k["cast_transpose_amax_e4m3"] / 1e9, "us": k["cast_transpose_amax_e4m3"] * 1e6},
+        "cast_transpose_amax_acc_e4m3": {"gbs": 4.0 * nel / k["cast_transpose_amax_acc_e4m3"] / 1e9,
+                                         "us": k["cast_transpose_amax_acc_e4m3"] * 1e6},
         "cast_transpose_amax_e5m2": {"gbs": 4.0 * nel / k["cast_transpose_amax_e5m2"] / 1e9, "us": k["cast_transpose_amax_e5m2"] * 1e6},
         "cast_transpose_amax_e5m2_sr": {"gbs": 4.0 * nel / k["cast_transpose_amax_e5m2_sr"] / 1e9,
                                         "us": k["cast_transpose_amax_e5m2_sr"] * 1e6},
@@ -235,6 +269,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
         "launch": "hip_graph" if ms_step_graph is not None else "eager",
         "ms_per_step_eager": round(ms_step_eager, 4),
+        "ms_per_step_overwrite_casts": (round(ms_step_overwrite, 4)
+                                        if ms_step_overwrite is not None else None),
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3/e5m2 (fp32 accumulate)",
         "data": "synthetic (seeded numpy PCG64, bf16)",
         "config": {"workload": "delayed-scaling FP8 linear fwd+dgrad+wgrad, tokens 4096, in 4096, "

@@ -20,7 +20,7 @@ inline fp8_status launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8
 
 fp8_status cast_common(const void* x, int64_t rows, int64_t cols, const float* scale, uint8_t* y,
                        uint8_t* y_t, float* amax_out, int fmt, int sr, uint64_t seed,
-                       uint64_t offset, hipStream_t stream) {
+                       uint64_t offset, hipStream_t stream, int amax_acc = 0) {
   if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
   const bool empty = rows == 0 || cols == 0;
   if (!empty && (x == nullptr || scale == nullptr || (y == nullptr && y_t == nullptr)))
@@ -28,7 +28,7 @@ fp8_status cast_common(const void* x, int64_t rows, int64_t cols, const float* s
   if (!aligned16(x) || !aligned16(y) || !aligned16(y_t)) return FP8_ERR_ALIGN;
   if (amax_out && !aligned4(amax_out)) return FP8_ERR_ALIGN;
   return launched(launch_cast(static_cast<const uint16_t*>(x), rows, cols, scale, fmt, y, y_t,
-                              amax_out, sr, seed, offset, stream));
+                              amax_out, amax_acc, sr, seed, offset, stream));
 }
 
 }  // namespace
@@ -76,7 +76,7 @@ fp8_status compute_scale_common(const float* amax, int64_t n, fp8_format fmt, in
 
 fp8_status history_common(float* history, int64_t n, int64_t len, const float* amax_new,
                           fp8_format fmt, int margin, fp8_amax_algo algo, int pow2, float* scale,
-                          float* scale_inv, hipStream_t stream) {
+                          float* scale_inv, hipStream_t stream, int reset = 0) {
   if (n < 0 || len < 1 || len > 1024) return FP8_ERR_SHAPE;
   if (!fmt_ok(fmt) || margin < 0 || margin > 64) return FP8_ERR_ARG;
   if (algo != FP8_AMAX_MAX && algo != FP8_AMAX_MOST_RECENT) return FP8_ERR_ARG;
@@ -85,8 +85,10 @@ fp8_status history_common(float* history, int64_t n, int64_t len, const float* a
     return FP8_ERR_NULL;
   if (!aligned4(history) || !aligned4(amax_new) || !aligned4(scale) || !aligned4(scale_inv))
     return FP8_ERR_ALIGN;
-  return launched(launch_history_update(history, n, len, amax_new, fmt, margin, algo, pow2, scale,
-                                        scale_inv, stream));
+  // amax_new is written only when reset (the entry point that resets takes
+  // it as a mutable pointer)
+  return launched(launch_history_update(history, n, len, const_cast<float*>(amax_new), fmt, margin,
+                                        algo, pow2, reset, scale, scale_inv, stream));
 }
 
 fp8_status cast_block_common(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
@@ -131,6 +133,21 @@ fp8_status fp8_amax_history_update_pow2(float* history, int64_t n, int64_t len,
                                         fp8_amax_algo algo, float* scale, float* scale_inv,
                                         hipStream_t stream) {
   return history_common(history, n, len, amax_new, fmt, margin, algo, 1, scale, scale_inv, stream);
+}
+
+fp8_status fp8_amax_history_update_reset(float* history, int64_t n, int64_t len, float* amax_new,
+                                         fp8_format fmt, int margin, fp8_amax_algo algo,
+                                         float* scale, float* scale_inv, hipStream_t stream) {
+  return history_common(history, n, len, amax_new, fmt, margin, algo, 0, scale, scale_inv, stream,
+                        1);
+}
+
+fp8_status fp8_cast_amax_acc(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                             const float* scale, uint8_t* y, uint8_t* y_t, float* amax_acc,
+                             hipStream_t stream) {
+  if (!fmt_ok(fmt)) return FP8_ERR_ARG;
+  if (amax_acc == nullptr) return FP8_ERR_NULL;
+  return cast_common(x_bf16, rows, cols, scale, y, y_t, amax_acc, fmt, 0, 0, 0, stream, 1);
 }
 
 fp8_status fp8_cast_e4m3(const void* x_bf16, int64_t rows, int64_t cols, const float* scale,

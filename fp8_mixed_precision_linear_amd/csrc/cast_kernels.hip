@@ -270,9 +270,9 @@ hipError_t launch_cast_t(const uint16_t* x, int64_t rows, int64_t cols, const fl
 }  // namespace
 
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, const float* scale, int fmt,
-                       uint8_t* y, uint8_t* y_t, float* amax, int sr, uint64_t seed,
+                       uint8_t* y, uint8_t* y_t, float* amax, int amax_acc, int sr, uint64_t seed,
                        uint64_t offset, hipStream_t s) {
-  if (amax) {
+  if (amax && !amax_acc) {
     hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 1, 0u, s);
     if (e != hipSuccess) return e;
   }

@@ -24,8 +24,9 @@ hipError_t launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64
 hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, int margin, int pow2,
                                 float* scale, float* scale_inv, hipStream_t s);
 
-hipError_t launch_history_update(float* history, int64_t n, int64_t len, const float* amax_new,
-                                 int fmt, int margin, int algo, int pow2, float* scale,
+// reset != 0: amax_new[i] is set to 0 once consumed.
+hipError_t launch_history_update(float* history, int64_t n, int64_t len, float* amax_new,
+                                 int fmt, int margin, int algo, int pow2, int reset, float* scale,
                                  float* scale_inv, hipStream_t s);
 
 // Exponentially weighted amax and its scale, n tensors.
@@ -33,9 +34,10 @@ hipError_t launch_ewma_update(float* ewma, int64_t n, const float* amax_new, flo
                               int margin, float* scale, float* scale_inv, hipStream_t s);
 
 // Per-tensor cast with optional transpose and amax (zeroed here first when
-// given); sr != 0: stochastic rounding with Philox words from (seed, offset).
+// given, unless amax_acc: then max-accumulated into its current value);
+// sr != 0: stochastic rounding with Philox words from (seed, offset).
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, const float* scale, int fmt,
-                       uint8_t* y, uint8_t* y_t, float* amax, int sr, uint64_t seed,
+                       uint8_t* y, uint8_t* y_t, float* amax, int amax_acc, int sr, uint64_t seed,
                        uint64_t offset, hipStream_t s);
 
 // Block-wise cast (tile: 1 = 1x128, 2 = 128x128; pow2: power-of-two scales).

@@ -123,11 +123,15 @@ __global__ void k_ewma_update(float* __restrict__ ewma, int64_t n, const float* 
 // store instruction consumes the value of the one load instruction, so all
 // lanes have read their source entries before any lane writes; the next
 // (lower) chunk reads only entries below the ones already written.
+//
+// reset != 0: the consumed amax_new[i] is set to 0 afterwards (by lane 0,
+// after every lane's read of it has returned: the value feeds the
+// wavefront's reduction before the store is issued), ready for the next
+// step's casts to max-accumulate into.
 __global__ void __launch_bounds__(64) k_history_update(float* __restrict__ history, int64_t n,
-                                                       int64_t len,
-                                                       const float* __restrict__ amax_new,
+                                                       int64_t len, float* amax_new,
                                                        float fmax, int margin, int algo, int pow2,
-                                                       float* __restrict__ scale,
+                                                       int reset, float* __restrict__ scale,
                                                        float* __restrict__ scale_inv) {
   const int64_t i = blockIdx.x;
   const int lane = threadIdx.x;
@@ -156,6 +160,7 @@ __global__ void __launch_bounds__(64) k_history_update(float* __restrict__ histo
       scale[i] = s;
       scale_inv[i] = si;
     }
+    if (reset) amax_new[i] = 0.0f;
   }
 }
 
@@ -250,13 +255,13 @@ hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, int margi
   return hipGetLastError();
 }
 
-hipError_t launch_history_update(float* history, int64_t n, int64_t len, const float* amax_new,
-                                 int fmt, int margin, int algo, int pow2, float* scale,
+hipError_t launch_history_update(float* history, int64_t n, int64_t len, float* amax_new,
+                                 int fmt, int margin, int algo, int pow2, int reset, float* scale,
                                  float* scale_inv, hipStream_t s) {
   if (n == 0) return hipSuccess;
   if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_history_update, dim3((unsigned)n), dim3(64), 0, s, history, n, len,
-                     amax_new, fmax_of(fmt), margin, algo, pow2, scale, scale_inv);
+                     amax_new, fmax_of(fmt), margin, algo, pow2, reset, scale, scale_inv);
   return hipGetLastError();
 }
 

@@ -59,6 +59,8 @@ def _load():
         "fp8_compute_scale_pow2": (i32, [vp, i64, i32, i32, vp, vp, vp]),
         "fp8_amax_history_update": (i32, [vp, i64, i64, vp, i32, i32, i32, vp, vp, vp]),
         "fp8_amax_history_update_pow2": (i32, [vp, i64, i64, vp, i32, i32, i32, vp, vp, vp]),
+        "fp8_amax_history_update_reset": (i32, [vp, i64, i64, vp, i32, i32, i32, vp, vp, vp]),
+        "fp8_cast_amax_acc": (i32, [vp, i64, i64, i32, vp, vp, vp, vp, vp]),
         "fp8_cast_e4m3": (i32, [vp, i64, i64, vp, vp, vp, vp, vp]),
         "fp8_cast_e5m2": (i32, [vp, i64, i64, vp, vp, vp, vp, vp]),
         "fp8_cast_block": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
@@ -187,6 +189,25 @@ def fp8_amax_history_update_pow2(history, amax_new, fmt, margin, algo, scale, sc
                                  stream=None):
     _history(_L.fp8_amax_history_update_pow2, history, amax_new, fmt, margin, algo, scale,
              scale_inv, stream)
+
+
+def fp8_amax_history_update_reset(history, amax_new, fmt, margin, algo, scale, scale_inv,
+                                  stream=None):
+    """fp8_amax_history_update, then amax_new is set to 0 (the slots the next
+    step's fp8_cast_amax_acc calls accumulate into)."""
+    _history(_L.fp8_amax_history_update_reset, history, amax_new, fmt, margin, algo, scale,
+             scale_inv, stream)
+
+
+def fp8_cast_amax_acc(x, fmt, scale, amax_acc, y=None, y_t=None, stream=None):
+    """Per-tensor cast with the amax of x max-accumulated into amax_acc."""
+    if amax_acc is None:
+        raise ValueError("amax_acc is required")
+    rows, cols = _cast_sizes(x, scale, y, y_t, amax_acc)
+    _check("fp8_cast_amax_acc",
+           _L.fp8_cast_amax_acc(_ptr(x, _BF16, "x"), rows, cols, fmt, _ptr(scale, _F32, "scale"),
+                                _ptr(y, _U8, "y"), _ptr(y_t, _U8, "y_t"),
+                                _ptr(amax_acc, _F32, "amax_acc"), _stream(stream)))
 
 
 def _cast_sizes(x, scale, y, y_t, amax_out):

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 5
+#define FP8LIN_ABI_VERSION 6
 
 /* [MPG] "The precision formats", "FP8 E4M3", "FP8 E5M2": E4M3 = 4 exponent
  * and 3 mantissa bits, range about 2^-9..448; E5M2 = 5 and 2, range about
@@ -173,6 +173,21 @@ fp8_status fp8_amax_history_update_pow2(float* history, int64_t n, int64_t len,
                                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fp8_amax_history_update_reset -- fp8_amax_history_update, after which
+ * every consumed amax_new[i] is set to 0.
+ * [MPG] "Delayed scaling (the default recipe)": the amax observed at step t
+ * enters the history that sets the scale of step t+1.  With the slots
+ * cleared here, the casts of the next step accumulate into them with
+ * fp8_cast_amax_acc and no separate zeroing is needed between steps: one
+ * step is then casts -> GEMMs -> this update, with amax_new starting at 0.
+ *   amax_new   [n] floats (device), read, then overwritten with 0.
+ *   Other arguments, order and errors as fp8_amax_history_update.
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_amax_history_update_reset(float* history, int64_t n, int64_t len, float* amax_new,
+                                         fp8_format fmt, int margin, fp8_amax_algo algo,
+                                         float* scale, float* scale_inv, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fp8_amax_ewma_update -- delayed scaling from an exponentially weighted
  * amax.  [MPG] "Delayed scaling (the default recipe)": the scale used at
  * step t is the one right for step t-1, or an exponentially weighted
@@ -211,6 +226,26 @@ fp8_status fp8_cast_e4m3(const void* x_bf16, int64_t rows, int64_t cols, const f
                          uint8_t* y, uint8_t* y_t, float* amax_out, hipStream_t stream);
 fp8_status fp8_cast_e5m2(const void* x_bf16, int64_t rows, int64_t cols, const float* scale,
                          uint8_t* y, uint8_t* y_t, float* amax_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_cast_amax_acc -- the per-tensor cast of fp8_cast_e4m3 / e5m2 with the
+ * fused amax max-accumulated into *amax_acc instead of overwriting it.
+ * [MPG] "Per-tensor scaling" (the cast), "Delayed scaling (the default
+ * recipe)" (the amax of the step feeds the next step's scale): with the
+ * slot cleared by fp8_amax_history_update_reset, a delayed-scaling step
+ * needs no zeroing kernel before its casts.
+ *   fmt        FP8_E4M3 or FP8_E5M2.
+ *   amax_acc   1 float (device), required: on return
+ *              max(previous value, max |x|), compared as binary32 bit
+ *              patterns, so the previous value must be +0 or positive
+ *              (NaN in x propagates as in fp8_amax).
+ *   Other arguments, layouts and errors as fp8_cast_e4m3, plus FP8_ERR_ARG
+ *   (fmt) and FP8_ERR_NULL (amax_acc).  Calls that accumulate into one slot
+ *   may run concurrently on several streams.
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_cast_amax_acc(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                             const float* scale, uint8_t* y, uint8_t* y_t, float* amax_acc,
+                             hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * fp8_cast_sr -- per-tensor cast with stochastic rounding.

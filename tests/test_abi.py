@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.abi_version() == 5
+    assert L.abi_version() == 6
     for s in range(7):
         assert isinstance(L.status_string(s), str) and L.status_string(s)
     assert L.status_string(99) == "unknown status"
@@ -91,6 +91,17 @@ def test_host_validation_before_launch(L):
     assert f.fp8_cast_sr(x, 4, 4, 0, s, 1, 0, None, None, None, None) == 1
     assert f.fp8_cast_sr(x, 4, 4, 1, s, 1, 0, C.c_void_p(0x2004), None, None, None) == 3
     assert f.fp8_cast_sr(x, -4, 4, 1, s, 1, 0, y, None, None, None) == 2
+    a = C.c_void_p(0x5000)
+    # accumulating cast: bad format, missing amax slot or outputs, misaligned slot
+    assert f.fp8_cast_amax_acc(x, 4, 4, 2, s, y, None, a, None) == 6
+    assert f.fp8_cast_amax_acc(x, 4, 4, 0, s, y, None, None, None) == 1
+    assert f.fp8_cast_amax_acc(x, 4, 4, 1, s, None, None, a, None) == 1
+    assert f.fp8_cast_amax_acc(x, 4, 4, 0, s, y, None, C.c_void_p(0x5002), None) == 3
+    assert f.fp8_cast_amax_acc(x, -4, 4, 0, s, y, None, a, None) == 2
+    # resetting history update: as the plain update
+    assert f.fp8_amax_history_update_reset(None, 1, 0, None, 0, 0, 0, None, None, None) == 2
+    assert f.fp8_amax_history_update_reset(None, 1, 16, None, 0, 0, 5, None, None, None) == 6
+    assert f.fp8_amax_history_update_reset(None, 1, 16, None, 0, 0, 0, None, None, None) == 1
     # EWMA update: beta outside [0, 1] or NaN, margin, sizes, pointers
     e, a = C.c_void_p(0x4000), C.c_void_p(0x5000)
     assert f.fp8_amax_ewma_update(e, 1, a, 1.5, 0, 0, s, s, None) == 6

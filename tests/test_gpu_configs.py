@@ -103,8 +103,11 @@ def test_config1_current_scaling_forward(O, L):
 class DelayedRun:
     """The measured delayed-scaling step, run step by step on the GPU."""
 
-    def __init__(self, L, T=4096, DI=4096, DO=4096):
+    def __init__(self, L, T=4096, DI=4096, DO=4096, fused=False):
         self.L = L
+        # fused: casts accumulate into the amax slots that the resetting
+        # history update clears (no zeroing kernel before the casts)
+        self.fused = fused
         self.xq, self.xtq = u8((T, DI)), u8((DI, T))
         self.wq, self.wtq = u8((DI, DO)), u8((DO, DI))
         self.dyq, self.dytq = u8((T, DO)), u8((DO, T))
@@ -117,6 +120,8 @@ class DelayedRun:
         self.amax = torch.zeros(3, dtype=torch.float32, device="cuda")
 
     def step(self, x, w, dy):
+        if self.fused:
+            return self.step_fused(x, w, dy)
         L, s, si = self.L, self.scale, self.sinv
         L.fp8_cast_e4m3(x, s[0:1], y=self.xq, y_t=self.xtq, amax_out=self.amax[0:1])
         L.fp8_cast_e4m3(w, s[1:2], y=self.wq, y_t=self.wtq, amax_out=self.amax[1:2])
@@ -126,6 +131,17 @@ class DelayedRun:
         L.fp8_scaled_gemm(self.xtq, 0, 0, si[0:1], self.dytq, 1, 0, si[2:3], self.dw)
         L.fp8_amax_history_update(self.hist[0:2], self.amax[0:2], 0, 0, 0, s[0:2], si[0:2])
         L.fp8_amax_history_update(self.hist[2:3], self.amax[2:3], 1, 0, 0, s[2:3], si[2:3])
+
+    def step_fused(self, x, w, dy):
+        L, s, si, am = self.L, self.scale, self.sinv, self.amax
+        L.fp8_cast_amax_acc(x, 0, s[0:1], am[0:1], y=self.xq, y_t=self.xtq)
+        L.fp8_cast_amax_acc(w, 0, s[1:2], am[1:2], y=self.wq, y_t=self.wtq)
+        L.fp8_scaled_gemm(self.xq, 0, 0, si[0:1], self.wtq, 0, 0, si[1:2], self.y)
+        L.fp8_cast_amax_acc(dy, 1, s[2:3], am[2:3], y=self.dyq, y_t=self.dytq)
+        L.fp8_scaled_gemm(self.dyq, 1, 0, si[2:3], self.wq, 0, 0, si[1:2], self.dx)
+        L.fp8_scaled_gemm(self.xtq, 0, 0, si[0:1], self.dytq, 1, 0, si[2:3], self.dw)
+        L.fp8_amax_history_update_reset(self.hist[0:2], am[0:2], 0, 0, 0, s[0:2], si[0:2])
+        L.fp8_amax_history_update_reset(self.hist[2:3], am[2:3], 1, 0, 0, s[2:3], si[2:3])
 
     def state(self):
         return (self.hist.cpu().numpy().copy(), self.scale.cpu().numpy().copy(),
@@ -141,8 +157,9 @@ def c2_data():
     return out
 
 
-def test_config2_delayed_16_steps(O, L, c2_data):
-    run = DelayedRun(L)
+@pytest.mark.parametrize("fused", [False, True])
+def test_config2_delayed_16_steps(O, L, c2_data, fused):
+    run = DelayedRun(L, fused=fused)
     h = np.zeros((3, 16), np.float32)
     s = np.ones(3, np.float32)
     si = np.ones(3, np.float32)
@@ -155,7 +172,10 @@ def test_config2_delayed_16_steps(O, L, c2_data):
         torch.cuda.synchronize()
         am = np.array([O.amax_parallel(d["x"]), O.amax_parallel(d["w"]), O.amax_parallel(d["dy"])],
                       np.float32)
-        assert np.array_equal(bits(run.amax.cpu().numpy()), bits(am)), t
+        if fused:   # consumed: the amaxes are in the history's newest entries
+            assert np.all(bits(run.amax.cpu().numpy()) == 0), t
+        else:
+            assert np.array_equal(bits(run.amax.cpu().numpy()), bits(am)), t
         for i, f in enumerate(fmts):
             hh, ss, sii = h[i:i + 1].copy(), s[i:i + 1].copy(), si[i:i + 1].copy()
             O.history_update(hh, am[i:i + 1], f, 0, 0, ss, sii)

@@ -32,7 +32,8 @@ def _capture(fn):
     return g
 
 
-def test_delayed_step_graph_replay(L):
+@pytest.mark.parametrize("fused", [False, True])
+def test_delayed_step_graph_replay(L, fused):
     T, DI, DO = 512, 384, 640
     steps = []
     for t in range(2):
@@ -55,6 +56,19 @@ def test_delayed_step_graph_replay(L):
 
     def step(t):
         x, w, dy = steps[t]
+        if fused:   # accumulating casts, resetting history updates
+            am = o["amax"]
+            L.fp8_cast_amax_acc(x, 0, o["scale"][0:1], am[0:1], y=o["xq"], y_t=o["xtq"])
+            L.fp8_cast_amax_acc(w, 0, o["scale"][1:2], am[1:2], y=o["wq"], y_t=o["wtq"])
+            L.fp8_scaled_gemm(o["xq"], 0, 0, o["sinv"][0:1], o["wtq"], 0, 0, o["sinv"][1:2], o["y"])
+            L.fp8_cast_amax_acc(dy, 1, o["scale"][2:3], am[2:3], y=o["dyq"], y_t=o["dytq"])
+            L.fp8_scaled_gemm(o["dyq"], 1, 0, o["sinv"][2:3], o["wq"], 0, 0, o["sinv"][1:2], o["dx"])
+            L.fp8_scaled_gemm(o["xtq"], 0, 0, o["sinv"][0:1], o["dytq"], 1, 0, o["sinv"][2:3], o["dw"])
+            L.fp8_amax_history_update_reset(o["hist"][0:2], am[0:2], 0, 0, 0, o["scale"][0:2],
+                                            o["sinv"][0:2])
+            L.fp8_amax_history_update_reset(o["hist"][2:3], am[2:3], 1, 0, 0, o["scale"][2:3],
+                                            o["sinv"][2:3])
+            return
         L.fp8_cast_e4m3(x, o["scale"][0:1], y=o["xq"], y_t=o["xtq"], amax_out=o["amax"][0:1])
         L.fp8_cast_e4m3(w, o["scale"][1:2], y=o["wq"], y_t=o["wtq"], amax_out=o["amax"][1:2])
         L.fp8_scaled_gemm(o["xq"], 0, 0, o["sinv"][0:1], o["wtq"], 0, 0, o["sinv"][1:2], o["y"])
@@ -71,12 +85,16 @@ def test_delayed_step_graph_replay(L):
     # a non-trivial starting state (a history and scales from one eager step)
     step(1)
     torch.cuda.synchronize()
-    state0 = {k: o[k].clone() for k in ("hist", "scale", "sinv")}
+    # (fused: the amax slots are part of the state, cleared by the update)
+    state_keys = ("hist", "scale", "sinv") + (("amax",) if fused else ())
+    state0 = {k: o[k].clone() for k in state_keys}
+    if fused:
+        assert torch.all(state0["amax"] == 0)
 
     def reset():
         for k, v in state0.items():
             o[k].copy_(v)
-        for k in ("xq", "xtq", "wq", "wtq", "dyq", "dytq", "y", "dx", "dw", "amax"):
+        for k in ("xq", "xtq", "wq", "wtq", "dyq", "dytq", "y", "dx", "dw") + (() if fused else ("amax",)):
             o[k].view(torch.uint8).fill_(0x5A)
 
     reset()

@@ -186,3 +186,69 @@ def test_cast_shapes(O, L, shape, fmt):
     assert np.array_equal(yt.np(), want.T)
     assert np.array_equal(yt1.np(), want.T)
     assert bits(am.np())[0] == bits(O.amax(x))
+
+
+# ----------------------------------------- accumulating cast, resetting update ---
+@pytest.mark.parametrize("shape", [(3, 5), (17, 33), (144, 272), (272, 16), (1024, 2048)])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_cast_amax_acc(O, L, shape, fmt):
+    """fp8_cast_amax_acc writes the codes of fp8_cast_e4m3 / e5m2 (flat,
+    transposed and both, every kernel path) and leaves
+    max(previous slot, amax(x)) in the slot: from 0, from a larger value
+    (unchanged), from a smaller one; two tensors into one slot give the
+    larger of their amaxes."""
+    say("cast amax acc", shape, fmt)
+    rng = np.random.default_rng(shape[0] + 3 * shape[1] + fmt)
+    x = datagen.normal(rng, shape, 1.0 if fmt == 0 else 1e-4)
+    x2 = datagen.normal(rng, shape, 3.0 if fmt == 0 else 3e-4)
+    a1, a2 = O.amax(x), O.amax(x2)
+    s = np.float32(448.0 if fmt == 0 else 57344.0) / a1
+    want = O.cast(x, s, fmt)
+    xd, sd = dev_bf16(x), dev(np.array([s], np.float32))
+    for start in (0.0, float(a1) * 4.0, float(a1) / 4.0):
+        for outs in ("y", "y_t", "both"):
+            y = Guarded(shape, torch.uint8) if outs != "y_t" else None
+            yt = Guarded(shape[::-1], torch.uint8) if outs != "y" else None
+            slot = Guarded((1,), torch.float32)
+            slot.t.fill_(start)
+            L.fp8_cast_amax_acc(xd, fmt, sd, slot.t, y=y.t if y else None, y_t=yt.t if yt else None)
+            torch.cuda.synchronize()
+            for g in (y, yt, slot):
+                if g is not None:
+                    g.check()
+            if y is not None:
+                assert np.array_equal(y.np(), want), (start, outs)
+            if yt is not None:
+                assert np.array_equal(yt.np(), want.T), (start, outs)
+            assert bits(slot.np())[0] == bits(max(np.float32(start), a1)), (start, outs)
+    slot = torch.zeros(1, dtype=torch.float32, device="cuda")
+    y = torch.empty(shape, dtype=torch.uint8, device="cuda")
+    L.fp8_cast_amax_acc(xd, fmt, sd, slot, y=y)
+    L.fp8_cast_amax_acc(dev_bf16(x2), fmt, sd, slot, y=y)
+    torch.cuda.synchronize()
+    assert bits(slot.cpu().numpy())[0] == bits(max(a1, a2))
+
+
+@pytest.mark.parametrize("ln,algo", [(16, 0), (16, 1), (65, 0)])
+def test_history_update_reset(O, L, ln, algo):
+    """The resetting update gives the histories and scales of the plain one,
+    step after step, and leaves every consumed amax at 0."""
+    say("history reset", ln, algo)
+    rng = np.random.default_rng(100 + ln + algo)
+    n, steps = 5, 30
+    am = np.abs(rng.standard_normal((steps, n))).astype(np.float32) * np.float32(10)
+    am[3, 0] = 1000.0
+    am[:4, 1] = 0.0
+    am[7, 2] = np.nan
+    for fmt in (0, 1):
+        h = np.zeros((n, ln), np.float32); s = np.ones(n, np.float32); si = np.ones(n, np.float32)
+        hd, sd, sid = dev(h), dev(s), dev(si)
+        for t in range(steps):
+            ad = dev(am[t])
+            L.fp8_amax_history_update_reset(hd, ad, fmt, 0, algo, sd, sid)
+            O.history_update(h, am[t], fmt, 0, algo, s, si)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(hd.cpu().numpy()), bits(h)), t
+            assert np.array_equal(bits(sd.cpu().numpy()), bits(s)), t
+            assert np.array_equal(bits(sid.cpu().numpy()), bits(si)), t
+            assert np.all(bits(ad.cpu().numpy()) == 0), t
