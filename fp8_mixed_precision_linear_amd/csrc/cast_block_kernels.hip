@@ -88,7 +88,7 @@ __device__ __forceinline__ void store_transposed(uint8_t* lds, const uint32_t (&
     const int64_t gc = c0 + c, gr = r0 + 16 * ch;
     if (gc < cols && gr < rows) {
       uint4 v = *reinterpret_cast<const uint4*>(lds + c * 128 + phys * 16);
-      st_nt16(v, (yt + gc * rows + gr));
+      st_out16(v, (yt + gc * rows + gr));
     }
   }
 }
@@ -154,7 +154,7 @@ __global__ void __launch_bounds__(kThreads)
       w[i][0] = qa.x; w[i][1] = qa.y; w[i][2] = qb.x; w[i][3] = qb.y;
       const int64_t r = r0 + 4 * rg + i;
       if (WANT_Y && col_ok && r < rows)
-        st_nt16(make_uint4(qa.x, qa.y, qb.x, qb.y),
+        st_out16(make_uint4(qa.x, qa.y, qb.x, qb.y),
                                     reinterpret_cast<uint4*>(y + r * cols + cbase));
     }
     if (WANT_T) store_transposed(lds, w, cg, rg, t, r0, c0, rows, cols, yt);
@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(kThreads)
         if (col_ok && r < rows) {
           uint2 qa = cvt8_bf16<FMT>(v[i][0], s);
           uint2 qb = cvt8_bf16<FMT>(v[i][1], s);
-          st_nt16(make_uint4(qa.x, qa.y, qb.x, qb.y),
+          st_out16(make_uint4(qa.x, qa.y, qb.x, qb.y),
                                       reinterpret_cast<uint4*>(y + r * cols + cbase));
         }
       }

@@ -77,7 +77,7 @@ __global__ void __launch_bounds__(kBig)
       qa = cvt8_bf16<FMT>(a, s);
       qb = cvt8_bf16<FMT>(b, s);
     }
-    st_nt16(make_uint4(qa.x, qa.y, qb.x, qb.y), yv + u);
+    st_out16(make_uint4(qa.x, qa.y, qb.x, qb.y), yv + u);
   }
   uint32_t mb = AMAX ? absmax_fold(m) : 0u;
   if (blockIdx.x == 0 && threadIdx.x < (n & 15)) {
@@ -166,7 +166,7 @@ __global__ void __launch_bounds__(kBig)
       }
       w[i][0] = qa.x; w[i][1] = qa.y; w[i][2] = qb.x; w[i][3] = qb.y;
       if (WANT_Y && col_ok && r < rows)
-        st_nt16(make_uint4(qa.x, qa.y, qb.x, qb.y), reinterpret_cast<uint4*>(y + r * cols + cbase));
+        st_out16(make_uint4(qa.x, qa.y, qb.x, qb.y), reinterpret_cast<uint4*>(y + r * cols + cbase));
     }
     // transposed dwords into LDS: column c = 16*cg + 4*j + k, rows 4*rg..+3
 #pragma unroll
@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(kBig)
       const int64_t gc = c0 + c, gr = r0 + 16 * ch;
       if (gc < cols && gr < rows) {
         uint4 v = *reinterpret_cast<const uint4*>(lds + c * 128 + phys * 16);
-        st_nt16(v, (yt + gc * rows + gr));
+        st_out16(v, (yt + gc * rows + gr));
       }
     }
     __syncthreads();   // the next pass overwrites the LDS tile

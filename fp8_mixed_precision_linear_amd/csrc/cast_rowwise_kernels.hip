@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(1024)
       const int64_t gc = c0 + c, gr = r0 + 16 * ch;
       if (gc < cols && gr < rows) {
         const uint4 v = *reinterpret_cast<const uint4*>(lds + c * 128 + phys * 16);
-        st_nt16(v, yt + gc * rows + gr);
+        st_out16(v, yt + gc * rows + gr);
       }
     }
     __syncthreads();   // the next pass overwrites the tile and its scales

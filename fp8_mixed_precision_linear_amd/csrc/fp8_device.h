@@ -37,6 +37,11 @@ __device__ __forceinline__ uint4 ld_nt16(const void* p) {
   u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// FP8 outputs of the casts: a GEMM reads them next, so they are written
+// with ordinary stores, which leave them in the last-level cache (the
+// 256 MB MALL holds every operand of a 4096^3 step) instead of streaming
+// them past it as a non-temporal store does.
+__device__ __forceinline__ void st_out16(uint4 v, void* p) { *reinterpret_cast<uint4*>(p) = v; }
 __device__ __forceinline__ void st_nt16(uint4 v, void* p) {
   u32x4_t w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
