@@ -94,7 +94,9 @@ __global__ void __launch_bounds__(NT * G)
     for (int c = 0; c < NCH; ++c) {
       const int64_t col = (int64_t)c * CH + 8 * t;
       v[c] = make_uint4(0, 0, 0, 0);
-      if (have && col < cols) v[c] = ld_nt16(xr + col);   // cols % 8 == 0: all 8 in or out
+      // cols % 8 == 0: all 8 in or out.  An ordinary load: the transposed
+      // pass reads x again, from the last-level cache when it stayed there
+      if (have && col < cols) v[c] = *reinterpret_cast<const uint4*>(xr + col);
       m = absmax_pk(m, v[c].x); m = absmax_pk(m, v[c].y);
       m = absmax_pk(m, v[c].z); m = absmax_pk(m, v[c].w);
       if constexpr (COLS) {
