@@ -19,11 +19,15 @@ Also reported (same JSON line):
   roofline      -- the dominant kernel (the GEMMs), per-launch duration from
                    HIP events around R launches captured in a HIP graph, on
                    the stream the kernels run on;
-  kernels       -- per-kernel throughput (GEMM TFLOP/s, cast GB/s of
-                   algorithmic bytes) for this workload (also dY's cast with
+  kernels       -- per-kernel throughput, warm (R launches back to back in one
+                   graph, inputs left in the caches by the previous launch;
+                   GEMM TFLOP/s, cast GB/s of algorithmic bytes) for this workload (also dY's cast with
                    stochastic rounding and the EWMA scale update), plus the forward
                    GEMM with its output quantised in the epilogue (E4M3,
                    transposed copy, amax) beside the unfused GEMM + cast;
+  kernels_cold  -- the step's GEMMs, casts and amax timed cold: a 512 MiB
+                   read evicts the 256 MB MALL before every launch (median
+                   of single launches);
   rowwise       -- per-row (per-channel) scaling on the same shapes and data:
                    row-wise casts into both orientations and the three GEMMs
                    with per-row scales;
@@ -258,6 +262,47 @@ def main():
                 "achieved": round(g_ach, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(g_ach / FP8_PEAK_TFLOPS, 4), "traffic": gemm_traffic()}
 
+    # ---- cold timings: before every timed launch a 512 MiB read evicts the
+    # 256 MB last-level cache (MALL) with clean lines, so inputs come from
+    # HBM and no dirty victims are written back during the timed kernel; each
+    # launch is bracketed by its own HIP events on the stream (median of the
+    # reps; the brackets include the dispatch of that one launch)
+    flush = torch.zeros(256 << 20, dtype=torch.bfloat16, device=dev)
+    flush_amax = torch.zeros(1, dtype=torch.float32, device=dev)
+    L.fp8_amax(flush, flush_amax)
+    torch.cuda.synchronize()
+
+    def time_cold(fn, reps):
+        evs = []
+        for i in range(reps):
+            L.fp8_amax(flush, flush_amax)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        return ts[len(ts) // 2] * 1e-3   # seconds
+
+    kc = {}
+    kc["gemm_fwd_tensor"] = time_cold(lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y), R)
+    kc["gemm_dgrad_tensor"] = time_cold(lambda: L.fp8_scaled_gemm(dyq, 1, 0, sinv[2:3], wq, 0, 0, sinv[1:2], dx), R)
+    kc["gemm_wgrad_tensor"] = time_cold(lambda: L.fp8_scaled_gemm(xtq, 0, 0, sinv[0:1], dytq, 1, 0, sinv[2:3], dw), R)
+    kc["cast_transpose_amax_acc_e4m3"] = time_cold(lambda: L.fp8_cast_amax_acc(x0, 0, scale[0:1], amax[0:1], y=xq, y_t=xtq), R)
+    kc["cast_transpose_amax_acc_e5m2"] = time_cold(lambda: L.fp8_cast_amax_acc(dy0, 1, scale[2:3], amax[2:3], y=dyq, y_t=dytq), R)
+    kc["cast_e4m3"] = time_cold(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq), R)
+    kc["amax"] = time_cold(lambda: L.fp8_amax(x0, amax[0:1]), R)
+    del flush
+    kernels_cold = {"note": "MALL evicted (512 MiB read) before every timed launch; median of "
+                            f"{R} single launches, each bracketed by HIP events"}
+    for n in ("gemm_fwd_tensor", "gemm_dgrad_tensor", "gemm_wgrad_tensor"):
+        kernels_cold[n] = {"tflops": round(2.0 * T * DI * DO / kc[n] / 1e12, 2), "us": round(kc[n] * 1e6, 2)}
+    for n, bpe in (("cast_transpose_amax_acc_e4m3", 4.0), ("cast_transpose_amax_acc_e5m2", 4.0),
+                   ("cast_e4m3", 3.0), ("amax", 2.0)):
+        kernels_cold[n] = {"gbs": round(bpe * nel / kc[n] / 1e9, 2), "us": round(kc[n] * 1e6, 2),
+                           "pct_hbm_peak": round(100 * bpe * nel / kc[n] / 1e9 / HBM_PEAK_GBS, 2)}
+
     # ---- block-wise path at 8192 x 4096 x 14336
     blockwise = None
     if not args.no_blockwise:
@@ -280,6 +325,7 @@ def main():
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "roofline": roofline,
         "kernels": {n: {kk: round(vv, 2) for kk, vv in d.items()} for n, d in kernels.items()},
+        "kernels_cold": kernels_cold,
     }
     result["rowwise"] = rowwise
     if blockwise is not None:
