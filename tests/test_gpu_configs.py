@@ -42,13 +42,16 @@ def f32(shape):
     return torch.empty(shape, dtype=torch.float32, device="cuda")
 
 
-def check_gemm_sampled(O, G_dev, A, af, asc, sa, B, bf, bsc, sb, bf16, seed, a16=None, b16=None):
-    """Compare GPU output rows/cols (sampled) with the oracle."""
+def check_gemm_sampled(O, G_dev, A, af, asc, sa, B, bf, bsc, sb, bf16, seed, a16=None, b16=None,
+                       sample=None):
+    """Compare GPU output rows/cols (sampled) with the oracle.  A sampled row
+    spans every N and K block, a sampled column every M and K block."""
     M, K = A.shape
     N = B.shape[0]
+    n_s = SAMPLE if sample is None else sample
     rng = np.random.default_rng(seed)
-    ms = np.sort(rng.choice(M, min(SAMPLE, M), replace=False)).astype(np.int64)
-    ns = np.sort(rng.choice(N, min(SAMPLE, N), replace=False)).astype(np.int64)
+    ms = np.sort(rng.choice(M, min(n_s, M), replace=False)).astype(np.int64)
+    ns = np.sort(rng.choice(N, min(n_s, N), replace=False)).astype(np.int64)
     Gf = G_dev.float()
     rows = Gf[torch.from_numpy(ms).cuda()].cpu().numpy()
     cols = Gf[:, torch.from_numpy(ns).cuda()].cpu().numpy()
@@ -59,7 +62,7 @@ def check_gemm_sampled(O, G_dev, A, af, asc, sa, B, bf, bsc, sb, bf16, seed, a16
         assert ok1 and ok2, (m1, m2)
         worst.append((m1, m2))
     if a16 is not None:  # the unquantised fp64 reference on a smaller sample
-        ms2, ns2 = ms[:16], ns[:32]
+        ms2, ns2 = ms[:min(16, len(ms))], ns[:min(32, len(ns))]
         R, Bd = O.gemm_ref_bound(A, af, asc, sa, B, bf, bsc, sb, a16, b16, ms=ms2, ns=ns2)
         G = Gf[torch.from_numpy(ms2).cuda()][:, torch.from_numpy(ns2).cuda()].cpu().numpy()
         assert np.all(np.abs(G - R) <= Bd + (2.0 ** -8 if bf16 else 0) * np.abs(G))
@@ -338,3 +341,94 @@ def test_config5_qkv_linear(O, L, mode):
         assert np.array_equal(xq.cpu().numpy(), ox["y"])
         assert np.array_equal(wtq.cpu().numpy(), ow["y_t"])
         check_gemm_sampled(O, y, ox["y"], 0, 1, ox["sinv"], ow["y_t"], 0, 2, ow["sinv_t"], True, 52)
+
+
+_C5_CACHE = {}
+# tokens for the four linears below: their in / out sizes are the
+# configuration's; generating 8192 tokens of the 28672-wide activation
+# alone takes over a minute of CPU (the QKV test above runs 8192 tokens)
+C5_TOKENS = 2048
+
+
+def _c5(name):
+    if name not in _C5_CACHE:
+        _C5_CACHE.clear()   # one linear's tensors at a time (up to ~1 GB of bf16)
+        _C5_CACHE[name] = datagen.config5_linear(name, scale_rows=C5_TOKENS)
+    return _C5_CACHE[name]
+
+
+@pytest.mark.parametrize("mode", ["delayed", "block"])
+@pytest.mark.parametrize("name", ["o", "gate", "up", "down"])
+def test_config5_linear_fwd_bwd(O, L, name, mode):
+    """The other linears of the transformer-block set (in / out sizes of the
+    configuration, C5_TOKENS tokens), forward and backward: casts bit-exact
+    against the oracle (every byte and scale),
+    FWD / DGRAD / WGRAD on 8 sampled rows and 8 sampled columns each (every
+    M, N and K block), with the delayed-scaling state after one filling step
+    or with block scales."""
+    say("config5", name, mode)
+    d = _c5(name)
+    x, w, dy = d["x"], d["w"], d["dy"]
+    T, DI = x.shape
+    DO = w.shape[1]
+    xd, wd, dyd = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
+    y = torch.empty((T, DO), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty((T, DI), dtype=torch.bfloat16, device="cuda")
+    dw = f32((DI, DO))
+    xq, xtq, wq, wtq = u8((T, DI)), u8((DI, T)), u8((DI, DO)), u8((DO, DI))
+    dyq, dytq = u8((T, DO)), u8((DO, T))
+    n = 8
+    if mode == "delayed":
+        # one step fills the histories; the second step is checked
+        hist = torch.zeros((3, 16), dtype=torch.float32, device="cuda")
+        s = torch.ones(3, dtype=torch.float32, device="cuda")
+        si = torch.ones(3, dtype=torch.float32, device="cuda")
+        am = torch.zeros(3, dtype=torch.float32, device="cuda")
+        for _ in range(2):
+            s_used, si_used = s.cpu().numpy().copy(), si.cpu().numpy().copy()
+            L.fp8_cast_amax_acc(xd, 0, s[0:1], am[0:1], y=xq, y_t=xtq)
+            L.fp8_cast_amax_acc(wd, 0, s[1:2], am[1:2], y=wq, y_t=wtq)
+            L.fp8_scaled_gemm(xq, 0, 0, si[0:1], wtq, 0, 0, si[1:2], y)
+            L.fp8_cast_amax_acc(dyd, 1, s[2:3], am[2:3], y=dyq, y_t=dytq)
+            L.fp8_scaled_gemm(dyq, 1, 0, si[2:3], wq, 0, 0, si[1:2], dx)
+            L.fp8_scaled_gemm(xtq, 0, 0, si[0:1], dytq, 1, 0, si[2:3], dw)
+            L.fp8_amax_history_update_reset(hist[0:2], am[0:2], 0, 0, 0, s[0:2], si[0:2])
+            L.fp8_amax_history_update_reset(hist[2:3], am[2:3], 1, 0, 0, s[2:3], si[2:3])
+        torch.cuda.synchronize()
+        xr, wr, dr = O.cast(x, s_used[0], 0), O.cast(w, s_used[1], 0), O.cast(dy, s_used[2], 1)
+        for got, want in ((xq, xr), (xtq, xr.T), (wq, wr), (wtq, wr.T), (dyq, dr), (dytq, dr.T)):
+            assert np.array_equal(got.cpu().numpy(), want)
+        sa = lambda i: np.array([si_used[i]], np.float32)
+        say("config5 gemms", name)
+        check_gemm_sampled(O, y, xr, 0, 0, sa(0), np.ascontiguousarray(wr.T), 0, 0, sa(1), True,
+                           61, sample=n)
+        check_gemm_sampled(O, dx, dr, 1, 0, sa(2), wr, 0, 0, sa(1), True, 62, sample=n)
+        check_gemm_sampled(O, dw, np.ascontiguousarray(xr.T), 0, 0, sa(0),
+                           np.ascontiguousarray(dr.T), 1, 0, sa(2), False, 63, sample=n)
+    else:
+        sx, sxt = f32((DI // 128, T)), f32((T // 128, DI))
+        sw, swt = f32((DO // 128, DI // 128)), f32((DI // 128, DO // 128))
+        sd, sdt = f32((DO // 128, T)), f32((T // 128, DO))
+        L.fp8_cast_block(xd, 0, 1, xq, sx, xtq, sxt)
+        L.fp8_cast_block(wd, 0, 2, wq, sw, wtq, swt)
+        L.fp8_scaled_gemm(xq, 0, 1, sx, wtq, 0, 2, swt, y)
+        L.fp8_cast_block(dyd, 1, 1, dyq, sd, dytq, sdt)
+        L.fp8_scaled_gemm(dyq, 1, 1, sd, wq, 0, 2, sw, dx)
+        L.fp8_scaled_gemm(xtq, 0, 1, sxt, dytq, 1, 1, sdt, dw)
+        torch.cuda.synchronize()
+        ox = O.cast_block(x, 0, O.S1x128, want_y=True, want_t=True)
+        ow = O.cast_block(w, 0, O.S128x128, want_y=True, want_t=True)
+        od = O.cast_block(dy, 1, O.S1x128, want_y=True, want_t=True)
+        for got, want in ((xq, ox["y"]), (xtq, ox["y_t"]), (wq, ow["y"]), (wtq, ow["y_t"]),
+                          (dyq, od["y"]), (dytq, od["y_t"])):
+            assert np.array_equal(got.cpu().numpy(), want)
+        for got, want in ((sx, ox["sinv"]), (sxt, ox["sinv_t"]), (sw, ow["sinv"]),
+                          (swt, ow["sinv_t"]), (sd, od["sinv"]), (sdt, od["sinv_t"])):
+            assert np.array_equal(bits(got.cpu().numpy()), bits(want))
+        say("config5 gemms", name)
+        check_gemm_sampled(O, y, ox["y"], 0, 1, ox["sinv"], ow["y_t"], 0, 2, ow["sinv_t"], True, 64,
+                           sample=n)
+        check_gemm_sampled(O, dx, od["y"], 1, 1, od["sinv"], ow["y"], 0, 2, ow["sinv"], True, 65,
+                           sample=n)
+        check_gemm_sampled(O, dw, ox["y_t"], 0, 1, ox["sinv_t"], od["y_t"], 1, 1, od["sinv_t"],
+                           False, 66, sample=n)
