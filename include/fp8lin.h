@@ -54,7 +54,7 @@ typedef enum {
   FP8_ERR_NULL = 1,         /* a required pointer is NULL */
   FP8_ERR_SHAPE = 2,        /* negative size, or a shape rule is broken */
   FP8_ERR_ALIGN = 3,        /* pointer or leading dimension misaligned */
-  FP8_ERR_UNSUPPORTED = 4,  /* valid request this build does not implement */
+  FP8_ERR_UNSUPPORTED = 4,  /* valid request the library does not implement */
   FP8_ERR_LAUNCH = 5,       /* the HIP runtime rejected a kernel launch */
   FP8_ERR_ARG = 6           /* an enum or scalar argument is out of range */
 } fp8_status;
