@@ -13,12 +13,15 @@ normal with standard deviation s.  Weights are stored [in x out].
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 __all__ = [
     "bf16_bits", "bf16_to_f32", "normal", "student_t3", "with_outlier_columns",
     "config1", "config2_step", "config3", "config4_dy", "config5_linear",
-    "C5_LINEARS",
+    "config5_outlier_cols", "chunked_rows", "C5_LINEARS",
 ]
 
 _CHUNK_ROWS = 1024
@@ -27,11 +30,18 @@ _CHUNK_ROWS = 1024
 def bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round binary32 values to bf16 (nearest, ties to even) -> uint16 bits."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    b = a.view(np.uint32).astype(np.uint64)
-    nan = (b & 0x7FFFFFFF) > 0x7F800000
-    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    b = a.view(np.uint32)
+    # 32-bit arithmetic, in place: only NaN patterns can wrap, and those are
+    # replaced below
+    r = b >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += b
+    r >>= np.uint32(16)
+    r = r.astype(np.uint16)
+    nan = np.isnan(a)
     if nan.any():
-        r[nan] = ((b[nan] >> 16) | 0x40).astype(np.uint16)
+        r[nan] = ((b[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
     return r
 
 
@@ -64,12 +74,18 @@ def student_t3(rng: np.random.Generator, shape, scale: float = 1.0,
     out = np.empty((rows, cols), dtype=np.uint16)
     for r0 in range(0, rows, _CHUNK_ROWS):
         r1 = min(rows, r0 + _CHUNK_ROWS)
-        z0 = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
-        z1 = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
-        z2 = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
-        z3 = rng.standard_normal((r1 - r0, cols), dtype=np.float32)
-        den = np.sqrt((z1 * z1 + z2 * z2 + z3 * z3) / np.float32(3.0))
-        t = z0 / den
+        t = rng.standard_normal((r1 - r0, cols), dtype=np.float32)      # z0
+        den = rng.standard_normal((r1 - r0, cols), dtype=np.float32)    # z1
+        den *= den
+        z = rng.standard_normal((r1 - r0, cols), dtype=np.float32)      # z2
+        z *= z
+        den += z
+        rng.standard_normal((r1 - r0, cols), dtype=np.float32, out=z)   # z3
+        z *= z
+        den += z
+        den /= np.float32(3.0)
+        np.sqrt(den, out=den)
+        t /= den
         if scale != 1.0:
             t *= np.float32(scale)
         if outlier_cols is not None:
@@ -124,7 +140,7 @@ def config4_dy(rng: np.random.Generator, tokens: int = 8192, d_out: int = 14336)
     return normal(rng, (tokens, d_out), 1e-3)
 
 
-# Transformer-block linear set: name -> (in, out, activation input group)
+# Transformer-block linear set: name -> (in, out)
 C5_LINEARS = {
     "qkv": (8192, 10240),
     "o": (8192, 8192),
@@ -133,23 +149,68 @@ C5_LINEARS = {
     "down": (28672, 8192),
 }
 _C5_ORDER = ["qkv", "o", "gate", "up", "down"]
+_X, _W, _DY = 0, 1, 2
 
 
-def config5_linear(name: str, seed: int = 0, tokens: int = 8192, scale_rows: int = None):
-    """One linear of the transformer-block set.  Each linear has its own
-    generator: SeedSequence(seed, spawn_key=(index,)); gate and up share the
-    gate/up activation (index of "gate").  Draw order: X (Student-t(3) with
-    round(0.001*in) channels x100), W [in x out] N(0,0.02), dY [T x out]
-    N(0,1e-3).  `scale_rows` limits T for parity-sized runs."""
+def _workers() -> int:
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def chunked_rows(shape, seed: int, key: tuple, draw, row_range=None) -> np.ndarray:
+    """bf16 bits of a [rows x cols] tensor drawn in chunks of 1024 rows, chunk
+    c from its own generator default_rng(SeedSequence(seed, spawn_key=key +
+    (c,))) by `draw(rng, chunk_shape)`, so chunks are independent and are
+    drawn on worker threads.  `row_range` = (r0, r1) (chunk-aligned r0)
+    returns only those rows, with the same values as the full tensor."""
+    rows, cols = shape
+    r0, r1 = (0, rows) if row_range is None else row_range
+    assert r0 % _CHUNK_ROWS == 0 and 0 <= r0 <= r1 <= rows
+    out = np.empty((r1 - r0, cols), dtype=np.uint16)
+
+    def one(c):
+        a = c * _CHUNK_ROWS
+        b = min(rows, a + _CHUNK_ROWS, r1)
+        rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=tuple(key) + (c,)))
+        out[a - r0:b - r0] = draw(rng, (min(rows, a + _CHUNK_ROWS) - a, cols))[:b - a]
+
+    chunks = range(r0 // _CHUNK_ROWS, (r1 + _CHUNK_ROWS - 1) // _CHUNK_ROWS)
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, chunks))
+    return out
+
+
+def config5_outlier_cols(name: str, seed: int = 0) -> np.ndarray:
+    """The round(0.001 * in) outlier channels of a linear's activation
+    (gate and up share theirs), from SeedSequence(seed, spawn_key=(i, 0))."""
+    d_in = C5_LINEARS[name][0]
+    x_idx = _C5_ORDER.index("gate") if name == "up" else _C5_ORDER.index(name)
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(x_idx, _X)))
+    return np.sort(rng.choice(d_in, int(round(0.001 * d_in)), replace=False))
+
+
+def config5_linear(name: str, seed: int = 0, tokens: int = 8192, token_range=None,
+                   parts=("x", "w", "dy")):
+    """One linear of the transformer-block set, [T x in] activation X,
+    [in x out] weight W, [T x out] gradient dY:
+      X  Student-t(3) with round(0.001*in) channels x100 (config5_outlier_cols);
+      W  N(0, 0.02);  dY  N(0, 1e-3).
+    Linear i (qkv, o, gate, up, down = 0..4) draws tensor r (X 0, W 1, dY 2)
+    in chunks of 1024 rows, chunk c from SeedSequence(seed, spawn_key=(i, r,
+    c)); gate and up share the activation of "gate".  `token_range` limits
+    X and dY to those token rows (same values as in the full tensors)."""
     d_in, d_out = C5_LINEARS[name]
-    t = tokens if scale_rows is None else scale_rows
     idx = _C5_ORDER.index(name)
     x_idx = _C5_ORDER.index("gate") if name == "up" else idx
-    rng_x = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(x_idx,)))
-    n_out = int(round(0.001 * d_in))
-    cols = np.sort(rng_x.choice(d_in, n_out, replace=False))
-    x = student_t3(rng_x, (t, d_in), 1.0, outlier_cols=cols, outlier_mul=100.0)
-    rng_w = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(idx, 1)))
-    w = normal(rng_w, (d_in, d_out), 0.02)
-    dy = normal(rng_w, (t, d_out), 1e-3)
-    return {"x": x, "w": w, "dy": dy, "outlier_cols": cols}
+    cols = config5_outlier_cols(name, seed)
+    out = {"outlier_cols": cols}
+    if "x" in parts:
+        out["x"] = chunked_rows((tokens, d_in), seed, (x_idx, _X),
+                                lambda r, sh: student_t3(r, sh, 1.0, outlier_cols=cols,
+                                                         outlier_mul=100.0),
+                                token_range)
+    if "w" in parts:
+        out["w"] = chunked_rows((d_in, d_out), seed, (idx, _W), lambda r, sh: normal(r, sh, 0.02))
+    if "dy" in parts:
+        out["dy"] = chunked_rows((tokens, d_out), seed, (idx, _DY),
+                                 lambda r, sh: normal(r, sh, 1e-3), token_range)
+    return out
