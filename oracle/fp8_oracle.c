@@ -631,9 +631,9 @@ typedef struct {
 
 /* floor(log2(v)) of a positive 128-bit integer */
 static int ilog2_u128(unsigned __int128 v) {
-  int e = -1;
-  while (v) { v >>= 1; ++e; }
-  return e;
+  const uint64_t hi = (uint64_t)(v >> 64), lo = (uint64_t)v;
+  if (hi) return 127 - __builtin_clzll(hi);
+  return lo ? 63 - __builtin_clzll(lo) : -1;
 }
 
 static void* gemm_worker(void* p) {
@@ -670,27 +670,36 @@ static void* gemm_worker(void* p) {
         unsigned __int128 Sabs = 0;
         float sa = scale_at(g->a_scaling, g->a_sinv, g->M, m, kb);
         float sb = scale_at(g->b_scaling, g->b_sinv, g->N, n, kb);
-        for (int64_t k = k0; k < k1; ++k) {
-          __int128 p = (__int128)arow[k] * (__int128)lut_b[brow[k]];
-          S += p;
-          Sabs += (unsigned __int128)(p < 0 ? -p : p);
+        /* products of two integer significands (below 2^64 in magnitude;
+         * both E5M2 may exceed 2^63), each formed once per block */
+        __int128 pk[128];
+        for (int64_t k = k0; k < k1; ++k) pk[k - k0] = (__int128)arow[k] * (__int128)lut_b[brow[k]];
+        for (int64_t k = 0; k < k1 - k0; ++k) {
+          S += pk[k];
+          Sabs += (unsigned __int128)(pk[k] < 0 ? -pk[k] : pk[k]);
         }
         if (jb->H) {
-          /* per group of hgroup consecutive k: (hgroup-1) products may each
-           * lose less than 2^(e_max - hbits), e_max = exponent of the
-           * group's largest |product| */
-          for (int64_t k = k0; k < k1; k += jb->hgroup) {
+          /* per group of hgroup consecutive k, with step q = 2^(e_max -
+           * hbits) (e_max = exponent of the group's largest |product|):
+           * a product that is not a multiple of q may lose less than q
+           * (whichever way it is cut to the step); a multiple of q loses
+           * nothing */
+          for (int64_t k = 0; k < k1 - k0; k += jb->hgroup) {
+            const int64_t ke = k + jb->hgroup < k1 - k0 ? k + jb->hgroup : k1 - k0;
             unsigned __int128 gm = 0;
-            for (int64_t kk = k; kk < k + jb->hgroup && kk < k1; ++kk) {
-              __int128 p = (__int128)arow[kk] * (__int128)lut_b[brow[kk]];
-              unsigned __int128 ap = (unsigned __int128)(p < 0 ? -p : p);
+            for (int64_t kk = k; kk < ke; ++kk) {
+              unsigned __int128 ap = (unsigned __int128)(pk[kk] < 0 ? -pk[kk] : pk[kk]);
               if (ap > gm) gm = ap;
             }
             if (gm) {
               int e = ilog2_u128(gm) - jb->hbits;
-              double t = (double)(jb->hgroup - 1) * ldexp(1.0, e - (qa + qb));
-              hsum += t * fabs((double)scale_at(g->a_scaling, g->a_sinv, g->M, m, kb)) *
-                      fabs((double)scale_at(g->b_scaling, g->b_sinv, g->N, n, kb));
+              int inexact = 0;
+              if (e > 0) {
+                unsigned __int128 low = ((unsigned __int128)1 << e) - 1;
+                for (int64_t kk = k; kk < ke; ++kk)
+                  if ((unsigned __int128)(pk[kk] < 0 ? -pk[kk] : pk[kk]) & low) ++inexact;
+              }
+              hsum += (double)inexact * ldexp(1.0, e - (qa + qb)) * fabs((double)sa) * fabs((double)sb);
             }
           }
         }
@@ -747,10 +756,12 @@ void o_gemm(const o_gemm_args* g, const int64_t* ms, int64_t nm,
 }
 
 /* As o_gemm, plus H: a bound on the error of a matrix unit that sums each
- * group of `hgroup` consecutive products exactly after truncating every
- * product below 2^(e_max - hbits) (e_max: exponent of the group's largest
- * product), in original (dequantised) units.  This is a tolerance model for
- * tests of a GPU implementation, not part of what the layer computes. */
+ * group of `hgroup` consecutive products exactly after cutting every
+ * product to a multiple of 2^(e_max - hbits) (e_max: exponent of the
+ * group's largest product), toward zero or toward minus infinity: the
+ * number of products that are not such multiples times that step, in
+ * original (dequantised) units.  This is a tolerance model for tests of a
+ * GPU implementation, not part of what the layer computes. */
 void o_gemm_h(const o_gemm_args* g, const int64_t* ms, int64_t nm,
               const int64_t* ns, int64_t nn, double* E, float* F, double* Dm,
               double* H, int hgroup, int hbits, int nthreads) {

@@ -185,10 +185,32 @@ def test_bf16_output_rounding(O):
     assert np.array_equal(bits, datagen.bf16_bits(x))
 
 
+def _sim_truncating_unit(ia, ib, m, n, K, floor_div):
+    """Exact integer simulation of a unit that, in each group of 8
+    consecutive products, cuts every product to a multiple of
+    2^(e_max - 13) (floor_div: toward minus infinity, else toward zero),
+    then sums exactly."""
+    tot = 0
+    for g0 in range(0, K, 8):
+        p = [int(ia[m, k]) * int(ib[n, k]) for k in range(g0, g0 + 8)]
+        mx = max(abs(v) for v in p)
+        if mx == 0:
+            continue
+        grid = 1 << max(0, mx.bit_length() - 1 - 13)
+        if floor_div:
+            tot += sum((v // grid) * grid for v in p)
+        else:
+            tot += sum((abs(v) // grid) * grid * (1 if v >= 0 else -1) for v in p)
+    return tot
+
+
 def test_group_truncation_bound_covers_a_simulated_unit(O):
-    """H bounds the error of a summation unit that truncates, in each group
-    of 8 consecutive products, everything below 2^(e_max - 13) toward zero:
-    simulate that unit exactly in Python (integers) and compare."""
+    """H bounds the error of a summation unit that cuts, in each group of 8
+    consecutive products, everything below 2^(e_max - 13), toward zero or
+    toward minus infinity: simulate both exactly in Python (integers) and
+    compare; H counts only products with bits below that step, so it is
+    below the count-every-product bound (7 steps per group) and still not
+    vacuous."""
     rng = np.random.default_rng(41)
     M, N, K = 6, 5, 256
     for af, bf in [(0, 0), (1, 0)]:
@@ -203,16 +225,33 @@ def test_group_truncation_bound_covers_a_simulated_unit(O):
         worst = 0.0
         for m in range(M):
             for n in range(N):
-                tot = 0
+                loose = 0
                 for g0 in range(0, K, 8):
-                    p = [int(ia[m, k]) * int(ib[n, k]) for k in range(g0, g0 + 8)]
-                    mx = max(abs(v) for v in p)
-                    if mx == 0:
-                        continue
-                    grid = 1 << max(0, mx.bit_length() - 1 - 13)
-                    tot += sum((abs(v) // grid) * grid * (1 if v >= 0 else -1) for v in p)
-                sim = tot / 2.0 ** (qa + qb)
-                err = abs(sim - r["E"][m, n])
-                assert err <= r["H"][m, n] * (1 + 1e-12)
-                worst = max(worst, err / r["H"][m, n] if r["H"][m, n] else 0)
+                    mx = max(abs(int(ia[m, k]) * int(ib[n, k])) for k in range(g0, g0 + 8))
+                    if mx:
+                        loose += 7 * (1 << max(0, mx.bit_length() - 1 - 13))
+                assert r["H"][m, n] <= loose / 2.0 ** (qa + qb) * (1 + 1e-12)
+                for floor_div in (False, True):
+                    sim = _sim_truncating_unit(ia, ib, m, n, K, floor_div) / 2.0 ** (qa + qb)
+                    err = abs(sim - r["E"][m, n])
+                    assert err <= r["H"][m, n] * (1 + 1e-12)
+                    worst = max(worst, err / r["H"][m, n] if r["H"][m, n] else 0)
         assert worst > 0.05   # the bound is not vacuous
+
+
+def test_group_truncation_bound_is_zero_on_exactly_summable_codes(O):
+    """Magnitudes in [1, 8) (the narrow band of the strict GPU tests): every
+    product is a multiple of 2^-6 below 64, so no group can lose a bit and
+    H is exactly zero."""
+    rng = np.random.default_rng(43)
+    for af, bf in [(0, 0), (1, 0), (0, 1)]:
+        def narrow(shape, fmt):
+            if fmt == 0:
+                c = (rng.integers(7, 10, size=shape) << 3) | rng.integers(0, 8, size=shape)
+            else:
+                c = (rng.integers(15, 18, size=shape) << 2) | rng.integers(0, 4, size=shape)
+            return (c | (rng.integers(0, 2, size=shape) << 7)).astype(np.uint8)
+        A, B = narrow((7, 384), af), narrow((9, 384), bf)
+        one = np.ones(1, np.float32)
+        r = O.gemm(A, af, 0, one, B, bf, 0, one, want=("E", "H"))
+        assert np.all(r["H"] == 0)
