@@ -6,17 +6,18 @@ configuration bench.py times:
     scales and histories bit-exact every step; casts bit-exact; GEMMs on
     sampled rows and columns), and checkpoint / restore of the scale state
     in the middle of the run;
-  - block-wise forward at 8192 x 4096 x 14336 and backward (dgrad, wgrad);
-  - one transformer-block linear (QKV, 8192 tokens, 8192 -> 10240) in both
-    modes.
+  - block-wise forward at 8192 x 4096 x 14336 and backward (dgrad, wgrad).
 Casts are compared on every element; GEMMs on 128 sampled rows and 128
-sampled columns (seeded), which cover every K block and every N block."""
+sampled columns (seeded), which cover every K block and every N block,
+under the GEMM gate |G - F| <= 1e-3 max(|F|, D/64) (+ the matrix unit's
+in-instruction bound H, zero where it sums exactly) on every sampled
+element.  The transformer-block linear set is in test_gpu_c5.py."""
 import numpy as np
 import pytest
 import torch
 
 from fp8_mixed_precision_linear_amd import datagen
-from tests.gpu_util import dev, dev_bf16, gemm_check, say
+from tests.gpu_util import dev, dev_bf16, gate_stats, h_sampler, log_gate, say
 
 pytestmark = pytest.mark.gpu
 
@@ -43,9 +44,15 @@ def f32(shape):
 
 
 def check_gemm_sampled(O, G_dev, A, af, asc, sa, B, bf, bsc, sb, bf16, seed, a16=None, b16=None,
-                       sample=None):
-    """Compare GPU output rows/cols (sampled) with the oracle.  A sampled row
-    spans every N and K block, a sampled column every M and K block."""
+                       sample=None, label=""):
+    """Compare GPU output rows/cols (sampled) with the oracle under the GEMM
+    gate on every sampled element:
+        |G - F| <= 1e-3 max(|F|, D/64) + H
+    (plus half a bf16 ulp of F for BF16 outputs), H the oracle's bound on
+    what the matrix unit may drop inside one instruction (zero wherever the
+    unit sums exactly: see gate_stats); the plain ratio (without H) is
+    logged beside it.  A sampled row spans every N and K block, a sampled
+    column every M and K block."""
     M, K = A.shape
     N = B.shape[0]
     n_s = SAMPLE if sample is None else sample
@@ -56,11 +63,13 @@ def check_gemm_sampled(O, G_dev, A, af, asc, sa, B, bf, bsc, sb, bf16, seed, a16
     rows = Gf[torch.from_numpy(ms).cuda()].cpu().numpy()
     cols = Gf[:, torch.from_numpy(ns).cuda()].cpu().numpy()
     worst = []
-    for G, sel in ((rows, dict(ms=ms)), (cols, dict(ns=ns))):
-        ref = O.gemm(A, af, asc, sa, B, bf, bsc, sb, want=("E", "F", "D", "H"), **sel)
-        ok1, ok2, m1, m2 = gemm_check(G, ref, K, bf16=bf16)
-        assert ok1 and ok2, (m1, m2)
-        worst.append((m1, m2))
+    args = (A, af, asc, sa, B, bf, bsc, sb)
+    for G, sel, part in ((rows, dict(ms=ms), "rows"), (cols, dict(ns=ns), "cols")):
+        ref = O.gemm(*args, want=("E", "F", "D"), **sel)
+        st = gate_stats(G, ref, bf16, h_of=h_sampler(O, *args, **sel))
+        log_gate(f"{label} {part} M{M} N{N} K{K}", st)
+        assert st["max_rel_hw"] <= 1e-3, st
+        worst.append(st)
     if a16 is not None:  # the unquantised fp64 reference on a smaller sample
         ms2, ns2 = ms[:min(16, len(ms))], ns[:min(32, len(ns))]
         R, Bd = O.gemm_ref_bound(A, af, asc, sa, B, bf, bsc, sb, a16, b16, ms=ms2, ns=ns2)
@@ -97,7 +106,7 @@ def test_config1_current_scaling_forward(O, L):
     assert np.array_equal(xq.cpu().numpy(), xr)
     assert np.array_equal(wtq.cpu().numpy(), wtr)
     check_gemm_sampled(O, y, xr, 0, 0, np.array([six]), wtr, 0, 0, np.array([siw]), True, 1,
-                       a16=x, b16=np.ascontiguousarray(w.T))
+                       a16=x, b16=np.ascontiguousarray(w.T), label="config1 fwd")
     raw = y.view(torch.int16).cpu().numpy().view(np.uint16)
     assert bits(d_amax.cpu().numpy())[0] == (np.uint32(np.max(raw & 0x7FFF)) << 16)
 
@@ -200,10 +209,13 @@ def test_config2_delayed_16_steps(O, L, c2_data, fused):
                 sa = lambda i: np.array([si_used[i]], np.float32)
                 check_gemm_sampled(O, run.y, xr, 0, 0, sa(0), np.ascontiguousarray(wr.T), 0, 0,
                                    sa(1), True, 100 + t,
-                                   a16=d["x"], b16=np.ascontiguousarray(d["w"].T))
-                check_gemm_sampled(O, run.dx, dr, 1, 0, sa(2), wr, 0, 0, sa(1), True, 200 + t)
+                                   a16=d["x"], b16=np.ascontiguousarray(d["w"].T),
+                                   label=f"config2 step{t} fwd")
+                check_gemm_sampled(O, run.dx, dr, 1, 0, sa(2), wr, 0, 0, sa(1), True, 200 + t,
+                                   label=f"config2 step{t} dgrad")
                 check_gemm_sampled(O, run.dw, np.ascontiguousarray(xr.T), 0, 0, sa(0),
-                                   np.ascontiguousarray(dr.T), 1, 0, sa(2), False, 300 + t)
+                                   np.ascontiguousarray(dr.T), 1, 0, sa(2), False, 300 + t,
+                                   label=f"config2 step{t} wgrad")
 
 
 def test_config2_checkpoint_restore_bitexact(O, L, c2_data):
@@ -261,7 +273,7 @@ def test_config3_blockwise_forward(O, L, c34):
     assert np.array_equal(bits(swt.cpu().numpy()), bits(ow["sinv_t"]))
     say("config3 gemm")
     check_gemm_sampled(O, y, ox["y"], 0, 1, ox["sinv"], ow["y_t"], 0, 2, ow["sinv_t"], True, 3,
-                       a16=x, b16=np.ascontiguousarray(w.T))
+                       a16=x, b16=np.ascontiguousarray(w.T), label="config3 fwd")
 
 
 def test_config4_blockwise_backward(O, L, c34):
@@ -291,144 +303,8 @@ def test_config4_blockwise_backward(O, L, c34):
     ow = O.cast_block(w, 0, O.S128x128, want_y=True)
     say("config4 dgrad")
     check_gemm_sampled(O, dx, od["y"], 1, 1, od["sinv"], ow["y"], 0, 2, ow["sinv"], True, 4,
-                       a16=dy, b16=w)
+                       a16=dy, b16=w, label="config4 dgrad")
     say("config4 wgrad")
     check_gemm_sampled(O, dw, ox["y_t"], 0, 1, ox["sinv_t"], od["y_t"], 1, 1, od["sinv_t"], False, 5,
-                       a16=np.ascontiguousarray(x.T), b16=np.ascontiguousarray(dy.T))
-
-
-# ---------------------------------------------------------------- config 5 ---
-@pytest.mark.parametrize("mode", ["delayed", "block"])
-def test_config5_qkv_linear(O, L, mode):
-    say("config5 qkv", mode)
-    d = datagen.config5_linear("qkv")
-    x, w, dy = d["x"], d["w"], d["dy"]
-    T, DI = x.shape
-    DO = w.shape[1]
-    xd, wd = dev_bf16(x), dev_bf16(w)
-    y = torch.empty((T, DO), dtype=torch.bfloat16, device="cuda")
-    if mode == "delayed":
-        # one step to fill the histories, then the measured step's forward
-        hist = torch.zeros((2, 16), dtype=torch.float32, device="cuda")
-        s = torch.ones(2, dtype=torch.float32, device="cuda")
-        si = torch.ones(2, dtype=torch.float32, device="cuda")
-        am = torch.zeros(2, dtype=torch.float32, device="cuda")
-        xq, wtq = u8((T, DI)), u8((DO, DI))
-        for _ in range(2):
-            L.fp8_cast_e4m3(xd, s[0:1], y=xq, amax_out=am[0:1])
-            L.fp8_cast_e4m3(wd, s[1:2], y_t=wtq, amax_out=am[1:2])
-            s_used = s.cpu().numpy().copy()
-            si_used = si.cpu().numpy().copy()
-            L.fp8_scaled_gemm(xq, 0, 0, si[0:1], wtq, 0, 0, si[1:2], y)
-            L.fp8_amax_history_update(hist, am, 0, 0, 0, s, si)
-        torch.cuda.synchronize()
-        xr = O.cast(x, s_used[0], 0)
-        wr = O.cast(w, s_used[1], 0)
-        assert np.array_equal(xq.cpu().numpy(), xr)
-        assert np.array_equal(wtq.cpu().numpy(), wr.T)
-        check_gemm_sampled(O, y, xr, 0, 0, si_used[0:1], np.ascontiguousarray(wr.T), 0, 0,
-                           si_used[1:2], True, 51)
-    else:
-        xq, sx = u8((T, DI)), f32((DI // 128, T))
-        wtq, swt = u8((DO, DI)), f32((DI // 128, DO // 128))
-        wq, sw = u8((DI, DO)), f32((DO // 128, DI // 128))
-        L.fp8_cast_block(xd, 0, 1, xq, sx)
-        L.fp8_cast_block(wd, 0, 2, wq, sw, wtq, swt)
-        L.fp8_scaled_gemm(xq, 0, 1, sx, wtq, 0, 2, swt, y)
-        torch.cuda.synchronize()
-        ox = O.cast_block(x, 0, O.S1x128, want_y=True)
-        ow = O.cast_block(w, 0, O.S128x128, want_y=True, want_t=True)
-        assert np.array_equal(xq.cpu().numpy(), ox["y"])
-        assert np.array_equal(wtq.cpu().numpy(), ow["y_t"])
-        check_gemm_sampled(O, y, ox["y"], 0, 1, ox["sinv"], ow["y_t"], 0, 2, ow["sinv_t"], True, 52)
-
-
-_C5_CACHE = {}
-# tokens for the four linears below: their in / out sizes are the
-# configuration's; generating 8192 tokens of the 28672-wide activation
-# alone takes over a minute of CPU (the QKV test above runs 8192 tokens)
-C5_TOKENS = 2048
-
-
-def _c5(name):
-    if name not in _C5_CACHE:
-        _C5_CACHE.clear()   # one linear's tensors at a time (up to ~1 GB of bf16)
-        _C5_CACHE[name] = datagen.config5_linear(name, scale_rows=C5_TOKENS)
-    return _C5_CACHE[name]
-
-
-@pytest.mark.parametrize("mode", ["delayed", "block"])
-@pytest.mark.parametrize("name", ["o", "gate", "up", "down"])
-def test_config5_linear_fwd_bwd(O, L, name, mode):
-    """The other linears of the transformer-block set (in / out sizes of the
-    configuration, C5_TOKENS tokens), forward and backward: casts bit-exact
-    against the oracle (every byte and scale),
-    FWD / DGRAD / WGRAD on 8 sampled rows and 8 sampled columns each (every
-    M, N and K block), with the delayed-scaling state after one filling step
-    or with block scales."""
-    say("config5", name, mode)
-    d = _c5(name)
-    x, w, dy = d["x"], d["w"], d["dy"]
-    T, DI = x.shape
-    DO = w.shape[1]
-    xd, wd, dyd = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
-    y = torch.empty((T, DO), dtype=torch.bfloat16, device="cuda")
-    dx = torch.empty((T, DI), dtype=torch.bfloat16, device="cuda")
-    dw = f32((DI, DO))
-    xq, xtq, wq, wtq = u8((T, DI)), u8((DI, T)), u8((DI, DO)), u8((DO, DI))
-    dyq, dytq = u8((T, DO)), u8((DO, T))
-    n = 8
-    if mode == "delayed":
-        # one step fills the histories; the second step is checked
-        hist = torch.zeros((3, 16), dtype=torch.float32, device="cuda")
-        s = torch.ones(3, dtype=torch.float32, device="cuda")
-        si = torch.ones(3, dtype=torch.float32, device="cuda")
-        am = torch.zeros(3, dtype=torch.float32, device="cuda")
-        for _ in range(2):
-            s_used, si_used = s.cpu().numpy().copy(), si.cpu().numpy().copy()
-            L.fp8_cast_amax_acc(xd, 0, s[0:1], am[0:1], y=xq, y_t=xtq)
-            L.fp8_cast_amax_acc(wd, 0, s[1:2], am[1:2], y=wq, y_t=wtq)
-            L.fp8_scaled_gemm(xq, 0, 0, si[0:1], wtq, 0, 0, si[1:2], y)
-            L.fp8_cast_amax_acc(dyd, 1, s[2:3], am[2:3], y=dyq, y_t=dytq)
-            L.fp8_scaled_gemm(dyq, 1, 0, si[2:3], wq, 0, 0, si[1:2], dx)
-            L.fp8_scaled_gemm(xtq, 0, 0, si[0:1], dytq, 1, 0, si[2:3], dw)
-            L.fp8_amax_history_update_reset(hist[0:2], am[0:2], 0, 0, 0, s[0:2], si[0:2])
-            L.fp8_amax_history_update_reset(hist[2:3], am[2:3], 1, 0, 0, s[2:3], si[2:3])
-        torch.cuda.synchronize()
-        xr, wr, dr = O.cast(x, s_used[0], 0), O.cast(w, s_used[1], 0), O.cast(dy, s_used[2], 1)
-        for got, want in ((xq, xr), (xtq, xr.T), (wq, wr), (wtq, wr.T), (dyq, dr), (dytq, dr.T)):
-            assert np.array_equal(got.cpu().numpy(), want)
-        sa = lambda i: np.array([si_used[i]], np.float32)
-        say("config5 gemms", name)
-        check_gemm_sampled(O, y, xr, 0, 0, sa(0), np.ascontiguousarray(wr.T), 0, 0, sa(1), True,
-                           61, sample=n)
-        check_gemm_sampled(O, dx, dr, 1, 0, sa(2), wr, 0, 0, sa(1), True, 62, sample=n)
-        check_gemm_sampled(O, dw, np.ascontiguousarray(xr.T), 0, 0, sa(0),
-                           np.ascontiguousarray(dr.T), 1, 0, sa(2), False, 63, sample=n)
-    else:
-        sx, sxt = f32((DI // 128, T)), f32((T // 128, DI))
-        sw, swt = f32((DO // 128, DI // 128)), f32((DI // 128, DO // 128))
-        sd, sdt = f32((DO // 128, T)), f32((T // 128, DO))
-        L.fp8_cast_block(xd, 0, 1, xq, sx, xtq, sxt)
-        L.fp8_cast_block(wd, 0, 2, wq, sw, wtq, swt)
-        L.fp8_scaled_gemm(xq, 0, 1, sx, wtq, 0, 2, swt, y)
-        L.fp8_cast_block(dyd, 1, 1, dyq, sd, dytq, sdt)
-        L.fp8_scaled_gemm(dyq, 1, 1, sd, wq, 0, 2, sw, dx)
-        L.fp8_scaled_gemm(xtq, 0, 1, sxt, dytq, 1, 1, sdt, dw)
-        torch.cuda.synchronize()
-        ox = O.cast_block(x, 0, O.S1x128, want_y=True, want_t=True)
-        ow = O.cast_block(w, 0, O.S128x128, want_y=True, want_t=True)
-        od = O.cast_block(dy, 1, O.S1x128, want_y=True, want_t=True)
-        for got, want in ((xq, ox["y"]), (xtq, ox["y_t"]), (wq, ow["y"]), (wtq, ow["y_t"]),
-                          (dyq, od["y"]), (dytq, od["y_t"])):
-            assert np.array_equal(got.cpu().numpy(), want)
-        for got, want in ((sx, ox["sinv"]), (sxt, ox["sinv_t"]), (sw, ow["sinv"]),
-                          (swt, ow["sinv_t"]), (sd, od["sinv"]), (sdt, od["sinv_t"])):
-            assert np.array_equal(bits(got.cpu().numpy()), bits(want))
-        say("config5 gemms", name)
-        check_gemm_sampled(O, y, ox["y"], 0, 1, ox["sinv"], ow["y_t"], 0, 2, ow["sinv_t"], True, 64,
-                           sample=n)
-        check_gemm_sampled(O, dx, od["y"], 1, 1, od["sinv"], ow["y"], 0, 2, ow["sinv"], True, 65,
-                           sample=n)
-        check_gemm_sampled(O, dw, ox["y_t"], 0, 1, ox["sinv_t"], od["y_t"], 1, 1, od["sinv_t"],
-                           False, 66, sample=n)
+                       a16=np.ascontiguousarray(x.T), b16=np.ascontiguousarray(dy.T),
+                       label="config4 wgrad")

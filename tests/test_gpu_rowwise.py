@@ -219,10 +219,11 @@ def test_rowwise_fwd_bwd_full_size(O, L):
     rx, rw, rd = ref["x"], ref["w"], ref["dy"]
     say("rowwise full-size fwd")
     check_gemm_sampled(O, y, rx["y"], 0, ROW, rx["sinv"], rw["y_t"], 0, ROW, rw["sinv_t"], True, 61,
-                       a16=x, b16=np.ascontiguousarray(w.T))
+                       a16=x, b16=np.ascontiguousarray(w.T), label="rowwise 4096 fwd")
     say("rowwise full-size dgrad")
     check_gemm_sampled(O, dx, rd["y"], 1, ROW, rd["sinv"], rw["y"], 0, ROW, rw["sinv"], True, 62,
-                       a16=dy, b16=w)
+                       a16=dy, b16=w, label="rowwise 4096 dgrad")
     say("rowwise full-size wgrad")
     check_gemm_sampled(O, dw, rx["y_t"], 0, ROW, rx["sinv_t"], rd["y_t"], 1, ROW, rd["sinv_t"], False,
-                       63, a16=np.ascontiguousarray(x.T), b16=np.ascontiguousarray(dy.T))
+                       63, a16=np.ascontiguousarray(x.T), b16=np.ascontiguousarray(dy.T),
+                       label="rowwise 4096 wgrad")
