@@ -8,4 +8,4 @@ include/fp8lin.h; `fp8_mixed_precision_linear_amd.lib` is its Python binding
 `fp8_mixed_precision_linear_amd.datagen` holds the seeded synthetic inputs.
 """
 
-__all__ = ["lib", "datagen", "build", "layer"]
+__all__ = ["lib", "datagen", "build"]

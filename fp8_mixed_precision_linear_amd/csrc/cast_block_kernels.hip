@@ -22,19 +22,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
-                                             uint32_t& t0, uint32_t& t1, uint32_t& t2,
-                                             uint32_t& t3) {
-  uint32_t a01_lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
-  uint32_t a01_hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
-  uint32_t a23_lo = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
-  uint32_t a23_hi = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
-  t0 = __builtin_amdgcn_perm(a23_lo, a01_lo, 0x05040100u);
-  t1 = __builtin_amdgcn_perm(a23_lo, a01_lo, 0x07060302u);
-  t2 = __builtin_amdgcn_perm(a23_hi, a01_hi, 0x05040100u);
-  t3 = __builtin_amdgcn_perm(a23_hi, a01_hi, 0x07060302u);
-}
-
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
 // Halfwise unsigned 16-bit maximum of two packed pairs.

@@ -268,4 +268,42 @@ __device__ __forceinline__ void atomic_max_bits(float* dst, uint32_t bits) {
   if (bits > cur) atomicMax(p, bits);
 }
 
+// ---------------------------------------------------------------------
+// Helpers shared by the cast and GEMM kernels.
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// 4 x 4 byte transpose in registers: wK holds bytes [row K][col 0..3], tJ
+// receives bytes [row 0..3][col J].  __builtin_amdgcn_perm(hi, lo, sel):
+// selector bytes 0-3 pick from lo, 4-7 from hi.
+__device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                             uint32_t& t0, uint32_t& t1, uint32_t& t2,
+                                             uint32_t& t3) {
+  const uint32_t a01_lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // r0c0 r1c0 r0c1 r1c1
+  const uint32_t a01_hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // r0c2 r1c2 r0c3 r1c3
+  const uint32_t a23_lo = __builtin_amdgcn_perm(w3, w2, 0x05010400u);  // r2c0 r3c0 r2c1 r3c1
+  const uint32_t a23_hi = __builtin_amdgcn_perm(w3, w2, 0x07030602u);  // r2c2 r3c2 r2c3 r3c3
+  t0 = __builtin_amdgcn_perm(a23_lo, a01_lo, 0x05040100u);             // column 0
+  t1 = __builtin_amdgcn_perm(a23_lo, a01_lo, 0x07060302u);             // column 1
+  t2 = __builtin_amdgcn_perm(a23_hi, a01_hi, 0x05040100u);             // column 2
+  t3 = __builtin_amdgcn_perm(a23_hi, a01_hi, 0x07060302u);             // column 3
+}
+
+// binary32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// One v_mfma_f32_16x16x128_f8f6f4: c + a . b with FP8 operands, format codes
+// 0 = E4M3 (fp8), 1 = E5M2 (bf8) per operand; zero scale operands select the
+// unscaled instruction.
+template <int AF, int BF>
+__device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, 0, 0, 0);
+}
+
 }  // namespace fp8lin

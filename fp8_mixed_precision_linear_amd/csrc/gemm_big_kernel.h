@@ -51,8 +51,6 @@ namespace fp8lin {
 
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 128;
@@ -68,11 +66,6 @@ constexpr int GROUP_M = 8;
 constexpr uint32_t kOOB = 0x7FFFFFF0u;   // a buffer offset past any operand
 constexpr int kRsrcWord3 = 0x00020000;
 
-template <int AF, int BF>
-__device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, 0, 0, 0);
-}
-
 // The same instruction with per-lane E8M0 block scales: lane l of operand
 // `a` holds one row and applies 2^(sa - 127) to it, likewise for `b`.
 template <int AF, int BF>
@@ -82,13 +75,6 @@ __device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, const v4f& c,
 
 // E8M0 code of a power of two 2^e (|e| <= 126): its binary32 exponent field.
 __device__ __forceinline__ int e8m0_of(float pow2) { return (int)(__float_as_uint(pow2) >> 23) & 0xFF; }
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
-}
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -151,6 +137,12 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
   __shared__ float su_tab[NWAVES][MAX_KB];
   constexpr bool ROWS = !BLOCK && SA_ROWS && SB_COL;
+  // The next stage's DMA goes out right after the end-of-step barrier
+  // (a full step of latency before its wait) in the kernels without block
+  // promotion; with promotion the longer-lived DMA addresses push the
+  // kernel past 256 registers (measured: spills), so there it goes out
+  // after the step's first fragment reads.
+  constexpr bool EARLY_DMA = !BLOCK && !OUT8;
   // per-row scales of the tile's 256 D rows and 256 D columns, staged once
   // (rows clamped into D for edge tiles); read in the epilogue
   __shared__ float rs_tab[ROWS ? BM + BN : 1];
@@ -276,7 +268,8 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     v8i bfr[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) bfr[j] = frag(Bs, wn * WTN + 16 * j + l16, g);
-    if (kb > 0 && kb + 1 < nk) load_stage(kb + 1, lds[stage ^ 1]);
+    if constexpr (!EARLY_DMA)
+      if (kb > 0 && kb + 1 < nk) load_stage(kb + 1, lds[stage ^ 1]);
 
     // The MFMA takes B as its first operand, so each 16x16 result tile is
     // the transpose of the D tile: lane (g, l16) holds D row 16*i + l16,
@@ -378,6 +371,10 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    // every wavefront is past its reads of this stage: the step after next
+    // loads into it now, a whole step before it is needed
+    if constexpr (EARLY_DMA)
+      if (kb + 2 < nk) load_stage(kb + 2, lds[stage]);
   }
 
   // ---- epilogue.  Lane (g, l16) holds, for each (i, j), D row 16*i + l16,

@@ -35,25 +35,8 @@ namespace fp8lin {
 
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
 constexpr int kThreads = 256;
 constexpr int BM = 128, BN = 128, BK = 128;
-
-template <int AF, int BF>
-__device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
-  // format codes: 0 = E4M3 (fp8), 1 = E5M2 (bf8); zero scale operands select
-  // the unscaled instruction.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x40u);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
-}
 
 __device__ __forceinline__ float scale_at(int scaling, const float* __restrict__ s, int64_t rows,
                                           int64_t row, int64_t kb) {
