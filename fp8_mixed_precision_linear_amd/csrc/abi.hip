@@ -20,7 +20,8 @@ inline fp8_status launched(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8
 
 fp8_status cast_common(const void* x, int64_t rows, int64_t cols, const float* scale, uint8_t* y,
                        uint8_t* y_t, float* amax_out, int fmt, int sr, uint64_t seed,
-                       uint64_t offset, hipStream_t stream, int amax_acc = 0) {
+                       uint64_t offset, hipStream_t stream, int amax_acc = 0,
+                       uint64_t* rng = nullptr, uint64_t advance = 0) {
   if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
   const bool empty = rows == 0 || cols == 0;
   if (!empty && (x == nullptr || scale == nullptr || (y == nullptr && y_t == nullptr)))
@@ -28,7 +29,7 @@ fp8_status cast_common(const void* x, int64_t rows, int64_t cols, const float* s
   if (!aligned16(x) || !aligned16(y) || !aligned16(y_t)) return FP8_ERR_ALIGN;
   if (amax_out && !aligned4(amax_out)) return FP8_ERR_ALIGN;
   return launched(launch_cast(static_cast<const uint16_t*>(x), rows, cols, scale, fmt, y, y_t,
-                              amax_out, amax_acc, sr, seed, offset, stream));
+                              amax_out, amax_acc, sr, seed, offset, rng, advance, stream));
 }
 
 }  // namespace
@@ -165,6 +166,16 @@ fp8_status fp8_cast_sr(const void* x_bf16, int64_t rows, int64_t cols, fp8_forma
                        uint8_t* y_t, float* amax_out, hipStream_t stream) {
   if (!fmt_ok(fmt)) return FP8_ERR_ARG;
   return cast_common(x_bf16, rows, cols, scale, y, y_t, amax_out, fmt, 1, seed, offset, stream);
+}
+
+fp8_status fp8_cast_sr_state(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                             const float* scale, uint64_t* rng_state, uint64_t advance,
+                             uint8_t* y, uint8_t* y_t, float* amax_out, hipStream_t stream) {
+  if (!fmt_ok(fmt)) return FP8_ERR_ARG;
+  if (rng_state == nullptr) return FP8_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(rng_state) & 7u) != 0) return FP8_ERR_ALIGN;
+  return cast_common(x_bf16, rows, cols, scale, y, y_t, amax_out, fmt, 1, 0, 0, stream, 0,
+                     rng_state, advance);
 }
 
 fp8_status fp8_amax_ewma_update(float* ewma, int64_t n, const float* amax_new, float beta,

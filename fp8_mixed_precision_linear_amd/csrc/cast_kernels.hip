@@ -54,7 +54,9 @@ template <int FMT, bool AMAX, bool SR>
 __global__ void __launch_bounds__(kBig)
     k_cast_flat(const uint16_t* __restrict__ x, int64_t n, const float* __restrict__ scale,
                 uint8_t* __restrict__ y, float* __restrict__ amax, uint64_t seed,
-                uint64_t offset) {
+                uint64_t offset, const uint64_t* __restrict__ rng) {
+  if constexpr (SR)
+    if (rng) { seed = rng[0]; offset = rng[1]; }
   const float s = *scale;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint4* yv = reinterpret_cast<uint4*>(y);
@@ -103,27 +105,15 @@ __global__ void __launch_bounds__(kBig)
 // chunks of 16 rows); chunk ch of line c sits at physical chunk
 // ch ^ ((c/16) & 7).
 // ---------------------------------------------------------------------
-__device__ __forceinline__ void transpose4x4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
-                                             uint32_t& t0, uint32_t& t1, uint32_t& t2,
-                                             uint32_t& t3) {
-  // wK holds bytes [r=K][c=0..3]; tJ gets bytes [r=0..3][c=J].
-  // __builtin_amdgcn_perm(hi, lo, sel): selector bytes 0-3 pick lo, 4-7 hi.
-  uint32_t a01_lo = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // r0c0 r1c0 r0c1 r1c1
-  uint32_t a01_hi = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // r0c2 r1c2 r0c3 r1c3
-  uint32_t a23_lo = __builtin_amdgcn_perm(w3, w2, 0x05010400u);  // r2c0 r3c0 r2c1 r3c1
-  uint32_t a23_hi = __builtin_amdgcn_perm(w3, w2, 0x07030602u);  // r2c2 r3c2 r2c3 r3c3
-  t0 = __builtin_amdgcn_perm(a23_lo, a01_lo, 0x05040100u);       // r0c0 r1c0 r2c0 r3c0
-  t1 = __builtin_amdgcn_perm(a23_lo, a01_lo, 0x07060302u);       // c1
-  t2 = __builtin_amdgcn_perm(a23_hi, a01_hi, 0x05040100u);       // c2
-  t3 = __builtin_amdgcn_perm(a23_hi, a01_hi, 0x07060302u);       // c3
-}
-
 template <int FMT, bool AMAX, bool WANT_Y, bool SR>
 __global__ void __launch_bounds__(kBig)
     k_cast_transpose(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                      const float* __restrict__ scale, uint8_t* __restrict__ y,
                      uint8_t* __restrict__ yt, float* __restrict__ amax, int tiles_c,
-                     int ntiles, uint64_t seed, uint64_t offset) {
+                     int ntiles, uint64_t seed, uint64_t offset,
+                     const uint64_t* __restrict__ rng) {
+  if constexpr (SR)
+    if (rng) { seed = rng[0]; offset = rng[1]; }
   // four 256-thread groups, each on its own tile and 16 KB of LDS; the grid
   // walks the tiles row-major, four per workgroup per pass
   __shared__ __attribute__((aligned(16))) uint8_t lds_all[4][128 * 128];
@@ -209,7 +199,9 @@ __global__ void __launch_bounds__(kThreads)
     k_cast_generic(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                    const float* __restrict__ scale, uint8_t* __restrict__ y,
                    uint8_t* __restrict__ yt, float* __restrict__ amax, uint64_t seed,
-                   uint64_t offset) {
+                   uint64_t offset, const uint64_t* __restrict__ rng) {
+  if constexpr (SR)
+    if (rng) { seed = rng[0]; offset = rng[1]; }
   const float s = *scale;
   const int64_t n = rows * cols;
   uint32_t m = 0;
@@ -230,10 +222,16 @@ __global__ void __launch_bounds__(kThreads)
   if (AMAX) block_amax_to<kThreads>(amax, m);
 }
 
+// The generator state of a stochastic-rounding cast that reads (seed,
+// offset) from device memory moves on by `adv` once the cast has read it.
+__global__ void k_rng_advance(uint64_t* rng, uint64_t adv) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) rng[1] += adv;
+}
+
 template <int FMT, bool AMAX, bool SR>
 hipError_t launch_cast_t(const uint16_t* x, int64_t rows, int64_t cols, const float* scale,
                          uint8_t* y, uint8_t* yt, float* amax, uint64_t seed, uint64_t offset,
-                         hipStream_t s) {
+                         const uint64_t* rng, hipStream_t s) {
   const int64_t n = rows * cols;
   const int64_t cus = device_cu_count();
   if (yt == nullptr) {
@@ -242,7 +240,7 @@ hipError_t launch_cast_t(const uint16_t* x, int64_t rows, int64_t cols, const fl
     if (blocks > cus) blocks = cus;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL((k_cast_flat<FMT, AMAX, SR>), dim3((unsigned)blocks), dim3(kBig), 0, s, x,
-                       n, scale, y, amax, seed, offset);
+                       n, scale, y, amax, seed, offset, rng);
     return hipGetLastError();
   }
   if (rows % 16 == 0 && cols % 16 == 0 && (rows + 127) / 128 * ((cols + 127) / 128) < (1LL << 30)) {
@@ -253,17 +251,17 @@ hipError_t launch_cast_t(const uint16_t* x, int64_t rows, int64_t cols, const fl
     if (y)
       hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, true, SR>), dim3((unsigned)blocks),
                          dim3(kBig), 0, s, x, rows, cols, scale, y, yt, amax, tiles_c, ntiles,
-                         seed, offset);
+                         seed, offset, rng);
     else
       hipLaunchKernelGGL((k_cast_transpose<FMT, AMAX, false, SR>), dim3((unsigned)blocks),
                          dim3(kBig), 0, s, x, rows, cols, scale, y, yt, amax, tiles_c, ntiles,
-                         seed, offset);
+                         seed, offset, rng);
     return hipGetLastError();
   }
   int64_t blocks = (n + kThreads - 1) / kThreads;
   if (blocks > cus) blocks = cus;
   hipLaunchKernelGGL((k_cast_generic<FMT, AMAX, SR>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                     x, rows, cols, scale, y, yt, amax, seed, offset);
+                     x, rows, cols, scale, y, yt, amax, seed, offset, rng);
   return hipGetLastError();
 }
 
@@ -271,23 +269,32 @@ hipError_t launch_cast_t(const uint16_t* x, int64_t rows, int64_t cols, const fl
 
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, const float* scale, int fmt,
                        uint8_t* y, uint8_t* y_t, float* amax, int amax_acc, int sr, uint64_t seed,
-                       uint64_t offset, hipStream_t s) {
+                       uint64_t offset, uint64_t* rng, uint64_t advance, hipStream_t s) {
   if (amax && !amax_acc) {
     hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 1, 0u, s);
     if (e != hipSuccess) return e;
   }
-  if (rows == 0 || cols == 0) return hipSuccess;
-  const int key = fmt * 4 + (amax ? 2 : 0) + (sr ? 1 : 0);
-  switch (key) {
-    case 0: return launch_cast_t<0, false, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
-    case 1: return launch_cast_t<0, false, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
-    case 2: return launch_cast_t<0, true, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
-    case 3: return launch_cast_t<0, true, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
-    case 4: return launch_cast_t<1, false, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
-    case 5: return launch_cast_t<1, false, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
-    case 6: return launch_cast_t<1, true, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
-    default: return launch_cast_t<1, true, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, s);
+  hipError_t e = hipSuccess;
+  if (rows != 0 && cols != 0) {
+    const int key = fmt * 4 + (amax ? 2 : 0) + (sr ? 1 : 0);
+    const uint64_t* r = rng;
+    switch (key) {
+      case 0: e = launch_cast_t<0, false, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, r, s); break;
+      case 1: e = launch_cast_t<0, false, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, r, s); break;
+      case 2: e = launch_cast_t<0, true, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, r, s); break;
+      case 3: e = launch_cast_t<0, true, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, r, s); break;
+      case 4: e = launch_cast_t<1, false, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, r, s); break;
+      case 5: e = launch_cast_t<1, false, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, r, s); break;
+      case 6: e = launch_cast_t<1, true, false>(x, rows, cols, scale, y, y_t, amax, seed, offset, r, s); break;
+      default: e = launch_cast_t<1, true, true>(x, rows, cols, scale, y, y_t, amax, seed, offset, r, s); break;
+    }
+    if (e != hipSuccess) return e;
   }
+  if (rng && advance) {   // after the cast has read the state (stream order)
+    hipLaunchKernelGGL(k_rng_advance, dim3(1), dim3(64), 0, s, rng, advance);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace fp8lin

@@ -35,10 +35,12 @@ hipError_t launch_ewma_update(float* ewma, int64_t n, const float* amax_new, flo
 
 // Per-tensor cast with optional transpose and amax (zeroed here first when
 // given, unless amax_acc: then max-accumulated into its current value);
-// sr != 0: stochastic rounding with Philox words from (seed, offset).
+// sr != 0: stochastic rounding with Philox words from (seed, offset), or,
+// when rng is given, from (rng[0], rng[1]) read on the device, after which
+// rng[1] is advanced by `advance`.
 hipError_t launch_cast(const uint16_t* x, int64_t rows, int64_t cols, const float* scale, int fmt,
                        uint8_t* y, uint8_t* y_t, float* amax, int amax_acc, int sr, uint64_t seed,
-                       uint64_t offset, hipStream_t s);
+                       uint64_t offset, uint64_t* rng, uint64_t advance, hipStream_t s);
 
 // Block-wise cast (tile: 1 = 1x128, 2 = 128x128; pow2: power-of-two scales).
 hipError_t launch_cast_block(const uint16_t* x, int64_t rows, int64_t cols, int fmt, int tile,

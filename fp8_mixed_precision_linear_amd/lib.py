@@ -67,6 +67,7 @@ def _load():
         "fp8_cast_block_pow2": (i32, [vp, i64, i64, i32, i32, vp, vp, vp, vp, vp]),
         "fp8_cast_rowwise": (i32, [vp, i64, i64, i32, vp, vp, vp, vp, vp]),
         "fp8_cast_sr": (i32, [vp, i64, i64, i32, vp, C.c_uint64, C.c_uint64, vp, vp, vp, vp]),
+        "fp8_cast_sr_state": (i32, [vp, i64, i64, i32, vp, vp, C.c_uint64, vp, vp, vp, vp]),
         "fp8_amax_ewma_update": (i32, [vp, i64, vp, C.c_float, i32, i32, vp, vp, vp]),
         "fp8_scaled_gemm": (i32, [C.POINTER(GemmArgs), vp]),
     }
@@ -117,6 +118,7 @@ def _stream(stream):
 
 _BF16 = (torch.bfloat16,)
 _F32 = (torch.float32,)
+_I64 = (torch.int64,)
 _U8 = (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2)
 
 
@@ -232,6 +234,22 @@ def fp8_cast_sr(x, fmt, scale, seed, offset=0, y=None, y_t=None, amax_out=None, 
            _L.fp8_cast_sr(_ptr(x, _BF16, "x"), rows, cols, fmt, _ptr(scale, _F32, "scale"),
                           int(seed), int(offset), _ptr(y, _U8, "y"), _ptr(y_t, _U8, "y_t"),
                           _ptr(amax_out, _F32, "amax_out"), _stream(stream)))
+
+
+def fp8_cast_sr_state(x, fmt, scale, rng_state, advance=1, y=None, y_t=None, amax_out=None,
+                      stream=None):
+    """Stochastic-rounding cast whose (seed, offset) are read on the device
+    from rng_state (an int64 tensor of 2: seed, offset, as unsigned 64-bit
+    words); rng_state[1] then moves on by `advance` in stream order, so a
+    replayed graph draws fresh words each time."""
+    rows, cols = _cast_sizes(x, scale, y, y_t, amax_out)
+    if rng_state.numel() < 2:
+        raise ValueError("rng_state needs 2 elements (seed, offset)")
+    _check("fp8_cast_sr_state",
+           _L.fp8_cast_sr_state(_ptr(x, _BF16, "x"), rows, cols, fmt, _ptr(scale, _F32, "scale"),
+                                _ptr(rng_state, _I64, "rng_state"), int(advance),
+                                _ptr(y, _U8, "y"), _ptr(y_t, _U8, "y_t"),
+                                _ptr(amax_out, _F32, "amax_out"), _stream(stream)))
 
 
 def fp8_amax_ewma_update(ewma, amax_new, beta, fmt, margin, scale, scale_inv, stream=None):

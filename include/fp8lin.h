@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 6
+#define FP8LIN_ABI_VERSION 7
 
 /* [MPG] "The precision formats", "FP8 E4M3", "FP8 E5M2": E4M3 = 4 exponent
  * and 3 mantissa bits, range about 2^-9..448; E5M2 = 5 and 2, range about
@@ -259,9 +259,9 @@ fp8_status fp8_cast_amax_acc(const void* x_bf16, int64_t rows, int64_t cols, fp8
  * (row-major index) is word i % 4 of Philox4x32-10 (Salmon et al., SC 2011)
  * with counter (i / 4 low, i / 4 high, offset low, offset high) and key
  * (seed low, seed high); y_t holds the same codes transposed.  Calls with the
- * same (seed, offset) repeat the same draw: advance offset by at least
- * ceil(rows * cols / 4) per call for fresh words (the values are baked into
- * a captured graph).
+ * same (seed, offset) repeat the same draw; a call with another offset draws
+ * fresh words (the offset is its own pair of counter words).  The values are
+ * baked into a captured graph: see fp8_cast_sr_state.
  *   fmt        FP8_E4M3 or FP8_E5M2.
  *   Other arguments, layouts and errors as fp8_cast_e4m3, plus FP8_ERR_ARG
  *   (fmt).
@@ -269,6 +269,26 @@ fp8_status fp8_cast_amax_acc(const void* x_bf16, int64_t rows, int64_t cols, fp8
 fp8_status fp8_cast_sr(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
                        const float* scale, uint64_t seed, uint64_t offset, uint8_t* y,
                        uint8_t* y_t, float* amax_out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_cast_sr_state -- fp8_cast_sr with the generator state in device
+ * memory, for steps captured once and replayed.  [MPG] "Stochastic
+ * rounding": the rounding is unbiased only if every step draws fresh random
+ * words, which by-value (seed, offset) cannot give a replayed graph.
+ *   rng_state  2 x uint64 (device, 8-byte aligned, caller-owned): seed and
+ *              offset, read by the cast when it runs on the stream; the codes
+ *              equal fp8_cast_sr with those values.  Afterwards, in stream
+ *              order, rng_state[1] += advance (modulo 2^64).
+ *   advance    any nonzero value gives the next call fresh words: the offset
+ *              is its own pair of Philox counter words, distinct from the
+ *              element index; 0 repeats the draw.
+ *   Other arguments, layouts and errors as fp8_cast_sr, plus FP8_ERR_NULL
+ *   (rng_state) and FP8_ERR_ALIGN (rng_state not 8-byte aligned).  Calls on
+ *   one rng_state must be stream-ordered (concurrent calls race on it).
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_cast_sr_state(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                             const float* scale, uint64_t* rng_state, uint64_t advance,
+                             uint8_t* y, uint8_t* y_t, float* amax_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * fp8_cast_block -- block-wise cast with per-tile scales computed on the fly.

@@ -28,7 +28,8 @@ def test_header_declares_the_layer_calls():
     for f in ["fp8_amax", "fp8_compute_scale", "fp8_amax_history_update", "fp8_cast_e4m3",
               "fp8_cast_e5m2", "fp8_cast_block", "fp8_scaled_gemm", "fp8_abi_version",
               "fp8_status_string", "fp8_compute_scale_pow2", "fp8_amax_history_update_pow2",
-              "fp8_cast_block_pow2", "fp8_cast_rowwise", "fp8_cast_sr", "fp8_amax_ewma_update"]:
+              "fp8_cast_block_pow2", "fp8_cast_rowwise", "fp8_cast_sr", "fp8_amax_ewma_update",
+              "fp8_cast_sr_state"]:
         assert f in fns
 
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.abi_version() == 6
+    assert L.abi_version() == 7
     for s in range(7):
         assert isinstance(L.status_string(s), str) and L.status_string(s)
     assert L.status_string(99) == "unknown status"
@@ -91,6 +92,13 @@ def test_host_validation_before_launch(L):
     assert f.fp8_cast_sr(x, 4, 4, 0, s, 1, 0, None, None, None, None) == 1
     assert f.fp8_cast_sr(x, 4, 4, 1, s, 1, 0, C.c_void_p(0x2004), None, None, None) == 3
     assert f.fp8_cast_sr(x, -4, 4, 1, s, 1, 0, y, None, None, None) == 2
+    # the same with device generator state: bad format, missing or misaligned state
+    g = C.c_void_p(0x6000)
+    assert f.fp8_cast_sr_state(x, 4, 4, 2, s, g, 1, y, None, None, None) == 6
+    assert f.fp8_cast_sr_state(x, 4, 4, 1, s, None, 1, y, None, None, None) == 1
+    assert f.fp8_cast_sr_state(x, 4, 4, 1, s, C.c_void_p(0x6004), 1, y, None, None, None) == 3
+    assert f.fp8_cast_sr_state(x, 4, 4, 1, s, g, 1, None, None, None, None) == 1
+    assert f.fp8_cast_sr_state(x, -4, 4, 1, s, g, 1, y, None, None, None) == 2
     a = C.c_void_p(0x5000)
     # accumulating cast: bad format, missing amax slot or outputs, misaligned slot
     assert f.fp8_cast_amax_acc(x, 4, 4, 2, s, y, None, a, None) == 6

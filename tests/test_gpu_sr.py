@@ -123,3 +123,73 @@ def test_ewma_update(O, L, beta, fmt, margin):
         assert np.array_equal(bits(ed.cpu().numpy()), bits(e)), t
         assert np.array_equal(bits(sd.cpu().numpy()), bits(s)), t
         assert np.array_equal(bits(sid.cpu().numpy()), bits(si)), t
+
+
+# ------------------------------------------- generator state on the device ---
+def _state(seed, offset):
+    """int64 tensor holding two unsigned 64-bit words (seed, offset)."""
+    w = np.array([seed, offset], np.uint64).view(np.int64)
+    return torch.from_numpy(w.copy()).cuda()
+
+
+@pytest.mark.parametrize("shape", [(256, 384), (33, 17), (4096, 4096)])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_cast_sr_state_equals_by_value_call(O, L, shape, fmt):
+    """Seed and offset read on the device give the codes of the by-value
+    call (every kernel path), and the offset then moves on by `advance`."""
+    rows, cols = shape
+    say("cast_sr_state", shape, fmt)
+    rng = np.random.default_rng(rows + 3 * cols + fmt)
+    x = datagen.normal(rng, shape, 1e-3)
+    s = 448.0 / 4e-3 if fmt == 0 else 57344.0 / 4e-3
+    seed, offset = 0xDEADBEEF12345678, (1 << 40) + 7
+    want_y, want_t, want_am = run_sr(L, x, fmt, s, seed, offset, want_y=True, want_t=True, amax=True)
+    st = _state(seed, offset)
+    y, yt, am = Guarded(shape, torch.uint8), Guarded(shape[::-1], torch.uint8), Guarded((1,), torch.float32)
+    L.fp8_cast_sr_state(dev_bf16(x), fmt, dev(np.array([s], np.float32)), st, 5,
+                        y=y.t, y_t=yt.t, amax_out=am.t)
+    torch.cuda.synchronize()
+    for g in (y, yt, am):
+        g.check()
+    assert np.array_equal(y.np(), want_y) and np.array_equal(yt.np(), want_t)
+    assert bits(am.np()[0]) == bits(want_am)
+    got = st.cpu().numpy().view(np.uint64)
+    assert int(got[0]) == seed and int(got[1]) == offset + 5
+    if rows * cols <= 1 << 17:   # the oracle on the small shapes
+        ry, _ = O.cast_sr(x, np.float32(s), fmt, seed, offset, want_y=True)
+        assert np.array_equal(y.np(), ry)
+
+
+def test_cast_sr_state_graph_replays_draw_fresh_words(O, L):
+    """One stochastic-rounding cast captured in a HIP graph and replayed
+    three times (host reads between replays): replay k uses offset0 + k,
+    each replay's codes equal the oracle's at that offset, and they differ."""
+    say("cast_sr_state graph")
+    rng = np.random.default_rng(5)
+    shape = (512, 768)
+    x = datagen.normal(rng, shape, 1e-3)
+    s = np.float32(57344.0 / 5e-3)
+    seed, off0 = 1234, 99
+    xd, sd = dev_bf16(x), dev(np.array([s], np.float32))
+    st = _state(seed, off0)
+    y = torch.empty(shape, dtype=torch.uint8, device="cuda")
+    yt = torch.empty(shape[::-1], dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.fp8_cast_sr_state(xd, 1, sd, st, 1, y=y, y_t=yt)
+    torch.cuda.synchronize()
+    st.copy_(_state(seed, off0))      # capture ran nothing; start from off0
+    torch.cuda.synchronize()
+    outs = []
+    for k in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        got, got_t = y.cpu().numpy(), yt.cpu().numpy()
+        ry, rt = O.cast_sr(x, s, 1, seed, off0 + k, want_y=True, want_t=True)
+        assert np.array_equal(got, ry), k
+        assert np.array_equal(got_t, rt), k
+        assert int(st.cpu().numpy().view(np.uint64)[1]) == off0 + k + 1
+        outs.append(got)
+    assert not np.array_equal(outs[0], outs[1]) and not np.array_equal(outs[1], outs[2])
+    del g
