@@ -1,54 +1,63 @@
 """Benchmark of the FP8 scaled linear layer on one MI355X.
 
-Workload (the measured step): delayed-scaling FP8 linear fwd + bwd, tokens
-4096, in 4096, out 4096, over 16 steps whose inputs are regenerated per step
-from seed + step (X ~ N(0,1), W ~ N(0,0.02), dY ~ N(0,1e-4), bf16), all
-resident in HBM before timing.  One step = the whole hot path:
-  cast X -> E4M3 (+transpose, +amax), cast W -> E4M3 (+transpose, +amax),
-  FWD GEMM (bf16 Y), cast dY -> E5M2 (+transpose, +amax), DGRAD GEMM (bf16
-  dX), WGRAD GEMM (fp32 dW), amax-history update (len 16, max) for X, W, dY.
-`value` = GEMM FLOPs of the step (3 x 2*4096^3) / measured step time, with
-the K timed steps captured once into a HIP graph and replayed (the eager
-per-call time is reported beside it as ms_per_step_eager).  The casts
-max-accumulate their amax into slots that the history update clears after
-reading them (fp8_cast_amax_acc, fp8_amax_history_update_reset); the same
-step with overwriting casts, each zeroing its slot with a fill kernel
-first, is reported as ms_per_step_overwrite_casts.
+Workload (the measured step): the transformer-block FP8 linear set at
+hidden 8192, FFN 28672, 8192 tokens -- QKV 8192 -> 10240, O 8192 -> 8192,
+gate and up 8192 -> 28672 each (one shared activation), down 28672 -> 8192 --
+forward, dgrad and wgrad of every linear, once in per-tensor delayed
+scaling and once in block-wise scaling.  One step runs both passes, so it
+covers the whole hot path: amax fused into the casts, scales from the amax
+histories, saturating RNE casts with fused transposes (per-tensor and
+block-wise), and the FWD / DGRAD / WGRAD GEMMs with FP32 accumulation,
+block-scale promotion and the dequantising epilogue.
+
+  delayed pass: per linear (forward order) cast X and W (E4M3, both
+    orientations, amax max-accumulated into the tensor's slot), FWD GEMM
+    (bf16 Y); per linear (backward order) cast dY (E5M2), DGRAD (bf16 dX),
+    WGRAD (fp32 dW); then the amax-history update (length 16, max) of all
+    14 tensors (two calls: E4M3 and E5M2), which also clears the slots;
+  block pass: the same with block-wise casts (X and dY 1x128 tiles in both
+    orientations, W 128x128 blocks with the transposed copy) and block
+    scales promoted per 128-wide K block in the GEMMs.
+
+Inputs are synthetic (seeded numpy PCG64, bf16) and resident in HBM before
+timing; warm-up steps fill the amax histories first.  `value` = GEMM FLOPs
+of one step (2 x 42.06 TFLOP) / measured step time, the K timed steps
+captured once into a HIP graph and replayed.
 
 Also reported (same JSON line):
-  roofline      -- the dominant kernel (the GEMMs), per-launch duration from
-                   HIP events around R launches captured in a HIP graph, on
-                   the stream the kernels run on;
-  kernels       -- per-kernel throughput, warm (R launches back to back in one
-                   graph, inputs left in the caches by the previous launch;
-                   GEMM TFLOP/s, cast GB/s of algorithmic bytes) for this workload (also dY's cast with
-                   stochastic rounding and the EWMA scale update), plus the forward
-                   GEMM with its output quantised in the epilogue (E4M3,
-                   transposed copy, amax) beside the unfused GEMM + cast;
-  kernels_cold  -- the step's GEMMs, casts and amax timed cold: a 512 MiB
-                   read evicts the 256 MB MALL before every launch (median
-                   of single launches);
-  rowwise       -- per-row (per-channel) scaling on the same shapes and data:
-                   row-wise casts into both orientations and the three GEMMs
-                   with per-row scales;
-  blockwise     -- the block-wise path on 8192 tokens x 4096 in x 14336 out:
-                   forward (1x128 activation tiles, 128x128 weight blocks)
-                   and backward (dgrad, wgrad with token-axis tiles), with
-                   binary32 block scales and with power-of-two ones, and
-                   the row-wise path on the same shapes;
-  cpu_baseline  -- the plain CPU oracle timed on a bounded sample of the
-                   same step (rank 0, N = 1 only).
+  c5            -- per pass and per linear: every launch of one eager step
+                   bracketed by HIP events on the library's stream (GEMM
+                   TFLOP/s, cast GB/s of algorithmic bytes);
+  roofline      -- the dominant kernel of the step (the GEMM kernel with the
+                   largest share of the step), achieved = its FLOPs per
+                   launch / its average launch duration from those events;
+                   traffic from the committed counter summary while the
+                   kernel sources are unchanged;
+  delayed4096, kernels, kernels_cold, rowwise, blockwise -- the smaller
+                   workloads (delayed-scaling fwd+bwd at 4096^3; per-kernel
+                   throughput warm and with the 256 MB last-level cache
+                   evicted before every launch; per-row scaling; the
+                   block-wise path at 8192 x 4096 x 14336);
+  cpu_baseline  -- the plain CPU oracle timed on a bounded sample of the step
+                   (rank 0, N = 1 only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--no-blockwise] [--no-graph] [--kernel-reps R]
+       [--no-extras] [--kernel-reps R]
+       python bench.py --traffic-run            (under rocprofv3 --pmc)
+       python bench.py --traffic-summarize DIR OUT.json
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -58,49 +67,301 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+C5_ORDER = ["qkv", "o", "gate", "up", "down"]
+C5_X = {"qkv": "qkv", "o": "o", "gate": "gate", "up": "gate", "down": "down"}
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemm_c5_traffic.json")
+TRAFFIC_SOURCES = ("csrc/gemm_big_kernel.h", "csrc/gemm_big.hip", "csrc/fp8_device.h")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=32)
-    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-blockwise", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline step (no 4096^3 / 8192x4096x14336 extras)")
     ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--no-graph", action="store_true",
-                    help="time the eager launches only (default: the K steps are captured "
-                         "into one HIP graph and replayed)")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="run the step's GEMMs and a copy of known size (for rocprofv3 --pmc)")
+    ap.add_argument("--traffic-summarize", nargs=2, metavar=("DIR", "OUT"))
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the FP8 linear path here has no multi-GPU "
-              "(sharded) mode; run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+# ----------------------------------------------------------------------------
+# the transformer-block linear set
+# ----------------------------------------------------------------------------
+class C5Set:
+    """Device tensors of the five linears (inputs, FP8 operands in both
+    orientations, outputs, delayed-scaling state and block scales) and the
+    launches of one step, as (label, kind, work, fn) with kind gemm (work =
+    FLOPs) or cast / state (work = algorithmic bytes)."""
 
-    import torch
-    from fp8_mixed_precision_linear_amd import datagen
-    from fp8_mixed_precision_linear_amd import lib as L
+    def __init__(self, torch, L, datagen, dev):
+        self.torch, self.L = torch, L
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
+        def d_bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
+        self.shapes = {n: datagen.C5_LINEARS[n] for n in C5_ORDER}
+        T = 8192
+        self.T = T
+        t0 = time.time()
+        self.x, self.w, self.dy = {}, {}, {}
+        for n in C5_ORDER:
+            parts = ("x", "w", "dy") if C5_X[n] == n else ("w", "dy")
+            d = datagen.config5_linear(n, parts=parts)
+            if "x" in d:
+                self.x[n] = d_bf16(d["x"])
+            self.w[n] = d_bf16(d["w"])
+            self.dy[n] = d_bf16(d["dy"])
+            del d
+        self.gen_s = time.time() - t0
+        # FP8 operands (shared by both passes), outputs
+        self.xq, self.xtq = {}, {}
+        for n in self.x:
+            di = self.shapes[n][0]
+            self.xq[n], self.xtq[n] = torch.empty((T, di), **u8), torch.empty((di, T), **u8)
+        self.wq, self.wtq, self.dyq, self.dytq, self.y, self.dx, self.dw = ({} for _ in range(7))
+        for n in C5_ORDER:
+            di, do = self.shapes[n]
+            self.wq[n], self.wtq[n] = torch.empty((di, do), **u8), torch.empty((do, di), **u8)
+            self.dyq[n], self.dytq[n] = torch.empty((T, do), **u8), torch.empty((do, T), **u8)
+            self.y[n] = torch.empty((T, do), **bf)
+            self.dx[n] = torch.empty((T, di), **bf)
+            self.dw[n] = torch.empty((di, do), **f32)
+        # delayed-scaling state: E4M3 tensors first (X of 4 inputs, W of 5
+        # linears), then E5M2 (dY of 5 linears); one amax slot per tensor
+        xs = list(self.x)
+        self.slot = {("x", n): i for i, n in enumerate(xs)}
+        for i, n in enumerate(C5_ORDER):
+            self.slot[("w", n)] = len(xs) + i
+            self.slot[("dy", n)] = len(xs) + len(C5_ORDER) + i
+        self.n_e4m3 = len(xs) + len(C5_ORDER)
+        nt = self.n_e4m3 + len(C5_ORDER)
+        self.hist = torch.zeros((nt, 16), **f32)
+        self.scale = torch.ones(nt, **f32)
+        self.sinv = torch.ones(nt, **f32)
+        self.amax = torch.zeros(nt, **f32)
+        # block scales
+        self.sx, self.sxt, self.sw, self.swt, self.sd, self.sdt = ({} for _ in range(6))
+        for n in xs:
+            di = self.shapes[n][0]
+            self.sx[n] = torch.empty((di // 128, T), **f32)
+            self.sxt[n] = torch.empty((T // 128, di), **f32)
+        for n in C5_ORDER:
+            di, do = self.shapes[n]
+            self.sw[n] = torch.empty((do // 128, di // 128), **f32)
+            self.swt[n] = torch.empty((di // 128, do // 128), **f32)
+            self.sd[n] = torch.empty((do // 128, T), **f32)
+            self.sdt[n] = torch.empty((T // 128, do), **f32)
+        self.ops = {"delayed": self._delayed_ops(), "block": self._block_ops()}
+
+    def flops_per_pass(self):
+        return sum(3 * 2.0 * self.T * di * do for di, do in self.shapes.values())
+
+    def _delayed_ops(self):
+        L, T, s, si, am = self.L, self.T, self.scale, self.sinv, self.amax
+        ops = []
+
+        def sl(key):
+            i = self.slot[key]
+            return i, i + 1
+
+        for n in C5_ORDER:
+            di, do = self.shapes[n]
+            xn = C5_X[n]
+            xa, xb = sl(("x", xn))
+            wa, wb = sl(("w", n))
+            if xn == n:
+                ops.append((f"delayed cast X {n}", "cast", 4.0 * T * di,
+                            lambda xn=xn, xa=xa, xb=xb: L.fp8_cast_amax_acc(
+                                self.x[xn], 0, s[xa:xb], am[xa:xb], y=self.xq[xn], y_t=self.xtq[xn])))
+            ops.append((f"delayed cast W {n}", "cast", 4.0 * di * do,
+                        lambda n=n, wa=wa, wb=wb: L.fp8_cast_amax_acc(
+                            self.w[n], 0, s[wa:wb], am[wa:wb], y=self.wq[n], y_t=self.wtq[n])))
+            ops.append((f"delayed fwd {n}", "gemm", 2.0 * T * di * do,
+                        lambda n=n, xn=xn, xa=xa, xb=xb, wa=wa, wb=wb: L.fp8_scaled_gemm(
+                            self.xq[xn], 0, 0, si[xa:xb], self.wtq[n], 0, 0, si[wa:wb], self.y[n])))
+        for n in reversed(C5_ORDER):
+            di, do = self.shapes[n]
+            xn = C5_X[n]
+            xa, xb = sl(("x", xn))
+            wa, wb = sl(("w", n))
+            da, db = sl(("dy", n))
+            ops.append((f"delayed cast dY {n}", "cast", 4.0 * T * do,
+                        lambda n=n, da=da, db=db: L.fp8_cast_amax_acc(
+                            self.dy[n], 1, s[da:db], am[da:db], y=self.dyq[n], y_t=self.dytq[n])))
+            ops.append((f"delayed dgrad {n}", "gemm", 2.0 * T * di * do,
+                        lambda n=n, wa=wa, wb=wb, da=da, db=db: L.fp8_scaled_gemm(
+                            self.dyq[n], 1, 0, si[da:db], self.wq[n], 0, 0, si[wa:wb], self.dx[n])))
+            ops.append((f"delayed wgrad {n}", "gemm", 2.0 * T * di * do,
+                        lambda n=n, xn=xn, xa=xa, xb=xb, da=da, db=db: L.fp8_scaled_gemm(
+                            self.xtq[xn], 0, 0, si[xa:xb], self.dytq[n], 1, 0, si[da:db], self.dw[n])))
+        e = self.n_e4m3
+        ops.append(("delayed history E4M3", "state", 8.0 * 16 * e,
+                    lambda: L.fp8_amax_history_update_reset(self.hist[0:e], am[0:e], 0, 0, 0,
+                                                            s[0:e], si[0:e])))
+        ops.append(("delayed history E5M2", "state", 8.0 * 16 * (len(self.scale) - e),
+                    lambda: L.fp8_amax_history_update_reset(self.hist[e:], am[e:], 1, 0, 0,
+                                                            s[e:], si[e:])))
+        return ops
+
+    def _block_ops(self):
+        L, T = self.L, self.T
+        ops = []
+        for n in C5_ORDER:
+            di, do = self.shapes[n]
+            xn = C5_X[n]
+            if xn == n:
+                ops.append((f"block cast X {n}", "cast", T * di * (4 + 8 / 128),
+                            lambda xn=xn: L.fp8_cast_block(self.x[xn], 0, 1, self.xq[xn], self.sx[xn],
+                                                           self.xtq[xn], self.sxt[xn])))
+            ops.append((f"block cast W {n}", "cast", di * do * (4 + 8 / 16384),
+                        lambda n=n: L.fp8_cast_block(self.w[n], 0, 2, self.wq[n], self.sw[n],
+                                                     self.wtq[n], self.swt[n])))
+            ops.append((f"block fwd {n}", "gemm", 2.0 * T * di * do,
+                        lambda n=n, xn=xn: L.fp8_scaled_gemm(self.xq[xn], 0, 1, self.sx[xn],
+                                                             self.wtq[n], 0, 2, self.swt[n], self.y[n])))
+        for n in reversed(C5_ORDER):
+            di, do = self.shapes[n]
+            xn = C5_X[n]
+            ops.append((f"block cast dY {n}", "cast", T * do * (4 + 8 / 128),
+                        lambda n=n: L.fp8_cast_block(self.dy[n], 1, 1, self.dyq[n], self.sd[n],
+                                                     self.dytq[n], self.sdt[n])))
+            ops.append((f"block dgrad {n}", "gemm", 2.0 * T * di * do,
+                        lambda n=n: L.fp8_scaled_gemm(self.dyq[n], 1, 1, self.sd[n], self.wq[n], 0, 2,
+                                                      self.sw[n], self.dx[n])))
+            ops.append((f"block wgrad {n}", "gemm", 2.0 * T * di * do,
+                        lambda n=n, xn=xn: L.fp8_scaled_gemm(self.xtq[xn], 0, 1, self.sxt[xn],
+                                                             self.dytq[n], 1, 1, self.sdt[n],
+                                                             self.dw[n])))
+        return ops
+
+    def step(self):
+        for mode in ("delayed", "block"):
+            for _, _, _, fn in self.ops[mode]:
+                fn()
+
+    def timed_eager_step(self, stream):
+        """One step with HIP events around every launch (on the library's
+        stream); returns [(label, kind, work, seconds)]."""
+        torch = self.torch
+        evs = []
+        for mode in ("delayed", "block"):
+            for lab, kind, work, fn in self.ops[mode]:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                evs.append((lab, kind, work, a, b))
+        torch.cuda.synchronize()
+        return [(lab, kind, work, a.elapsed_time(b) * 1e-3) for lab, kind, work, a, b in evs]
+
+
+# GEMM kernel (instantiation) of each pass: the dominant-kernel roofline is
+# taken over the launches of one kernel
+C5_KERNEL = {
+    "delayed fwd": "k_gemm_big<0, 0, false, false, false, false, false>",
+    "delayed dgrad": "k_gemm_big<1, 0, false, false, false, false, false>",
+    "delayed wgrad": "k_gemm_big<0, 1, false, false, false, false, false>",
+    "block fwd": "k_gemm_big<0, 0, true, true, false, false, false>",
+    "block dgrad": "k_gemm_big<1, 0, true, true, false, false, false>",
+    "block wgrad": "k_gemm_big<0, 1, true, true, true, false, false>",
+}
+
+
+def c5_summary(timed):
+    """Per-pass and per-kernel aggregates of one eager step's launches."""
+    out = {"launches": {}}
+    for lab, kind, work, sec in timed:
+        e = {"us": round(sec * 1e6, 1)}
+        if kind == "gemm":
+            e["tflops"] = round(work / sec / 1e12, 1)
+            e["pct_fp8_peak"] = round(100 * work / sec / 1e12 / FP8_PEAK_TFLOPS, 2)
+        elif kind == "cast":
+            e["gbs"] = round(work / sec / 1e9, 1)
+            e["pct_hbm_peak"] = round(100 * work / sec / 1e9 / HBM_PEAK_GBS, 2)
+        out["launches"][lab] = e
+    for mode in ("delayed", "block"):
+        g = [(w, s) for lab, k, w, s in timed if lab.startswith(mode) and k == "gemm"]
+        c = [(w, s) for lab, k, w, s in timed if lab.startswith(mode) and k == "cast"]
+        o = [s for lab, k, w, s in timed if lab.startswith(mode) and k == "state"]
+        gw, gs = sum(w for w, _ in g), sum(s for _, s in g)
+        cw, cs = sum(w for w, _ in c), sum(s for _, s in c)
+        out[mode] = {"gemm_tflops": round(gw / gs / 1e12, 1), "gemm_ms": round(gs * 1e3, 3),
+                     "gemm_pct_fp8_peak": round(100 * gw / gs / 1e12 / FP8_PEAK_TFLOPS, 2),
+                     "cast_gbs": round(cw / cs / 1e9, 1), "cast_ms": round(cs * 1e3, 3),
+                     "cast_pct_hbm_peak": round(100 * cw / cs / 1e9 / HBM_PEAK_GBS, 2),
+                     "other_ms": round(sum(o) * 1e3, 3),
+                     "sum_of_launches_ms": round((gs + cs + sum(o)) * 1e3, 3)}
+    kern = {}
+    for cls, name in C5_KERNEL.items():
+        sel = [(w, s) for lab, k, w, s in timed if lab.startswith(cls + " ")]
+        w, s = sum(x for x, _ in sel), sum(y for _, y in sel)
+        kern[cls] = {"kernel": name, "launches": len(sel), "total_us": round(s * 1e6, 1),
+                     "avg_us": round(s / len(sel) * 1e6, 1), "flop_per_launch": w / len(sel),
+                     "tflops": round(w / s / 1e12, 1)}
+    out["gemm_kernels"] = kern
+    return out
+
+
+def bench_c5(args, torch, L, datagen, dev, stream):
+    c5 = C5Set(torch, L, datagen, dev)
+    print(f"# generated the linear set's inputs in {c5.gen_s:.1f}s", file=sys.stderr, flush=True)
+    for _ in range(max(1, args.warmup)):     # the first step fills the histories
+        c5.step()
+    torch.cuda.synchronize()
+    g = capture(torch, lambda: [c5.step() for _ in range(args.steps)])
+    g.replay()                               # first replay uploads the graph
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    g.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    del g
+    print(f"# C5 step {ms_step:.3f} ms (graph)", file=sys.stderr, flush=True)
+    timed = c5.timed_eager_step(stream)
+    summ = c5_summary(timed)
+    flops = 2 * c5.flops_per_pass()
+    cast_bytes = sum(w for mode in ("delayed", "block") for _, k, w, _ in c5.ops[mode] if k == "cast")
+    dom_cls = max(summ["gemm_kernels"], key=lambda k: summ["gemm_kernels"][k]["total_us"])
+    dom = summ["gemm_kernels"][dom_cls]
+    ach = dom["flop_per_launch"] / (dom["avg_us"] * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "kernel": f"{dom['kernel']} ({dom_cls}, 5 launches per step)",
+                "achieved": round(ach, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / FP8_PEAK_TFLOPS, 4),
+                "traffic": gemm_traffic(dom_cls)}
+    del c5
+    torch.cuda.empty_cache()
+    return {"ms_step": ms_step, "flops": flops, "cast_bytes": cast_bytes, "wall": wall,
+            "summary": summ, "roofline": roofline}
+
+
+# ----------------------------------------------------------------------------
+# extras: the 4096^3 delayed-scaling step, per-kernel timings, row-wise and
+# block-wise paths at the smaller sizes
+# ----------------------------------------------------------------------------
+def bench_extras(args, torch, L, datagen, dev, stream):
     def d_bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    T, DI, DO = 4096, 4096, 4096
+    T = DI = DO = 4096
     NSTEPS_DATA = 16
     t0 = time.time()
-    data = []
-    for t in range(NSTEPS_DATA):
-        s = datagen.config2_step(t)
-        data.append((d_bf16(s["x"]), d_bf16(s["w"]), d_bf16(s["dy"])))
-    print(f"# generated 16 steps of inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        steps = list(ex.map(datagen.config2_step, range(NSTEPS_DATA)))
+    data = [(d_bf16(s["x"]), d_bf16(s["w"]), d_bf16(s["dy"])) for s in steps]
+    del steps
+    print(f"# generated 16 steps of 4096^3 inputs in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
     u8 = dict(dtype=torch.uint8, device=dev)
     xq, xtq = torch.empty((T, DI), **u8), torch.empty((DI, T), **u8)
     wq, wtq = torch.empty((DI, DO), **u8), torch.empty((DO, DI), **u8)
@@ -113,9 +374,6 @@ def main():
     sinv = torch.ones(3, dtype=torch.float32, device=dev)
     amax = torch.zeros(3, dtype=torch.float32, device=dev)
 
-    # The casts max-accumulate their amax into the slots that the history
-    # update reads and then clears (amax starts at 0), so a step needs no
-    # zeroing kernel: 3 casts, 3 GEMMs, 2 history updates.
     def step(t):
         x, w, dyt = data[t % NSTEPS_DATA]
         L.fp8_cast_amax_acc(x, 0, scale[0:1], amax[0:1], y=xq, y_t=xtq)
@@ -127,65 +385,25 @@ def main():
         L.fp8_amax_history_update_reset(hist[0:2], amax[0:2], 0, 0, 0, scale[0:2], sinv[0:2])
         L.fp8_amax_history_update_reset(hist[2:3], amax[2:3], 1, 0, 0, scale[2:3], sinv[2:3])
 
-    # the same step with overwriting casts (each zeroes its amax slot with a
-    # fill kernel first) and the plain history update, for comparison; timed
-    # after the accumulating step's graph (it leaves the slots nonzero)
-    def step_overwrite(t):
-        x, w, dyt = data[t % NSTEPS_DATA]
-        L.fp8_cast_e4m3(x, scale[0:1], y=xq, y_t=xtq, amax_out=amax[0:1])
-        L.fp8_cast_e4m3(w, scale[1:2], y=wq, y_t=wtq, amax_out=amax[1:2])
-        L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y)
-        L.fp8_cast_e5m2(dyt, scale[2:3], y=dyq, y_t=dytq, amax_out=amax[2:3])
-        L.fp8_scaled_gemm(dyq, 1, 0, sinv[2:3], wq, 0, 0, sinv[1:2], dx)
-        L.fp8_scaled_gemm(xtq, 0, 0, sinv[0:1], dytq, 1, 0, sinv[2:3], dw)
-        L.fp8_amax_history_update(hist[0:2], amax[0:2], 0, 0, 0, scale[0:2], sinv[0:2])
-        L.fp8_amax_history_update(hist[2:3], amax[2:3], 1, 0, 0, scale[2:3], sinv[2:3])
-
-    for t in range(args.warmup):
+    for t in range(4):
         step(t)
     torch.cuda.synchronize()
-
-    # eager: one Python call per library entry point
+    nst = 32
+    g = capture(torch, lambda: [step(4 + t) for t in range(nst)])
+    g.replay()
+    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
-    for t in range(args.steps):
-        step(args.warmup + t)
+    g.replay()
     ev1.record(stream)
     torch.cuda.synchronize()
-    ms_step_eager = ev0.elapsed_time(ev1) / args.steps
+    ms_step = ev0.elapsed_time(ev1) / nst
+    del g
+    delayed4096 = {"workload": "delayed-scaling fwd+dgrad+wgrad, tokens 4096, in 4096, out 4096, "
+                               "16 steps of inputs regenerated per step (graph of 32 steps)",
+                   "ms_per_step": round(ms_step, 4),
+                   "tflops_incl_casts": round(3 * 2.0 * T * DI * DO / (ms_step * 1e-3) / 1e12, 2)}
 
-    # graph: the same K steps captured once into a HIP graph and replayed
-    # (no host launch cost; the GPU runs the identical kernel sequence)
-    ms_step_graph = None
-    ms_step_overwrite = None
-    wall = None
-    if not args.no_graph:
-        g = capture(torch, lambda: [step(args.warmup + t) for t in range(args.steps)])
-        g.replay()                      # warm-up replay (first launch uploads the graph)
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        ev0.record(stream)
-        g.replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        ms_step_graph = ev0.elapsed_time(ev1) / args.steps
-        del g
-        g = capture(torch, lambda: [step_overwrite(args.warmup + t) for t in range(args.steps)])
-        g.replay()
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        g.replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        ms_step_overwrite = ev0.elapsed_time(ev1) / args.steps
-        del g
-    ms_step = ms_step_graph if ms_step_graph is not None else ms_step_eager
-    gemm_flops = 3 * 2.0 * T * DI * DO
-    value = gemm_flops / (ms_step * 1e-3) / 1e12
-
-    # ---- per-kernel timing: R launches captured in a graph, one replay timed
-    # with HIP events on the stream the kernels run on
     def time_launch(fn, reps):
         g = capture(torch, lambda: [fn() for _ in range(reps)])
         g.replay()
@@ -196,7 +414,7 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         del g
-        return a.elapsed_time(b) / reps * 1e-3  # seconds per launch
+        return a.elapsed_time(b) / reps * 1e-3
 
     x0, w0, dy0 = data[0]
     R = args.kernel_reps
@@ -204,8 +422,6 @@ def main():
     k["gemm_fwd_tensor"] = time_launch(lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y), R)
     k["gemm_dgrad_tensor"] = time_launch(lambda: L.fp8_scaled_gemm(dyq, 1, 0, sinv[2:3], wq, 0, 0, sinv[1:2], dx), R)
     k["gemm_wgrad_tensor"] = time_launch(lambda: L.fp8_scaled_gemm(xtq, 0, 0, sinv[0:1], dytq, 1, 0, sinv[2:3], dw), R)
-    # the forward GEMM with its output quantised in the epilogue (E4M3 codes,
-    # transposed copy, amax): the next layer's cast+transpose+amax fused in
     y8, y8t = torch.empty((T, DO), **u8), torch.empty((DO, T), **u8)
     am8 = torch.zeros(1, dtype=torch.float32, device=dev)
     k["gemm_fwd_tensor_fp8out"] = time_launch(
@@ -213,7 +429,6 @@ def main():
                                   d_scale=scale[0:1], d_fmt=0, D_t=y8t), R)
     k["cast_transpose_amax_e4m3"] = time_launch(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq, y_t=xtq, amax_out=amax[0:1]), R)
     k["cast_transpose_amax_acc_e4m3"] = time_launch(lambda: L.fp8_cast_amax_acc(x0, 0, scale[0:1], amax[0:1], y=xq, y_t=xtq), R)
-    k["cast_transpose_amax_e5m2"] = time_launch(lambda: L.fp8_cast_e5m2(dy0, scale[2:3], y=dyq, y_t=dytq, amax_out=amax[2:3]), R)
     k["cast_transpose_amax_e5m2_sr"] = time_launch(
         lambda: L.fp8_cast_sr(dy0, 1, scale[2:3], 1234, 0, y=dyq, y_t=dytq, amax_out=amax[2:3]), R)
     k["cast_e4m3"] = time_launch(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq), R)
@@ -222,27 +437,18 @@ def main():
     ewma = torch.zeros(3, dtype=torch.float32, device=dev)
     k["ewma_update"] = time_launch(lambda: L.fp8_amax_ewma_update(ewma, amax, 0.9, 0, 0, scale, sinv), R)
     nel = T * DI
-    kernels = {
-        "gemm_fwd_tensor": {"tflops": 2.0 * T * DI * DO / k["gemm_fwd_tensor"] / 1e12, "us": k["gemm_fwd_tensor"] * 1e6},
-        "gemm_dgrad_tensor": {"tflops": 2.0 * T * DI * DO / k["gemm_dgrad_tensor"] / 1e12, "us": k["gemm_dgrad_tensor"] * 1e6},
-        "gemm_wgrad_tensor": {"tflops": 2.0 * T * DI * DO / k["gemm_wgrad_tensor"] / 1e12, "us": k["gemm_wgrad_tensor"] * 1e6},
-        "gemm_fwd_tensor_fp8out": {"tflops": 2.0 * T * DI * DO / k["gemm_fwd_tensor_fp8out"] / 1e12,
-                                   "us": k["gemm_fwd_tensor_fp8out"] * 1e6,
-                                   "us_unfused_equivalent": (k["gemm_fwd_tensor"] + k["cast_transpose_amax_e4m3"]) * 1e6},
-        "cast_transpose_amax_e4m3": {"gbs": 4.0 * nel / k["cast_transpose_amax_e4m3"] / 1e9, "us": k["cast_transpose_amax_e4m3"] * 1e6},
-        "cast_transpose_amax_acc_e4m3": {"gbs": 4.0 * nel / k["cast_transpose_amax_acc_e4m3"] / 1e9,
-                                         "us": k["cast_transpose_amax_acc_e4m3"] * 1e6},
-        "cast_transpose_amax_e5m2": {"gbs": 4.0 * nel / k["cast_transpose_amax_e5m2"] / 1e9, "us": k["cast_transpose_amax_e5m2"] * 1e6},
-        "cast_transpose_amax_e5m2_sr": {"gbs": 4.0 * nel / k["cast_transpose_amax_e5m2_sr"] / 1e9,
-                                        "us": k["cast_transpose_amax_e5m2_sr"] * 1e6},
-        "cast_e4m3": {"gbs": 3.0 * nel / k["cast_e4m3"] / 1e9, "us": k["cast_e4m3"] * 1e6},
-        "amax": {"gbs": 2.0 * nel / k["amax"] / 1e9, "us": k["amax"] * 1e6},
-        "history_update": {"us": k["history_update"] * 1e6},
-        "ewma_update": {"us": k["ewma_update"] * 1e6},
-    }
-    # ---- row-wise (per-channel) scaling on the same shapes: each operand
-    # cast once into both orientations (row scales, column scales), the
-    # three GEMMs with per-row scales applied in the epilogue
+    fl = 2.0 * T * DI * DO
+    kernels = {"note": "warm: R launches back to back in one HIP graph, one replay timed"}
+    for n in ("gemm_fwd_tensor", "gemm_dgrad_tensor", "gemm_wgrad_tensor", "gemm_fwd_tensor_fp8out"):
+        kernels[n] = {"tflops": round(fl / k[n] / 1e12, 2), "us": round(k[n] * 1e6, 2)}
+    kernels["gemm_fwd_tensor_fp8out"]["us_unfused_equivalent"] = round(
+        (k["gemm_fwd_tensor"] + k["cast_transpose_amax_e4m3"]) * 1e6, 2)
+    for n, bpe in (("cast_transpose_amax_e4m3", 4), ("cast_transpose_amax_acc_e4m3", 4),
+                   ("cast_transpose_amax_e5m2_sr", 4), ("cast_e4m3", 3), ("amax", 2)):
+        kernels[n] = {"gbs": round(bpe * nel / k[n] / 1e9, 1), "us": round(k[n] * 1e6, 2)}
+    kernels["history_update"] = {"us": round(k["history_update"] * 1e6, 2)}
+    kernels["ewma_update"] = {"us": round(k["ewma_update"] * 1e6, 2)}
+
     f32 = dict(dtype=torch.float32, device=dev)
     sxr, sxc = torch.empty(T, **f32), torch.empty(DI, **f32)
     swr, swc = torch.empty(DI, **f32), torch.empty(DO, **f32)
@@ -253,28 +459,16 @@ def main():
     k["gemm_fwd_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(xq, 0, 5, sxr, wtq, 0, 5, swc, y), R)
     k["gemm_dgrad_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(dyq, 1, 5, sdr, wq, 0, 5, swr, dx), R)
     k["gemm_wgrad_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(xtq, 0, 5, sxc, dytq, 1, 5, sdc, dw), R)
-    rowwise = rowwise_summary(k, T, DI, DO, "row-wise fwd+dgrad+wgrad, tokens 4096, in 4096, out 4096 "
-                                           "(delayed-scaling workload data, step 0)")
-    g_avg = (k["gemm_fwd_tensor"] + k["gemm_dgrad_tensor"] + k["gemm_wgrad_tensor"]) / 3
-    g_ach = 2.0 * T * DI * DO / g_avg / 1e12
-    roofline = {"bound": "mfma",
-                "kernel": "k_gemm_big, per-tensor scales, 4096^3 (fwd/dgrad/wgrad average)",
-                "achieved": round(g_ach, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(g_ach / FP8_PEAK_TFLOPS, 4), "traffic": gemm_traffic()}
+    rowwise = rowwise_summary(k, T, DI, DO, "row-wise fwd+dgrad+wgrad, tokens 4096, in 4096, out 4096")
 
-    # ---- cold timings: before every timed launch a 512 MiB read evicts the
-    # 256 MB last-level cache (MALL) with clean lines, so inputs come from
-    # HBM and no dirty victims are written back during the timed kernel; each
-    # launch is bracketed by its own HIP events on the stream (median of the
-    # reps; the brackets include the dispatch of that one launch)
+    # cold: a 512 MiB read evicts the 256 MB MALL with clean lines before
+    # every timed launch; each launch bracketed by its own HIP events
     flush = torch.zeros(256 << 20, dtype=torch.bfloat16, device=dev)
     flush_amax = torch.zeros(1, dtype=torch.float32, device=dev)
-    L.fp8_amax(flush, flush_amax)
-    torch.cuda.synchronize()
 
     def time_cold(fn, reps):
         evs = []
-        for i in range(reps):
+        for _ in range(reps):
             L.fp8_amax(flush, flush_amax)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -283,65 +477,37 @@ def main():
             evs.append((a, b))
         torch.cuda.synchronize()
         ts = sorted(a.elapsed_time(b) for a, b in evs)
-        return ts[len(ts) // 2] * 1e-3   # seconds
+        return ts[len(ts) // 2] * 1e-3
 
     kc = {}
     kc["gemm_fwd_tensor"] = time_cold(lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y), R)
     kc["gemm_dgrad_tensor"] = time_cold(lambda: L.fp8_scaled_gemm(dyq, 1, 0, sinv[2:3], wq, 0, 0, sinv[1:2], dx), R)
     kc["gemm_wgrad_tensor"] = time_cold(lambda: L.fp8_scaled_gemm(xtq, 0, 0, sinv[0:1], dytq, 1, 0, sinv[2:3], dw), R)
     kc["cast_transpose_amax_acc_e4m3"] = time_cold(lambda: L.fp8_cast_amax_acc(x0, 0, scale[0:1], amax[0:1], y=xq, y_t=xtq), R)
-    kc["cast_transpose_amax_acc_e5m2"] = time_cold(lambda: L.fp8_cast_amax_acc(dy0, 1, scale[2:3], amax[2:3], y=dyq, y_t=dytq), R)
     kc["cast_e4m3"] = time_cold(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq), R)
     kc["amax"] = time_cold(lambda: L.fp8_amax(x0, amax[0:1]), R)
-    del flush
+    kc["cast_rowwise_dy"] = time_cold(lambda: L.fp8_cast_rowwise(dy0, 1, dyq, sdr, dytq, sdc), R)
     kernels_cold = {"note": "MALL evicted (512 MiB read) before every timed launch; median of "
                             f"{R} single launches, each bracketed by HIP events"}
     for n in ("gemm_fwd_tensor", "gemm_dgrad_tensor", "gemm_wgrad_tensor"):
-        kernels_cold[n] = {"tflops": round(2.0 * T * DI * DO / kc[n] / 1e12, 2), "us": round(kc[n] * 1e6, 2)}
-    for n, bpe in (("cast_transpose_amax_acc_e4m3", 4.0), ("cast_transpose_amax_acc_e5m2", 4.0),
-                   ("cast_e4m3", 3.0), ("amax", 2.0)):
-        kernels_cold[n] = {"gbs": round(bpe * nel / kc[n] / 1e9, 2), "us": round(kc[n] * 1e6, 2),
-                           "pct_hbm_peak": round(100 * bpe * nel / kc[n] / 1e9 / HBM_PEAK_GBS, 2)}
-
-    # ---- block-wise path at 8192 x 4096 x 14336
-    blockwise = None
-    if not args.no_blockwise:
-        blockwise = bench_blockwise(torch, L, datagen, dev, stream, d_bf16, time_launch, R)
-
-    result = {
-        "metric": "FP8 scaled-GEMM TFLOP/s (fwd+dgrad+wgrad, % FP8 peak) + cast GB/s",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "launch": "hip_graph" if ms_step_graph is not None else "eager",
-        "ms_per_step_eager": round(ms_step_eager, 4),
-        "ms_per_step_overwrite_casts": (round(ms_step_overwrite, 4)
-                                        if ms_step_overwrite is not None else None),
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3/e5m2 (fp32 accumulate)",
-        "data": "synthetic (seeded numpy PCG64, bf16)",
-        "config": {"workload": "delayed-scaling FP8 linear fwd+dgrad+wgrad, tokens 4096, in 4096, "
-                               "out 4096, amax history 16, inputs regenerated per step (16 steps)",
-                   "global_batch": T, "seq_len": None, "parallelism": "none (1 GPU)"},
-        "wall_s_timed": round(wall, 4) if wall is not None else None,
-        "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
-        "roofline": roofline,
-        "kernels": {n: {kk: round(vv, 2) for kk, vv in d.items()} for n, d in kernels.items()},
-        "kernels_cold": kernels_cold,
-    }
-    result["rowwise"] = rowwise
-    if blockwise is not None:
-        result["blockwise"] = blockwise
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(gemm_flops)
-    print(json.dumps(result), flush=True)
+        kernels_cold[n] = {"tflops": round(fl / kc[n] / 1e12, 2), "us": round(kc[n] * 1e6, 2)}
+    for n, by in (("cast_transpose_amax_acc_e4m3", 4.0 * nel), ("cast_e4m3", 3.0 * nel),
+                  ("amax", 2.0 * nel), ("cast_rowwise_dy", 4.0 * nel + 4.0 * (T + DO))):
+        kernels_cold[n] = {"gbs": round(by / kc[n] / 1e9, 1), "us": round(kc[n] * 1e6, 2),
+                           "pct_hbm_peak": round(100 * by / kc[n] / 1e9 / HBM_PEAK_GBS, 2)}
+    del data
+    blockwise = bench_blockwise(torch, L, datagen, dev, d_bf16, time_launch, time_cold, R)
+    del flush
+    return {"delayed4096": delayed4096, "kernels": kernels, "kernels_cold": kernels_cold,
+            "rowwise": rowwise, "blockwise": blockwise}
 
 
-def bench_blockwise(torch, L, datagen, dev, stream, d_bf16, time_launch, R):
+def bench_blockwise(torch, L, datagen, dev, d_bf16, time_launch, time_cold, R):
     T, DI, DO = 8192, 4096, 14336
-    t0 = time.time()
     c3 = datagen.config3()
     x, w = d_bf16(c3["x"]), d_bf16(c3["w"])
     dy = d_bf16(datagen.config4_dy(c3["rng"]))
-    print(f"# generated block-wise inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    del c3
     u8 = dict(dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
     xq, sx = torch.empty((T, DI), **u8), torch.empty((DI // 128, T), **f32)
@@ -353,100 +519,187 @@ def bench_blockwise(torch, L, datagen, dev, stream, d_bf16, time_launch, R):
     y = torch.empty((T, DO), dtype=torch.bfloat16, device=dev)
     dx = torch.empty((T, DI), dtype=torch.bfloat16, device=dev)
     dw = torch.empty((DI, DO), **f32)
-    k = {}
-    k["cast_block_x_dual"] = time_launch(lambda: L.fp8_cast_block(x, 0, 1, xq, sx, xtq, sxt), R)
-    k["cast_block_x_1x128"] = time_launch(lambda: L.fp8_cast_block(x, 0, 1, xq, sx), R)
-    k["cast_block_w_128x128_both"] = time_launch(lambda: L.fp8_cast_block(w, 0, 2, wq, sw, wtq, swt), R)
-    k["cast_block_dy_dual"] = time_launch(lambda: L.fp8_cast_block(dy, 1, 1, dyq, sdy, dytq, sdyt), R)
-    k["gemm_fwd_block"] = time_launch(lambda: L.fp8_scaled_gemm(xq, 0, 1, sx, wtq, 0, 2, swt, y), R)
-    k["gemm_dgrad_block"] = time_launch(lambda: L.fp8_scaled_gemm(dyq, 1, 1, sdy, wq, 0, 2, sw, dx), R)
-    k["gemm_wgrad_block"] = time_launch(lambda: L.fp8_scaled_gemm(xtq, 0, 1, sxt, dytq, 1, 1, sdyt, dw), R)
-    # the same path with power-of-two (exponent-bias) block scales: the GEMMs
-    # apply them inside the E8M0-scaled matrix instruction
-    k["cast_block_pow2_x_dual"] = time_launch(lambda: L.fp8_cast_block_pow2(x, 0, 1, xq, sx, xtq, sxt), R)
-    k["cast_block_pow2_w_128x128_both"] = time_launch(lambda: L.fp8_cast_block_pow2(w, 0, 2, wq, sw, wtq, swt), R)
-    k["cast_block_pow2_dy_dual"] = time_launch(lambda: L.fp8_cast_block_pow2(dy, 1, 1, dyq, sdy, dytq, sdyt), R)
-    k["gemm_fwd_block_pow2"] = time_launch(lambda: L.fp8_scaled_gemm(xq, 0, 3, sx, wtq, 0, 4, swt, y), R)
-    k["gemm_dgrad_block_pow2"] = time_launch(lambda: L.fp8_scaled_gemm(dyq, 1, 3, sdy, wq, 0, 4, sw, dx), R)
-    k["gemm_wgrad_block_pow2"] = time_launch(lambda: L.fp8_scaled_gemm(xtq, 0, 3, sxt, dytq, 1, 3, sdyt, dw), R)
+    k, kc = {}, {}
+    casts = {
+        "cast_block_x_dual": (lambda: L.fp8_cast_block(x, 0, 1, xq, sx, xtq, sxt), T * DI * (4 + 8 / 128)),
+        "cast_block_w_128x128_both": (lambda: L.fp8_cast_block(w, 0, 2, wq, sw, wtq, swt), DI * DO * (4 + 8 / 16384)),
+        "cast_block_dy_dual": (lambda: L.fp8_cast_block(dy, 1, 1, dyq, sdy, dytq, sdyt), T * DO * (4 + 8 / 128)),
+        "cast_block_pow2_dy_dual": (lambda: L.fp8_cast_block_pow2(dy, 1, 1, dyq, sdy, dytq, sdyt), T * DO * (4 + 8 / 128)),
+        "cast_rowwise_dy": (lambda: L.fp8_cast_rowwise(dy, 1, dyq, sdy[0], dytq, sdyt[0]), T * DO * 4.0 + 4.0 * (T + DO)),
+    }
+    for n, (fn, _) in casts.items():
+        k[n] = time_launch(fn, R)
+        kc[n] = time_cold(fn, R)
+    L.fp8_cast_block(x, 0, 1, xq, sx, xtq, sxt)
+    L.fp8_cast_block(w, 0, 2, wq, sw, wtq, swt)
+    L.fp8_cast_block(dy, 1, 1, dyq, sdy, dytq, sdyt)
+    gem = {
+        "gemm_fwd_block": lambda: L.fp8_scaled_gemm(xq, 0, 1, sx, wtq, 0, 2, swt, y),
+        "gemm_dgrad_block": lambda: L.fp8_scaled_gemm(dyq, 1, 1, sdy, wq, 0, 2, sw, dx),
+        "gemm_wgrad_block": lambda: L.fp8_scaled_gemm(xtq, 0, 1, sxt, dytq, 1, 1, sdyt, dw),
+    }
+    for n, fn in gem.items():
+        k[n] = time_launch(fn, R)
+    L.fp8_cast_block_pow2(x, 0, 1, xq, sx, xtq, sxt)
+    L.fp8_cast_block_pow2(w, 0, 2, wq, sw, wtq, swt)
+    L.fp8_cast_block_pow2(dy, 1, 1, dyq, sdy, dytq, sdyt)
+    gem2 = {
+        "gemm_fwd_block_pow2": lambda: L.fp8_scaled_gemm(xq, 0, 3, sx, wtq, 0, 4, swt, y),
+        "gemm_dgrad_block_pow2": lambda: L.fp8_scaled_gemm(dyq, 1, 3, sdy, wq, 0, 4, sw, dx),
+        "gemm_wgrad_block_pow2": lambda: L.fp8_scaled_gemm(xtq, 0, 3, sxt, dytq, 1, 3, sdyt, dw),
+    }
+    for n, fn in gem2.items():
+        k[n] = time_launch(fn, R)
     fl = 2.0 * T * DI * DO
     out = {"workload": "block-wise fwd (X 8192x4096 Student-t 1x128, W 4096x14336 128x128) + "
                        "bwd (dY 8192x14336 1x128 dual orientation; dgrad, wgrad)"}
-    for n in ("gemm_fwd_block", "gemm_dgrad_block", "gemm_wgrad_block", "gemm_fwd_block_pow2",
-              "gemm_dgrad_block_pow2", "gemm_wgrad_block_pow2"):
+    for n in list(gem) + list(gem2):
         out[n] = {"tflops": round(fl / k[n] / 1e12, 2), "us": round(k[n] * 1e6, 1),
                   "pct_fp8_peak": round(100 * fl / k[n] / 1e12 / FP8_PEAK_TFLOPS, 2)}
-    bytes_ = {"cast_block_x_dual": T * DI * (4 + 8 / 128), "cast_block_x_1x128": T * DI * (3 + 4 / 128),
-              "cast_block_w_128x128_both": DI * DO * 4.0, "cast_block_dy_dual": T * DO * (4 + 8 / 128),
-              "cast_block_pow2_x_dual": T * DI * (4 + 8 / 128),
-              "cast_block_pow2_w_128x128_both": DI * DO * 4.0,
-              "cast_block_pow2_dy_dual": T * DO * (4 + 8 / 128)}
-    for n, b in bytes_.items():
-        out[n] = {"gbs": round(b / k[n] / 1e9, 1), "us": round(k[n] * 1e6, 1),
-                  "pct_hbm_peak": round(100 * b / k[n] / 1e9 / HBM_PEAK_GBS, 2)}
-    tot = (k["cast_block_x_dual"] + k["cast_block_w_128x128_both"] + k["cast_block_dy_dual"]
-           + k["gemm_fwd_block"] + k["gemm_dgrad_block"] + k["gemm_wgrad_block"])
-    out["fwd_bwd_tflops_incl_casts"] = round(3 * fl / tot / 1e12, 2)
-    out["fwd_bwd_ms"] = round(tot * 1e3, 3)
-    tot2 = (k["cast_block_pow2_x_dual"] + k["cast_block_pow2_w_128x128_both"]
-            + k["cast_block_pow2_dy_dual"] + k["gemm_fwd_block_pow2"] + k["gemm_dgrad_block_pow2"]
-            + k["gemm_wgrad_block_pow2"])
-    out["fwd_bwd_tflops_incl_casts_pow2"] = round(3 * fl / tot2 / 1e12, 2)
-    out["fwd_bwd_ms_pow2"] = round(tot2 * 1e3, 3)
-    # row-wise scaling on the same shapes and data
-    sxr, sxc = torch.empty(T, **f32), torch.empty(DI, **f32)
-    swr, swc = torch.empty(DI, **f32), torch.empty(DO, **f32)
-    sdr, sdc = torch.empty(T, **f32), torch.empty(DO, **f32)
-    r = {}
-    r["cast_rowwise_x"] = time_launch(lambda: L.fp8_cast_rowwise(x, 0, xq, sxr, xtq, sxc), R)
-    r["cast_rowwise_w"] = time_launch(lambda: L.fp8_cast_rowwise(w, 0, wq, swr, wtq, swc), R)
-    r["cast_rowwise_dy"] = time_launch(lambda: L.fp8_cast_rowwise(dy, 1, dyq, sdr, dytq, sdc), R)
-    r["gemm_fwd_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(xq, 0, 5, sxr, wtq, 0, 5, swc, y), R)
-    r["gemm_dgrad_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(dyq, 1, 5, sdr, wq, 0, 5, swr, dx), R)
-    r["gemm_wgrad_rowwise"] = time_launch(lambda: L.fp8_scaled_gemm(xtq, 0, 5, sxc, dytq, 1, 5, sdc, dw), R)
-    out["rowwise"] = rowwise_summary(r, T, DI, DO, "row-wise on the same shapes and data")
+    for n, (_, by) in casts.items():
+        out[n] = {"gbs_cold": round(by / kc[n] / 1e9, 1), "us_cold": round(kc[n] * 1e6, 1),
+                  "pct_hbm_peak_cold": round(100 * by / kc[n] / 1e9 / HBM_PEAK_GBS, 2),
+                  "gbs_warm": round(by / k[n] / 1e9, 1), "us_warm": round(k[n] * 1e6, 1)}
     return out
 
 
 def rowwise_summary(k, T, DI, DO, workload):
-    """Row-wise path: GEMM TFLOP/s, cast GB/s of algorithmic bytes (bf16 read
-    once, both FP8 orientations written once, row and column scales), and
-    the whole fwd+bwd including the three casts."""
     fl = 2.0 * T * DI * DO
     out = {"workload": workload}
     for n in ("gemm_fwd_rowwise", "gemm_dgrad_rowwise", "gemm_wgrad_rowwise"):
-        out[n] = {"tflops": round(fl / k[n] / 1e12, 2), "us": round(k[n] * 1e6, 1),
-                  "pct_fp8_peak": round(100 * fl / k[n] / 1e12 / FP8_PEAK_TFLOPS, 2)}
+        out[n] = {"tflops": round(fl / k[n] / 1e12, 2), "us": round(k[n] * 1e6, 1)}
     shapes = {"cast_rowwise_x": (T, DI), "cast_rowwise_w": (DI, DO), "cast_rowwise_dy": (T, DO)}
     for n, (a, b) in shapes.items():
         by = a * b * 4.0 + 4.0 * (a + b)
-        out[n] = {"gbs": round(by / k[n] / 1e9, 1), "us": round(k[n] * 1e6, 1),
-                  "pct_hbm_peak": round(100 * by / k[n] / 1e9 / HBM_PEAK_GBS, 2)}
-    tot = sum(k[n] for n in list(shapes) + ["gemm_fwd_rowwise", "gemm_dgrad_rowwise",
-                                            "gemm_wgrad_rowwise"])
-    out["fwd_bwd_tflops_incl_casts"] = round(3 * fl / tot / 1e12, 2)
-    out["fwd_bwd_ms"] = round(tot * 1e3, 3)
+        out[n] = {"gbs": round(by / k[n] / 1e9, 1), "us": round(k[n] * 1e6, 1)}
     return out
 
 
-def gemm_traffic():
-    """HBM bytes per launch of the per-tensor 4096^3 GEMM (average of fwd,
-    dgrad, wgrad) from the committed counter summary, or None when the
-    kernel sources changed after the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "gemm_tensor4096_traffic.json")
+# ----------------------------------------------------------------------------
+# HBM traffic of the step's GEMM kernels (rocprofv3 counter runs)
+# ----------------------------------------------------------------------------
+def traffic_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "fp8_mixed_precision_linear_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def gemm_traffic(cls):
+    """Measured HBM bytes per launch of a GEMM kernel of the step (average
+    over its five launches), from the committed counter summary, or None
+    when the kernel sources changed after the counters were taken."""
     try:
-        with open(path) as f:
+        with open(TRAFFIC_JSON) as f:
             t = json.load(f)
-        from fp8_mixed_precision_linear_amd.traffic_probe import sources_sha256
-        if t.get("sources_sha256") != sources_sha256():
+        if t.get("sources_sha256") != traffic_sources_sha256():
             return None
-        k = t["kernels"]
-        names = ("gemm_fwd_tensor", "gemm_dgrad_tensor", "gemm_wgrad_tensor")
-        return round(sum(k[n]["traffic_bytes"] for n in names) / 3)
+        return round(t["kernels"][cls]["traffic_bytes"])
     except (OSError, KeyError, ValueError):
         return None
 
 
+COPY_BYTES = 256 << 20
+
+
+def traffic_run():
+    """Under rocprofv3 --pmc: a copy of known size (256 MiB read, 256 MiB
+    written), then each GEMM of the step twice (delayed pass, then block
+    pass; the first launch of each is discarded by the summary)."""
+    import torch
+    from fp8_mixed_precision_linear_amd import datagen
+    from fp8_mixed_precision_linear_amd import lib as L
+    dev = torch.device("cuda:0")
+    xin = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    xout = torch.empty_like(xin)
+    for _ in range(3):
+        torch.neg(xin, out=xout)
+    torch.cuda.synchronize()
+    del xin, xout
+    c5 = C5Set(torch, L, datagen, dev)
+    for mode in ("delayed", "block"):
+        for lab, kind, work, fn in c5.ops[mode]:
+            if kind != "gemm":
+                fn()
+        for lab, kind, work, fn in c5.ops[mode]:
+            if kind == "gemm":
+                fn()
+                fn()
+        torch.cuda.synchronize()
+    print("traffic-run: done", flush=True)
+
+
+def traffic_summarize(d, dst):
+    import re
+
+    def per_dispatch(sub, counter):
+        files = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise FileNotFoundError(f"no counter_collection.csv under {os.path.join(d, sub)}")
+        vals = {}
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])
+                vals[int(r["Dispatch_Id"])][1] += float(r["Counter_Value"])
+        return [vals[i] for i in sorted(vals)]
+
+    def classify(rows):
+        """copy dispatches, then per pass: each GEMM launched twice in the
+        step's order (fwd x5, dgrad/wgrad pairs x5); keep the second."""
+        copy = [v for n, v in rows if "neg_kernel" in n]
+        gem = [(n, v) for n, v in rows if "k_gemm_big" in n]
+        out = {}
+        order = []
+        for mode in ("delayed", "block"):
+            order += [f"{mode} fwd"] * 5
+            for _ in range(5):
+                order += [f"{mode} dgrad", f"{mode} wgrad"]
+        assert len(gem) == 2 * len(order), (len(gem), len(order))
+        for i, cls in enumerate(order):
+            name, v = gem[2 * i + 1]
+            want = C5_KERNEL[cls]
+            assert re.sub(r"\s", "", want) in re.sub(r"\s", "", name), (cls, name)
+            out.setdefault(cls, []).append(v)
+        return copy[1:] if len(copy) > 1 else copy, out
+
+    fcopy, fetch = classify(per_dispatch("fetch", "FETCH_SIZE"))
+    wcopy, write = classify(per_dispatch("write", "WRITE_SIZE"))
+    kib = COPY_BYTES / 1024.0
+    f_fetch = kib / (sum(fcopy) / len(fcopy))
+    f_write = kib / (sum(wcopy) / len(wcopy))
+    from fp8_mixed_precision_linear_amd import datagen
+    T = 8192
+    res = {"what": "HBM bytes per GEMM launch of the transformer-block linear set (average over "
+                   "the five linears of each pass): FETCH_SIZE and WRITE_SIZE (KiB per dispatch), "
+                   "each scaled by the reading for a 256 MiB elementwise copy (neg) of known size",
+           "copy_scale": {"fetch": round(f_fetch, 4), "write": round(f_write, 4)},
+           "sources_sha256": traffic_sources_sha256(), "kernels": {}}
+    for cls in C5_KERNEL:
+        alg = 0.0
+        for n in C5_ORDER:
+            di, do = datagen.C5_LINEARS[n]
+            if cls.endswith("fwd"):
+                alg += T * di + do * di + 2 * T * do
+            elif cls.endswith("dgrad"):
+                alg += T * do + di * do + 2 * T * di
+            else:
+                alg += di * T + do * T + 4 * di * do
+        alg /= 5
+        rd = sum(fetch[cls]) / 5 * f_fetch * 1024.0
+        wr = sum(write[cls]) / 5 * f_write * 1024.0
+        res["kernels"][cls] = {"kernel": C5_KERNEL[cls], "read_bytes": round(rd),
+                               "write_bytes": round(wr), "traffic_bytes": round(rd + wr),
+                               "algorithmic_bytes": round(alg),
+                               "traffic_over_algorithmic": round((rd + wr) / alg, 3)}
+    with open(dst, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+# ----------------------------------------------------------------------------
 def capture(torch, fn):
     """Capture fn's launches into a HIP graph (torch makes its capture stream
     the current stream, which is the stream the binding passes to the
@@ -459,35 +712,109 @@ def capture(torch, fn):
     return g
 
 
-def cpu_baseline(gemm_flops):
-    """The oracle, as it stands, on a bounded sample of one step: the three
-    casts (+amax) of one step at full size, and the three GEMMs (exact and
-    FP32-accumulated) on 64 sampled output rows each, extrapolated to the
-    full 4096 rows."""
+def cpu_model() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return "unknown"
+
+
+def cpu_baseline(step_flops, step_cast_bytes):
+    """The oracle, as it stands, on a bounded sample of the step: the O
+    linear (8192 tokens, 8192 -> 8192) in both passes -- the casts of X, W
+    and dY at full size (per-tensor with transpose, and block-wise) and the
+    three GEMMs of each pass on 48 of 8192 output rows -- extrapolated to
+    the step: GEMM time by FLOPs, cast time by algorithmic bytes."""
     from fp8_mixed_precision_linear_amd import datagen
     from oracle import oracle as O
-    s = datagen.config2_step(0)
+    d = datagen.config5_linear("o")
+    x, w, dy = d["x"], d["w"], d["dy"]
+    T, DI = x.shape
+    DO = w.shape[1]
     t0 = time.perf_counter()
-    ax, aw, ad = O.amax_parallel(s["x"]), O.amax_parallel(s["w"]), O.amax_parallel(s["dy"])
-    xq = O.cast(s["x"], 1.0, 0)
-    wq = O.cast(s["w"], 1.0, 0)
-    dq = O.cast(s["dy"], 1.0, 1)
+    ax, aw, ad = O.amax_parallel(x), O.amax_parallel(w), O.amax_parallel(dy)
+    sx, sxi, _ = O.compute_scale(ax, 0)
+    sw, swi, _ = O.compute_scale(aw, 0)
+    sd, sdi, _ = O.compute_scale(ad, 1)
+    xq, wq, dq = O.cast(x, sx, 0), O.cast(w, sw, 0), O.cast(dy, sd, 1)
+    bx = O.cast_block(x, 0, O.S1x128, want_y=True, want_t=True)
+    bw = O.cast_block(w, 0, O.S128x128, want_y=True, want_t=True)
+    bd = O.cast_block(dy, 1, O.S1x128, want_y=True, want_t=True)
     t_cast = time.perf_counter() - t0
-    rows = np.arange(64, dtype=np.int64)
-    one = np.ones(1, np.float32)
-    wt = np.ascontiguousarray(wq.T)
+    cast_bytes = 2 * 4.0 * (T * DI + DI * DO + T * DO)   # both passes, both orientations
+    rows = np.arange(48, dtype=np.int64)
     t1 = time.perf_counter()
-    O.gemm(xq, 0, 0, one, wt, 0, 0, one, ms=rows)                 # fwd
-    O.gemm(dq, 1, 0, one, wq, 0, 0, one, ms=rows)                 # dgrad
-    O.gemm(np.ascontiguousarray(xq.T), 0, 0, one, np.ascontiguousarray(dq.T), 1, 0, one, ms=rows)
-    t_gemm = (time.perf_counter() - t1) * (4096 / 64)
-    t_step = t_cast + t_gemm
-    return {"value": round(gemm_flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": O.nthreads(),
-            "kind": "oracle",
-            "sample": "one delayed-scaling step (4096^3): casts + amax at full size "
-                      f"({t_cast:.2f}s), the three GEMMs on 64 of 4096 output rows "
-                      f"({t_gemm * 64 / 4096:.2f}s), extrapolated to all rows",
-            "step_s_extrapolated": round(t_step, 2)}
+    one = lambda v: np.array([v], np.float32)
+    xt, dt_, wt = (np.ascontiguousarray(a.T) for a in (xq, dq, wq))
+    O.gemm(xq, 0, 0, one(sxi), wt, 0, 0, one(swi), ms=rows)
+    O.gemm(dq, 1, 0, one(sdi), wq, 0, 0, one(swi), ms=rows)
+    O.gemm(xt, 0, 0, one(sxi), dt_, 1, 0, one(sdi), ms=rows)
+    O.gemm(bx["y"], 0, 1, bx["sinv"], bw["y_t"], 0, 2, bw["sinv_t"], ms=rows)
+    O.gemm(bd["y"], 1, 1, bd["sinv"], bw["y"], 0, 2, bw["sinv"], ms=rows)
+    O.gemm(bx["y_t"], 0, 1, bx["sinv_t"], bd["y_t"], 1, 1, bd["sinv_t"], ms=rows)
+    t_gemm_sample = time.perf_counter() - t1
+    sample_flops = 6 * 2.0 * len(rows) * DO * DI   # each GEMM: 48 rows x 8192 x 8192
+    t_step = t_gemm_sample * step_flops / sample_flops + t_cast * step_cast_bytes / cast_bytes
+    return {"value": round(step_flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": O.nthreads(),
+            "kind": "oracle", "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
+            "sample": "the O linear (8192 tokens, 8192 -> 8192) in both passes: amax, scales and "
+                      f"casts of X, W, dY at full size ({t_cast:.2f}s), the six GEMMs on 48 of "
+                      f"8192 output rows ({t_gemm_sample:.2f}s); extrapolated to the step by FLOPs "
+                      "(GEMMs) and algorithmic bytes (casts)",
+            "step_s_extrapolated": round(t_step, 1)}
+
+
+def main():
+    args = parse()
+    if args.traffic_summarize:
+        traffic_summarize(*args.traffic_summarize)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the FP8 linear path here has no multi-GPU "
+              "(sharded) mode; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.traffic_run:
+        traffic_run()
+        return
+
+    import torch
+    from fp8_mixed_precision_linear_amd import datagen
+    from fp8_mixed_precision_linear_amd import lib as L
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    h = bench_c5(args, torch, L, datagen, dev, stream)
+    value = h["flops"] / (h["ms_step"] * 1e-3) / 1e12
+    summ = h["summary"]
+    result = {
+        "metric": "FP8 scaled-GEMM TFLOP/s (fwd+dgrad+wgrad, % FP8 peak) + cast GB/s",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(h["ms_step"], 4), "higher_is_better": True,
+        "launch": "hip_graph", "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3/e5m2 (fp32 accumulate)",
+        "data": "synthetic (seeded numpy PCG64, bf16)",
+        "config": {"workload": "transformer-block FP8 linear set, hidden 8192, FFN 28672, 8192 "
+                               "tokens: QKV 8192->10240, O 8192->8192, gate/up 8192->28672 "
+                               "(shared input), down 28672->8192; fwd+dgrad+wgrad of every "
+                               "linear in per-tensor delayed scaling (history 16) and in "
+                               "block-wise scaling (1x128 / 128x128); 2 x 42.06 TFLOP per step",
+                   "global_batch": 8192, "seq_len": None, "parallelism": "none (1 GPU)"},
+        "wall_s_timed": round(h["wall"], 4),
+        "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
+        "roofline": h["roofline"],
+        "c5": summ,
+    }
+    if not args.no_extras:
+        result.update(bench_extras(args, torch, L, datagen, dev, stream))
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(h["flops"], h["cast_bytes"])
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":
