@@ -159,6 +159,7 @@ class C5Set:
             self.sd[n] = torch.empty((do // 128, T), **f32)
             self.sdt[n] = torch.empty((T // 128, do), **f32)
         self.ops = {"delayed": self._delayed_ops(), "block": self._block_ops()}
+        assert [op[:3] for m in ("delayed", "block") for op in self.ops[m]] == c5_plan(T)
 
     def flops_per_pass(self):
         return sum(3 * 2.0 * self.T * di * do for di, do in self.shapes.values())
@@ -260,6 +261,40 @@ class C5Set:
                 evs.append((lab, kind, work, a, b))
         torch.cuda.synchronize()
         return [(lab, kind, work, a.elapsed_time(b) * 1e-3) for lab, kind, work, a, b in evs]
+
+
+def c5_plan(T=8192):
+    """The launches of one step in order, (label, kind, work), from the
+    shapes alone (the op lists of C5Set follow it)."""
+    from fp8_mixed_precision_linear_amd import datagen
+    sh = datagen.C5_LINEARS
+    plan = []
+    for n in C5_ORDER:
+        di, do = sh[n]
+        if C5_X[n] == n:
+            plan.append((f"delayed cast X {n}", "cast", 4.0 * T * di))
+        plan.append((f"delayed cast W {n}", "cast", 4.0 * di * do))
+        plan.append((f"delayed fwd {n}", "gemm", 2.0 * T * di * do))
+    for n in reversed(C5_ORDER):
+        di, do = sh[n]
+        plan += [(f"delayed cast dY {n}", "cast", 4.0 * T * do),
+                 (f"delayed dgrad {n}", "gemm", 2.0 * T * di * do),
+                 (f"delayed wgrad {n}", "gemm", 2.0 * T * di * do)]
+    n_e4m3 = len(set(C5_X.values())) + len(C5_ORDER)
+    plan += [("delayed history E4M3", "state", 8.0 * 16 * n_e4m3),
+             ("delayed history E5M2", "state", 8.0 * 16 * len(C5_ORDER))]
+    for n in C5_ORDER:
+        di, do = sh[n]
+        if C5_X[n] == n:
+            plan.append((f"block cast X {n}", "cast", T * di * (4 + 8 / 128)))
+        plan.append((f"block cast W {n}", "cast", di * do * (4 + 8 / 16384)))
+        plan.append((f"block fwd {n}", "gemm", 2.0 * T * di * do))
+    for n in reversed(C5_ORDER):
+        di, do = sh[n]
+        plan += [(f"block cast dY {n}", "cast", T * do * (4 + 8 / 128)),
+                 (f"block dgrad {n}", "gemm", 2.0 * T * di * do),
+                 (f"block wgrad {n}", "gemm", 2.0 * T * di * do)]
+    return plan
 
 
 # GEMM kernel (instantiation) of each pass: the dominant-kernel roofline is
@@ -605,8 +640,10 @@ COPY_BYTES = 256 << 20
 
 def traffic_run():
     """Under rocprofv3 --pmc: a copy of known size (256 MiB read, 256 MiB
-    written), then each GEMM of the step twice (delayed pass, then block
-    pass; the first launch of each is discarded by the summary)."""
+    written); then per pass the step's casts and history updates once and
+    each GEMM twice (the summary keeps the second launch); then the
+    row-wise cast of the O linear's activation (8192 x 8192, both
+    orientations) twice."""
     import torch
     from fp8_mixed_precision_linear_amd import datagen
     from fp8_mixed_precision_linear_amd import lib as L
@@ -627,10 +664,20 @@ def traffic_run():
                 fn()
                 fn()
         torch.cuda.synchronize()
+    x = c5.x["o"]
+    T, DI = x.shape
+    f32 = dict(dtype=torch.float32, device=dev)
+    sr, sc = torch.empty(T, **f32), torch.empty(DI, **f32)
+    for _ in range(2):
+        L.fp8_cast_rowwise(x, 0, c5.xq["o"], sr, c5.xtq["o"], sc)
+    torch.cuda.synchronize()
     print("traffic-run: done", flush=True)
 
 
 def traffic_summarize(d, dst):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE of traffic_run's program ->
+    bytes per launch of each GEMM kernel of the step (average over its five
+    linears), of each cast kind, and of the row-wise cast's kernels."""
     import re
 
     def per_dispatch(sub, counter):
@@ -646,24 +693,44 @@ def traffic_summarize(d, dst):
                 vals[int(r["Dispatch_Id"])][1] += float(r["Counter_Value"])
         return [vals[i] for i in sorted(vals)]
 
+    def nospace(t):
+        return re.sub(r"\s", "", t)
+
     def classify(rows):
-        """copy dispatches, then per pass: each GEMM launched twice in the
-        step's order (fwd x5, dgrad/wgrad pairs x5); keep the second."""
+        """(copy values, {class: [values]}): the launches in traffic_run's
+        order, each checked against the kernel it must be."""
         copy = [v for n, v in rows if "neg_kernel" in n]
-        gem = [(n, v) for n, v in rows if "k_gemm_big" in n]
-        out = {}
-        order = []
+        ours = [(n, v) for n, v in rows if "fp8lin" in n]
+        plan = c5_plan()
+        seq = []
         for mode in ("delayed", "block"):
-            order += [f"{mode} fwd"] * 5
-            for _ in range(5):
-                order += [f"{mode} dgrad", f"{mode} wgrad"]
-        assert len(gem) == 2 * len(order), (len(gem), len(order))
-        for i, cls in enumerate(order):
-            name, v = gem[2 * i + 1]
-            want = C5_KERNEL[cls]
-            assert re.sub(r"\s", "", want) in re.sub(r"\s", "", name), (cls, name)
-            out.setdefault(cls, []).append(v)
-        return copy[1:] if len(copy) > 1 else copy, out
+            seq += [(lab, k, w) for lab, k, w in plan if lab.startswith(mode) and k != "gemm"]
+            for lab, k, w in plan:
+                if lab.startswith(mode) and k == "gemm":
+                    seq += [(lab + " (first)", k, w), (lab, k, w)]
+        rw = ["k_rw_rows", "k_rw_colmax", "k_rw_transpose", "k_rw_finalize"]
+        seq += [(f"rowwise {k}", "rowwise", 0.0) for _ in range(2) for k in rw]
+        assert len(ours) == len(seq), (len(ours), len(seq))
+        out = {}
+        for (name, v), (lab, kind, w) in zip(ours, seq):
+            if lab.endswith("(first)"):
+                continue
+            if kind == "gemm":
+                cls = lab.rsplit(" ", 1)[0]
+                assert nospace(C5_KERNEL[cls]) in nospace(name), (lab, name)
+            elif kind == "cast":
+                cls = lab.rsplit(" ", 1)[0]
+                want = "k_cast_transpose" if cls.startswith("delayed") else (
+                    "k_cast_block<0,2" if cls.endswith("W") else "k_cast_block<")
+                assert want in nospace(name), (lab, name)
+            elif kind == "state":
+                cls = "delayed history"
+                assert "k_history_update" in name, (lab, name)
+            else:
+                cls = lab
+                assert lab.split(" ")[1] in name, (lab, name)
+            out.setdefault(cls, []).append((v, w))
+        return (copy[1:] if len(copy) > 1 else copy), out
 
     fcopy, fetch = classify(per_dispatch("fetch", "FETCH_SIZE"))
     wcopy, write = classify(per_dispatch("write", "WRITE_SIZE"))
@@ -672,12 +739,8 @@ def traffic_summarize(d, dst):
     f_write = kib / (sum(wcopy) / len(wcopy))
     from fp8_mixed_precision_linear_amd import datagen
     T = 8192
-    res = {"what": "HBM bytes per GEMM launch of the transformer-block linear set (average over "
-                   "the five linears of each pass): FETCH_SIZE and WRITE_SIZE (KiB per dispatch), "
-                   "each scaled by the reading for a 256 MiB elementwise copy (neg) of known size",
-           "copy_scale": {"fetch": round(f_fetch, 4), "write": round(f_write, 4)},
-           "sources_sha256": traffic_sources_sha256(), "kernels": {}}
-    for cls in C5_KERNEL:
+
+    def gemm_alg(cls):
         alg = 0.0
         for n in C5_ORDER:
             di, do = datagen.C5_LINEARS[n]
@@ -687,13 +750,44 @@ def traffic_summarize(d, dst):
                 alg += T * do + di * do + 2 * T * di
             else:
                 alg += di * T + do * T + 4 * di * do
-        alg /= 5
-        rd = sum(fetch[cls]) / 5 * f_fetch * 1024.0
-        wr = sum(write[cls]) / 5 * f_write * 1024.0
-        res["kernels"][cls] = {"kernel": C5_KERNEL[cls], "read_bytes": round(rd),
-                               "write_bytes": round(wr), "traffic_bytes": round(rd + wr),
-                               "algorithmic_bytes": round(alg),
-                               "traffic_over_algorithmic": round((rd + wr) / alg, 3)}
+        return alg / 5
+
+    res = {"what": "HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, each scaled "
+                   "by the reading for a 256 MiB elementwise copy (neg) of known size): the GEMM "
+                   "kernels of the transformer-block step (average over its five linears), its "
+                   "casts per kind, and the row-wise cast of an 8192 x 8192 activation",
+           "copy_scale": {"fetch": round(f_fetch, 4), "write": round(f_write, 4)},
+           "sources_sha256": traffic_sources_sha256(), "kernels": {}, "casts": {}, "rowwise": {}}
+    for cls in fetch:
+        nf = len(fetch[cls])
+        rd = sum(v for v, _ in fetch[cls]) / nf * f_fetch * 1024.0
+        wr = sum(v for v, _ in write[cls]) / nf * f_write * 1024.0
+        if cls in C5_KERNEL:
+            alg = gemm_alg(cls)
+            key = "kernels"
+            extra = {"kernel": C5_KERNEL[cls]}
+        elif cls.startswith("rowwise"):
+            alg = None
+            key = "rowwise"
+            extra = {}
+        elif cls == "delayed history":
+            continue
+        else:
+            alg = sum(w for _, w in fetch[cls]) / nf
+            key = "casts"
+            extra = {}
+        e = {**extra, "launches": nf, "read_bytes": round(rd), "write_bytes": round(wr),
+             "traffic_bytes": round(rd + wr)}
+        if alg:
+            e["algorithmic_bytes"] = round(alg)
+            e["traffic_over_algorithmic"] = round((rd + wr) / alg, 3)
+        res[key][cls] = e
+    rw = res["rowwise"]
+    if rw:
+        tot = sum(e["traffic_bytes"] for e in rw.values())
+        alg = 8192 * 8192 * 4.0 + 4.0 * 2 * 8192
+        rw["total"] = {"traffic_bytes": tot, "algorithmic_bytes": round(alg),
+                       "traffic_over_algorithmic": round(tot / alg, 3)}
     with open(dst, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
