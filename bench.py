@@ -439,17 +439,20 @@ def bench_extras(args, torch, L, datagen, dev, stream):
                    "ms_per_step": round(ms_step, 4),
                    "tflops_incl_casts": round(3 * 2.0 * T * DI * DO / (ms_step * 1e-3) / 1e12, 2)}
 
-    def time_launch(fn, reps):
+    def time_launch(fn, reps, replays=3):
         g = capture(torch, lambda: [fn() for _ in range(reps)])
         g.replay()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        g.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(replays):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b))
         del g
-        return a.elapsed_time(b) / reps * 1e-3
+        return best / reps * 1e-3
 
     x0, w0, dy0 = data[0]
     R = args.kernel_reps
@@ -459,7 +462,16 @@ def bench_extras(args, torch, L, datagen, dev, stream):
     k["gemm_wgrad_tensor"] = time_launch(lambda: L.fp8_scaled_gemm(xtq, 0, 0, sinv[0:1], dytq, 1, 0, sinv[2:3], dw), R)
     y8, y8t = torch.empty((T, DO), **u8), torch.empty((DO, T), **u8)
     am8 = torch.zeros(1, dtype=torch.float32, device=dev)
+    # the quantising epilogue (E4M3 codes, transposed copy, amax
+    # max-accumulated into the slot as in a delayed-scaling step), timed
+    # right after the same GEMM with a BF16 output; then with the amax
+    # overwritten (a one-word fill launched ahead of the GEMM)
+    k["gemm_fwd_tensor"] = min(k["gemm_fwd_tensor"], time_launch(
+        lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y), R))
     k["gemm_fwd_tensor_fp8out"] = time_launch(
+        lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y8, d_amax=am8,
+                                  d_scale=scale[0:1], d_fmt=0, D_t=y8t, amax_accumulate=True), R)
+    k["gemm_fwd_tensor_fp8out_amax_overwrite"] = time_launch(
         lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y8, d_amax=am8,
                                   d_scale=scale[0:1], d_fmt=0, D_t=y8t), R)
     k["cast_transpose_amax_e4m3"] = time_launch(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq, y_t=xtq, amax_out=amax[0:1]), R)
@@ -473,11 +485,13 @@ def bench_extras(args, torch, L, datagen, dev, stream):
     k["ewma_update"] = time_launch(lambda: L.fp8_amax_ewma_update(ewma, amax, 0.9, 0, 0, scale, sinv), R)
     nel = T * DI
     fl = 2.0 * T * DI * DO
-    kernels = {"note": "warm: R launches back to back in one HIP graph, one replay timed"}
-    for n in ("gemm_fwd_tensor", "gemm_dgrad_tensor", "gemm_wgrad_tensor", "gemm_fwd_tensor_fp8out"):
+    kernels = {"note": "warm: R launches back to back in one HIP graph, best of 3 replays"}
+    for n in ("gemm_fwd_tensor", "gemm_dgrad_tensor", "gemm_wgrad_tensor", "gemm_fwd_tensor_fp8out",
+              "gemm_fwd_tensor_fp8out_amax_overwrite"):
         kernels[n] = {"tflops": round(fl / k[n] / 1e12, 2), "us": round(k[n] * 1e6, 2)}
     kernels["gemm_fwd_tensor_fp8out"]["us_unfused_equivalent"] = round(
-        (k["gemm_fwd_tensor"] + k["cast_transpose_amax_e4m3"]) * 1e6, 2)
+        (k["gemm_fwd_tensor"] + k["cast_transpose_amax_acc_e4m3"]) * 1e6, 2)
+    kernels["gemm_fwd_tensor_fp8out"]["vs_bf16_out"] = round(k["gemm_fwd_tensor_fp8out"] / k["gemm_fwd_tensor"], 3)
     for n, bpe in (("cast_transpose_amax_e4m3", 4), ("cast_transpose_amax_acc_e4m3", 4),
                    ("cast_transpose_amax_e5m2_sr", 4), ("cast_e4m3", 3), ("amax", 2)):
         kernels[n] = {"gbs": round(bpe * nel / k[n] / 1e9, 1), "us": round(k[n] * 1e6, 2)}

@@ -233,6 +233,7 @@ fp8_status fp8_scaled_gemm(const fp8_gemm_args* a, hipStream_t stream) {
     return FP8_ERR_ARG;
   const bool fp8_out = a->d_dtype == FP8_OUT_E4M3 || a->d_dtype == FP8_OUT_E5M2;
   if (a->accumulate != 0 && a->accumulate != 1) return FP8_ERR_ARG;
+  if (a->amax_accumulate != 0 && a->amax_accumulate != 1) return FP8_ERR_ARG;
   if (a->accumulate && a->d_dtype != FP8_OUT_F32) return FP8_ERR_UNSUPPORTED;
   if (!fp8_out && a->D_t != nullptr) return FP8_ERR_ARG;
   const bool block = is_block(a->a_scaling) || is_block(a->b_scaling);
@@ -266,7 +267,7 @@ fp8_status fp8_scaled_gemm(const fp8_gemm_args* a, hipStream_t stream) {
   p.A = a->A; p.a_fmt = a->a_fmt; p.a_scaling = a->a_scaling; p.a_sinv = a->a_scale_inv;
   p.B = a->B; p.b_fmt = a->b_fmt; p.b_scaling = a->b_scaling; p.b_sinv = a->b_scale_inv;
   p.D = a->D; p.d_f32 = a->d_dtype == FP8_OUT_F32 ? 1 : 0;
-  p.d_amax = a->d_amax; p.accumulate = a->accumulate;
+  p.d_amax = a->d_amax; p.accumulate = a->accumulate; p.amax_acc = a->amax_accumulate;
   p.d_fp8 = a->d_dtype == FP8_OUT_E4M3 ? 1 : (a->d_dtype == FP8_OUT_E5M2 ? 2 : 0);
   p.d_scale = fp8_out ? a->d_scale : nullptr;
   p.D_t = fp8_out ? a->D_t : nullptr;

@@ -61,8 +61,10 @@ __device__ __forceinline__ float sat(float v) {
 
 // The conversion instructions emit one fixed NaN code whatever the input's
 // sign; the layer's cast maps NaN to 0x7F | sign.  Only wavefronts that
-// actually hold a NaN take this path.
-__device__ __noinline__ uint32_t nan_patch(uint32_t w, float a, float b, float c, float d) {
+// actually hold a NaN take this path.  The out-of-line copy keeps the casts'
+// loops small; the inlined one serves kernels whose register file is nearly
+// full, where a call would spill the caller's live registers to scratch.
+__device__ __forceinline__ uint32_t nan_patch_inl(uint32_t w, float a, float b, float c, float d) {
   const float v[4] = {a, b, c, d};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -72,10 +74,13 @@ __device__ __noinline__ uint32_t nan_patch(uint32_t w, float a, float b, float c
     }
   return w;
 }
+__device__ __noinline__ uint32_t nan_patch(uint32_t w, float a, float b, float c, float d) {
+  return nan_patch_inl(w, a, b, c, d);
+}
 
 // Four binary32 values -> four FP8 codes packed little-endian in a dword
 // (a in byte 0 ... d in byte 3), round to nearest even, saturating.
-template <int FMT>
+template <int FMT, bool INLINE_NAN = false>
 __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
   int w;
   if constexpr (FMT == 0) {
@@ -86,7 +91,7 @@ __device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
     w = __builtin_amdgcn_cvt_pk_bf8_f32(sat<1>(c), sat<1>(d), w, true);
   }
   if (__builtin_isnan(a) | __builtin_isnan(b) | __builtin_isnan(c) | __builtin_isnan(d))
-    return nan_patch((uint32_t)w, a, b, c, d);
+    return INLINE_NAN ? nan_patch_inl((uint32_t)w, a, b, c, d) : nan_patch((uint32_t)w, a, b, c, d);
   return (uint32_t)w;
 }
 
@@ -304,6 +309,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 template <int AF, int BF>
 __device__ __forceinline__ v4f mfma(const v8i& a, const v8i& b, const v4f& c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, 0, 0, 0);
+}
+
+// max(a, b, c) of unsigned words as one instruction that the compiler keeps
+// where it stands (volatile asm): an unsigned maximum over |x| bit patterns
+// is the amax of binary32 values, NaN above +Inf.
+__device__ __forceinline__ uint32_t max3_in_place(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm volatile("v_max3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 }  // namespace fp8lin

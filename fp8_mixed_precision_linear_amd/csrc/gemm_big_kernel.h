@@ -207,6 +207,20 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  // The epilogue's per-tensor scales are read now, ahead of the first DMA:
+  // the wait for stage 0 covers them, and the epilogue does not start with
+  // a round trip to memory.
+  float sa = 1.0f, sb = 1.0f, so = 1.0f;
+  if constexpr (!BLOCK) {
+    sa = p.a_sinv[0];
+    sb = p.b_sinv[0];
+  }
+  if constexpr (MX) {   // a per-tensor operand's scale is applied there
+    if (p.a_scaling == 0) sa = p.a_sinv[0];
+    if (p.b_scaling == 0) sb = p.b_sinv[0];
+  }
+  if constexpr (OUT8) so = p.d_scale[0];
+
   // the first two stages go out together, so the second one's latency
   // overlaps the first's; the loop's first step then issues no DMA
   load_stage(0, lds[0]);
@@ -385,15 +399,6 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   // per lane: one 128-byte line per tile row for BF16, two for FP32 (FP32
   // goes in two passes of 64 rows).  Other tiles store element by element
   // with bounds checks.
-  float sa = 1.0f, sb = 1.0f;
-  if constexpr (!BLOCK) {
-    sa = p.a_sinv[0];
-    sb = p.b_sinv[0];
-  }
-  if constexpr (MX) {   // a per-tensor operand's scale is applied here
-    if (p.a_scaling == 0) sa = p.a_sinv[0];
-    if (p.b_scaling == 0) sb = p.b_sinv[0];
-  }
   constexpr bool EPI_SCALE = !BLOCK || MX;
   // Can a dequantised output be a binary32 subnormal?  With per-tensor
   // scales every nonzero accumulator is a multiple of 2^-(qa+qb), the
@@ -428,7 +433,6 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     // then, for the transposed copy, column-major (row stride 144 bytes).
     __syncthreads();
     uint8_t* wl = &lds[0][0] + wave * 16384;
-    const float so = p.d_scale[0];
     auto epi8 = [&](auto fmttag) {
       constexpr int F = decltype(fmttag)::value;
       uint32_t code[TI][TJ];
@@ -438,12 +442,15 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
         for (int j = 0; j < TJ; ++j) {
           float v[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[q] = deq(i, j, q, acc[i][j][q]);
-            const uint32_t b = __float_as_uint(v[q]) & 0x7FFFFFFFu;
-            amax_bits = b > amax_bits ? b : amax_bits;
-          }
-          code[i][j] = cvt4<F>(v[0] * so, v[1] * so, v[2] * so, v[3] * so);
+          for (int q = 0; q < 4; ++q) v[q] = deq(i, j, q, acc[i][j][q]);
+          // The running maximum is taken here, in place: left to itself the
+          // compiler moves it past the NaN-patch branches to the end of the
+          // pass, which keeps all 128 dequantised values live (and spilled).
+          amax_bits = max3_in_place(max3_in_place(amax_bits, __float_as_uint(v[0]) & 0x7FFFFFFFu,
+                                                  __float_as_uint(v[1]) & 0x7FFFFFFFu),
+                                    __float_as_uint(v[2]) & 0x7FFFFFFFu,
+                                    __float_as_uint(v[3]) & 0x7FFFFFFFu);
+          code[i][j] = cvt4<F, true>(v[0] * so, v[1] * so, v[2] * so, v[3] * so);
           const int r = 16 * i + l16;
           *reinterpret_cast<uint32_t*>(wl + r * 64 + ((j ^ (r & 3)) << 4) + 4 * g) = code[i][j];
         }
@@ -459,15 +466,30 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
         }
       }
       if (p.D_t) {
-        // same wavefront, LDS operations in order: the row-major reads above
-        // complete before these writes reuse the region
+        // Transposed copy: a 4 x 4 byte transpose across each quad of lanes
+        // (same g, rows 16i + 4k .. +3): quad lane t gathers byte t of the
+        // four lanes' words (DPP quad permutes, then two byte selects), i.e.
+        // column 16j + 4g + t, rows 16i + 4k .. +3, and writes them as one
+        // dword of the column-major tile (row stride 144 bytes: the 64 lanes
+        // hit 64 different banks).  Same wavefront, LDS operations in order:
+        // the row-major reads above complete before these writes reuse the
+        // region.
+        const int t = l16 & 3, k4 = l16 >> 2;
+        const uint32_t sel_a = (t & 1) ? (uint32_t)((t + 4) | (t << 8)) : (uint32_t)(t | ((t + 4) << 8));
+        const uint32_t sel_f = t < 2 ? 0x05040100u : 0x01000504u;
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
-          for (int j = 0; j < TJ; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              wl[(16 * j + 4 * g + q) * 144 + 16 * i + l16] = (uint8_t)(code[i][j] >> (8 * q));
+          for (int j = 0; j < TJ; ++j) {
+            const uint32_t a0 = code[i][j];
+            const uint32_t a1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0xB1, 0xF, 0xF, false);
+            const uint32_t a2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0x4E, 0xF, 0xF, false);
+            const uint32_t a3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0x1B, 0xF, 0xF, false);
+            const uint32_t p01 = __builtin_amdgcn_perm(a1, a0, sel_a);
+            const uint32_t p23 = __builtin_amdgcn_perm(a3, a2, sel_a);
+            *reinterpret_cast<uint32_t*>(wl + (16 * j + 4 * g + t) * 144 + 16 * i + 4 * k4) =
+                __builtin_amdgcn_perm(p23, p01, sel_f);
+          }
         const int c = lane & 7, rr = lane >> 3;
 #pragma unroll
         for (int t = 0; t < WTN / 8; ++t) {
@@ -583,9 +605,9 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
           if (n + r >= N) continue;
           float x = deq(i, j, r, acc[i][j][r]);
           if (OUT8) {
-            const float xs = x * p.d_scale[0];
-            const uint8_t c = (uint8_t)((p.d_fp8 == 1 ? cvt4<0>(xs, 0.f, 0.f, 0.f)
-                                                      : cvt4<1>(xs, 0.f, 0.f, 0.f)) & 0xFFu);
+            const float xs = x * so;
+            const uint8_t c = (uint8_t)((p.d_fp8 == 1 ? cvt4<0, true>(xs, 0.f, 0.f, 0.f)
+                                                      : cvt4<1, true>(xs, 0.f, 0.f, 0.f)) & 0xFFu);
             reinterpret_cast<uint8_t*>(p.D)[m * p.ldd + n + r] = c;
             if (p.D_t) p.D_t[(n + r) * p.ldt + m] = c;
             const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;

@@ -243,7 +243,7 @@ hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
-  if (p.d_amax) {
+  if (p.d_amax && !p.amax_acc) {
     hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(p.d_amax), 1, 0u, s);
     if (e != hipSuccess) return e;
   }

@@ -62,8 +62,9 @@ struct GemmParams {
   const float* b_sinv;
   void* D;
   int d_f32;
-  float* d_amax;  // zeroed by the caller first when given
+  float* d_amax;  // max |output| is atomically max-ed into it
   int accumulate;
+  int amax_acc;             // 0: launch_gemm zeroes *d_amax first; 1: it does not
   int d_fp8;                // 0: BF16/FP32 output; 1: E4M3 codes; 2: E5M2 codes
   const float* d_scale;     // FP8 output: quantisation scale (1 float)
   uint8_t* D_t;             // FP8 output: optional transposed codes [N][ldt]

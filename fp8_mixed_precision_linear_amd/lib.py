@@ -43,7 +43,8 @@ class GemmArgs(C.Structure):
                 ("b_scale_inv", C.c_void_p),
                 ("D", C.c_void_p), ("d_dtype", C.c_int), ("d_amax", C.c_void_p),
                 ("accumulate", C.c_int),
-                ("d_scale", C.c_void_p), ("D_t", C.c_void_p), ("ldt", C.c_int64)]
+                ("d_scale", C.c_void_p), ("D_t", C.c_void_p), ("ldt", C.c_int64),
+                ("amax_accumulate", C.c_int)]
 
 
 def _load():
@@ -306,10 +307,12 @@ def fp8_cast_rowwise(x, fmt, y=None, scale_inv=None, y_t=None, scale_inv_t=None,
 
 
 def fp8_scaled_gemm(A, a_fmt, a_scaling, a_scale_inv, B, b_fmt, b_scaling, b_scale_inv, D,
-                    d_amax=None, accumulate=False, stream=None, d_scale=None, d_fmt=None, D_t=None):
+                    d_amax=None, accumulate=False, stream=None, d_scale=None, d_fmt=None, D_t=None,
+                    amax_accumulate=False):
     """D [M][N] = A [M][K] . B [N][K]^T with FP8 codes.  D is a bf16 or fp32
     tensor, or a uint8 tensor of FP8 codes (d_fmt E4M3 / E5M2, quantised
-    with d_scale; D_t optional [N][M] transposed codes)."""
+    with d_scale; D_t optional [N][M] transposed codes).  d_amax receives
+    max |output|, max-accumulated into its value with amax_accumulate."""
     M, K = A.shape
     N = B.shape[0]
     if B.shape[1] != K or tuple(D.shape) != (M, N):
@@ -339,5 +342,6 @@ def fp8_scaled_gemm(A, a_fmt, a_scaling, a_scale_inv, B, b_fmt, b_scaling, b_sca
                  _ptr(A, _U8, "A"), a_fmt, a_scaling, _ptr(a_scale_inv, _F32, "a_scale_inv"),
                  _ptr(B, _U8, "B"), b_fmt, b_scaling, _ptr(b_scale_inv, _F32, "b_scale_inv"),
                  _ptr(D, None, "D"), d_dtype, _ptr(d_amax, _F32, "d_amax"), 1 if accumulate else 0,
-                 _ptr(d_scale, _F32, "d_scale"), _ptr(D_t, _U8, "D_t"), M)
+                 _ptr(d_scale, _F32, "d_scale"), _ptr(D_t, _U8, "D_t"), M,
+                 1 if amax_accumulate else 0)
     _check("fp8_scaled_gemm", _L.fp8_scaled_gemm(C.byref(g), _stream(stream)))

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 7
+#define FP8LIN_ABI_VERSION 8
 
 /* [MPG] "The precision formats", "FP8 E4M3", "FP8 E5M2": E4M3 = 4 exponent
  * and 3 mantissa bits, range about 2^-9..448; E5M2 = 5 and 2, range about
@@ -388,7 +388,11 @@ fp8_status fp8_cast_rowwise(const void* x_bf16, int64_t rows, int64_t cols, fp8_
  * block promoted into the FP32 accumulator.  D is [M][ldd], BF16 (round
  * to nearest even) or FP32.  accumulate = 1 (FP32 output only) adds the
  * result to the existing D.  d_amax (nullable, 1 float) is overwritten with
- * max |D| of the stored output values.
+ * max |D| of the stored output values (a one-word fill runs ahead of the
+ * GEMM on the stream), or, with amax_accumulate = 1, max-accumulated into
+ * the value already there (no fill: the caller owns the slot, e.g. one
+ * cleared by fp8_amax_history_update_reset; calls that accumulate into one
+ * slot may overlap).
  * FP8 output (d_dtype FP8_OUT_E4M3 / FP8_OUT_E5M2; [TALK] outline
  * "quantisation fusions"; [MPG] "Transformer Engine internals": the cast
  * that the next layer would do, fused into this GEMM's epilogue): with v the
@@ -397,6 +401,7 @@ fp8_status fp8_cast_rowwise(const void* x_bf16, int64_t rows, int64_t cols, fp8_
  * the same codes transposed (the next layer's wgrad operand); d_amax is
  * max |v| (the amax of the quantised tensor, for its delayed scaling).
  * accumulate must be 0; requires ldt >= M when D_t is given.
+ * amax_accumulate: 0 or 1 (FP8_ERR_ARG otherwise), see d_amax.
  * Shape rules: M, N, K >= 0; K % 16 == 0 (tensor and row modes) or
  * K % 128 == 0 (block modes); lda, ldb >= K and multiples of 16; ldd >= N; A, B 16-byte
  * aligned; D 4-byte aligned.  K == 0 gives D = 0 (or D unchanged when
@@ -418,6 +423,7 @@ typedef struct {
   const float* d_scale;   /* FP8 output: quantisation scale (1 float); else ignored */
   uint8_t* D_t;           /* FP8 output: transposed codes [N][ldt], or NULL */
   int64_t ldt;
+  int amax_accumulate;    /* 1: max-accumulate into *d_amax instead of overwriting */
 } fp8_gemm_args;
 
 fp8_status fp8_scaled_gemm(const fp8_gemm_args* args, hipStream_t stream);

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.abi_version() == 7
+    assert L.abi_version() == 8
     for s in range(7):
         assert isinstance(L.status_string(s), str) and L.status_string(s)
     assert L.status_string(99) == "unknown status"
@@ -155,6 +155,8 @@ def test_gemm_validation(L):
     assert _gemm(L, d_dtype=3, d_scale=0x6000, accumulate=1) == 4
     assert _gemm(L, D_t=0x7000, ldt=64) == 6          # D_t with a BF16 output
     assert _gemm(L, d_dtype=2, d_scale=0x6000, D_t=0x7000, ldt=10) == 2
+    assert _gemm(L, amax_accumulate=2) == 6
+    assert _gemm(L, amax_accumulate=-1) == 6
 
 
 def test_binding_checks_buffer_sizes(L):

@@ -134,3 +134,35 @@ def test_gemm_fp8_output_full_size(O, L):
     assert np.array_equal(D8.np(), want)
     assert np.array_equal(Dt.np(), want.T)
     assert bits(am.np()[0]) == bits(np.max(np.abs(G)))
+
+
+@pytest.mark.parametrize("out", ["bf16", "e4m3"])
+@pytest.mark.parametrize("prior", ["below", "above"])
+def test_gemm_amax_accumulate(O, L, out, prior):
+    """amax_accumulate = 1: the GEMM max-accumulates max |output| into the
+    slot's existing value (no fill ahead of it); the output itself is the
+    same as with an overwritten amax.  A prior value below the result is
+    raised to it, one above it is kept."""
+    M, N, K = 512, 768, 384
+    say("gemm amax accumulate", out, prior)
+    rng = np.random.default_rng(5 + (out == "e4m3") + 2 * (prior == "above"))
+    A, B = rand_codes(rng, (M, K), 0), rand_codes(rng, (N, K), 0)
+    sa, sb = rand_scales(rng, 0, M, K), rand_scales(rng, 0, N, K)
+    dsc = dev(np.array([3.0], np.float32))
+    kw = dict(d_scale=dsc, d_fmt=0) if out == "e4m3" else {}
+    dt = torch.uint8 if out == "e4m3" else torch.bfloat16
+    D1, am1 = Guarded((M, N), dt), Guarded((1,), torch.float32)
+    L.fp8_scaled_gemm(dev(A), 0, 0, dev(sa), dev(B), 0, 0, dev(sb), D1.t, d_amax=am1.t, **kw)
+    torch.cuda.synchronize()
+    D1.check(); am1.check()
+    a1 = am1.np()[0]
+    assert a1 > 0
+    p0 = np.float32(a1 * 0.5 if prior == "below" else a1 * 2.0)
+    D2, am2 = Guarded((M, N), dt), Guarded((1,), torch.float32)
+    am2.t.fill_(float(p0))
+    L.fp8_scaled_gemm(dev(A), 0, 0, dev(sa), dev(B), 0, 0, dev(sb), D2.t, d_amax=am2.t,
+                      amax_accumulate=True, **kw)
+    torch.cuda.synchronize()
+    D2.check(); am2.check()
+    assert torch.equal(D1.t.view(torch.uint8), D2.t.view(torch.uint8))
+    assert bits(am2.np()[0]) == bits(max(a1, p0))
