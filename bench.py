@@ -479,7 +479,8 @@ def bench_extras(args, torch, L, datagen, dev, stream):
     k["cast_transpose_amax_e5m2_sr"] = time_launch(
         lambda: L.fp8_cast_sr(dy0, 1, scale[2:3], 1234, 0, y=dyq, y_t=dytq, amax_out=amax[2:3]), R)
     k["cast_e4m3"] = time_launch(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq), R)
-    k["amax"] = time_launch(lambda: L.fp8_amax(x0, amax[0:1]), R)
+    k["amax"] = time_launch(lambda: L.fp8_amax_acc(x0, amax[0:1]), R)
+    k["amax_overwrite"] = time_launch(lambda: L.fp8_amax(x0, amax[0:1]), R)
     k["history_update"] = time_launch(lambda: L.fp8_amax_history_update(hist[0:2], amax[0:2], 0, 0, 0, scale[0:2], sinv[0:2]), R)
     ewma = torch.zeros(3, dtype=torch.float32, device=dev)
     k["ewma_update"] = time_launch(lambda: L.fp8_amax_ewma_update(ewma, amax, 0.9, 0, 0, scale, sinv), R)
@@ -493,7 +494,8 @@ def bench_extras(args, torch, L, datagen, dev, stream):
         (k["gemm_fwd_tensor"] + k["cast_transpose_amax_acc_e4m3"]) * 1e6, 2)
     kernels["gemm_fwd_tensor_fp8out"]["vs_bf16_out"] = round(k["gemm_fwd_tensor_fp8out"] / k["gemm_fwd_tensor"], 3)
     for n, bpe in (("cast_transpose_amax_e4m3", 4), ("cast_transpose_amax_acc_e4m3", 4),
-                   ("cast_transpose_amax_e5m2_sr", 4), ("cast_e4m3", 3), ("amax", 2)):
+                   ("cast_transpose_amax_e5m2_sr", 4), ("cast_e4m3", 3), ("amax", 2),
+                   ("amax_overwrite", 2)):
         kernels[n] = {"gbs": round(bpe * nel / k[n] / 1e9, 1), "us": round(k[n] * 1e6, 2)}
     kernels["history_update"] = {"us": round(k["history_update"] * 1e6, 2)}
     kernels["ewma_update"] = {"us": round(k["ewma_update"] * 1e6, 2)}
@@ -534,16 +536,24 @@ def bench_extras(args, torch, L, datagen, dev, stream):
     kc["gemm_wgrad_tensor"] = time_cold(lambda: L.fp8_scaled_gemm(xtq, 0, 0, sinv[0:1], dytq, 1, 0, sinv[2:3], dw), R)
     kc["cast_transpose_amax_acc_e4m3"] = time_cold(lambda: L.fp8_cast_amax_acc(x0, 0, scale[0:1], amax[0:1], y=xq, y_t=xtq), R)
     kc["cast_e4m3"] = time_cold(lambda: L.fp8_cast_e4m3(x0, scale[0:1], y=xq), R)
-    kc["amax"] = time_cold(lambda: L.fp8_amax(x0, amax[0:1]), R)
+    kc["amax"] = time_cold(lambda: L.fp8_amax_acc(x0, amax[0:1]), R)
     kc["cast_rowwise_dy"] = time_cold(lambda: L.fp8_cast_rowwise(dy0, 1, dyq, sdr, dytq, sdc), R)
+    # the same bytes as the cast-transpose (2 B/elem read, 2 written) through
+    # a plain device copy: the practical ceiling of that traffic pattern
+    x0c = torch.empty_like(x0)
+    kc["copy_same_bytes"] = time_cold(lambda: x0c.copy_(x0), R)
     kernels_cold = {"note": "MALL evicted (512 MiB read) before every timed launch; median of "
                             f"{R} single launches, each bracketed by HIP events"}
     for n in ("gemm_fwd_tensor", "gemm_dgrad_tensor", "gemm_wgrad_tensor"):
         kernels_cold[n] = {"tflops": round(fl / kc[n] / 1e12, 2), "us": round(kc[n] * 1e6, 2)}
     for n, by in (("cast_transpose_amax_acc_e4m3", 4.0 * nel), ("cast_e4m3", 3.0 * nel),
-                  ("amax", 2.0 * nel), ("cast_rowwise_dy", 4.0 * nel + 4.0 * (T + DO))):
+                  ("amax", 2.0 * nel), ("cast_rowwise_dy", 4.0 * nel + 4.0 * (T + DO)),
+                  ("copy_same_bytes", 4.0 * nel)):
         kernels_cold[n] = {"gbs": round(by / kc[n] / 1e9, 1), "us": round(kc[n] * 1e6, 2),
                            "pct_hbm_peak": round(100 * by / kc[n] / 1e9 / HBM_PEAK_GBS, 2)}
+    kernels_cold["cast_transpose_amax_acc_e4m3"]["vs_copy_same_bytes"] = round(
+        kc["copy_same_bytes"] / kc["cast_transpose_amax_acc_e4m3"], 3)
+    del x0c
     del data
     blockwise = bench_blockwise(torch, L, datagen, dev, d_bf16, time_launch, time_cold, R)
     del flush

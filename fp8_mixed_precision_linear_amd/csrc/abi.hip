@@ -51,15 +51,27 @@ const char* fp8_status_string(fp8_status status) {
   return "unknown status";
 }
 
-fp8_status fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, float* amax,
-                    hipStream_t stream) {
+namespace {
+fp8_status amax_common(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, float* amax,
+                       int acc, hipStream_t stream) {
   if (rows < 0 || cols < 0 || ld < cols) return FP8_ERR_SHAPE;
   if (amax == nullptr) return FP8_ERR_NULL;
   if (rows > 0 && cols > 0 && x_bf16 == nullptr) return FP8_ERR_NULL;
   if (!aligned16(x_bf16) || !aligned4(amax)) return FP8_ERR_ALIGN;
   const uint16_t* x = static_cast<const uint16_t*>(x_bf16);
-  if (ld == cols || rows <= 1) return launched(launch_amax(x, rows * cols, amax, stream));
-  return launched(launch_amax_rows(x, rows, cols, ld, amax, stream));
+  if (ld == cols || rows <= 1) return launched(launch_amax(x, rows * cols, amax, acc, stream));
+  return launched(launch_amax_rows(x, rows, cols, ld, amax, acc, stream));
+}
+}  // namespace
+
+fp8_status fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, float* amax,
+                    hipStream_t stream) {
+  return amax_common(x_bf16, rows, cols, ld, amax, 0, stream);
+}
+
+fp8_status fp8_amax_acc(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                        float* amax_acc, hipStream_t stream) {
+  return amax_common(x_bf16, rows, cols, ld, amax_acc, 1, stream);
 }
 
 }  // extern "C"

@@ -14,11 +14,12 @@ int64_t device_cu_count();
 // Fill n dwords at p with v (a kernel, so it is safe inside graph capture).
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 
-// amax over n bf16 values (x 16-byte aligned); writes the result to *amax.
-hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t s);
-// amax over [rows][cols] bf16 with row stride ld >= cols (x 16-byte aligned).
+// amax over n bf16 values (x 16-byte aligned) into *amax: overwritten
+// (acc = 0, a fill kernel runs first) or max-accumulated (acc = 1).
+hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, int acc, hipStream_t s);
+// the same over [rows][cols] bf16 with row stride ld >= cols (x 16-byte aligned).
 hipError_t launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
-                            hipStream_t s);
+                            int acc, hipStream_t s);
 
 // pow2 != 0: power-of-two (exponent-bias) scales instead of fmax / amax.
 hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, int margin, int pow2,

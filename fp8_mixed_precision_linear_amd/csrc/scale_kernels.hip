@@ -223,8 +223,8 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
 }
 
 hipError_t launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
-                            hipStream_t s) {
-  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 1, 0u, s);
+                            int acc, hipStream_t s) {
+  hipError_t e = acc ? hipSuccess : launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 1, 0u, s);
   if (e != hipSuccess || rows == 0 || cols == 0) return e;
   int64_t blocks = rows < device_cu_count() ? rows : device_cu_count();
   hipLaunchKernelGGL(k_amax_rows, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, s, x, rows, cols,
@@ -232,8 +232,8 @@ hipError_t launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64
   return hipGetLastError();
 }
 
-hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, hipStream_t s) {
-  hipError_t e = launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 1, 0u, s);
+hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, int acc, hipStream_t s) {
+  hipError_t e = acc ? hipSuccess : launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 1, 0u, s);
   if (e != hipSuccess || n == 0) return e;
   int64_t nv = n >> 3;
   // a persistent grid of at most one 1024-thread workgroup per CU: each

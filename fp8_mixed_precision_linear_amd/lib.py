@@ -56,6 +56,7 @@ def _load():
         "fp8_abi_version": (i32, []),
         "fp8_status_string": (C.c_char_p, [i32]),
         "fp8_amax": (i32, [vp, i64, i64, i64, vp, vp]),
+        "fp8_amax_acc": (i32, [vp, i64, i64, i64, vp, vp]),
         "fp8_compute_scale": (i32, [vp, i64, i32, i32, vp, vp, vp]),
         "fp8_compute_scale_pow2": (i32, [vp, i64, i32, i32, vp, vp, vp]),
         "fp8_amax_history_update": (i32, [vp, i64, i64, vp, i32, i32, i32, vp, vp, vp]),
@@ -142,9 +143,7 @@ def _rc(x):
     return x.shape[0], cols
 
 
-def fp8_amax(x, amax, stream=None):
-    """amax of x: a contiguous tensor, or a 2-D view whose rows are strided
-    (row stride >= number of columns, unit column stride)."""
+def _amax(fn, x, amax, stream):
     _need(amax, 1, "amax")
     if x.dim() == 2 and not x.is_contiguous() and x.stride(1) == 1 and x.stride(0) >= x.shape[1]:
         rows, cols, ld = x.shape[0], x.shape[1], x.stride(0)
@@ -155,7 +154,20 @@ def fp8_amax(x, amax, stream=None):
         rows, cols = _rc(x)
         ld = cols
         xp = _ptr(x, _BF16, "x")
-    _check("fp8_amax", _L.fp8_amax(xp, rows, cols, ld, _ptr(amax, _F32, "amax"), _stream(stream)))
+    _check(fn.__name__, fn(xp, rows, cols, ld, _ptr(amax, _F32, "amax"), _stream(stream)))
+
+
+def fp8_amax(x, amax, stream=None):
+    """amax of x: a contiguous tensor, or a 2-D view whose rows are strided
+    (row stride >= number of columns, unit column stride)."""
+    _amax(_L.fp8_amax, x, amax, stream)
+
+
+def fp8_amax_acc(x, amax_acc, stream=None):
+    """fp8_amax max-accumulated into amax_acc (no fill ahead of the kernel)."""
+    if amax_acc is None:
+        raise ValueError("amax_acc is required")
+    _amax(_L.fp8_amax_acc, x, amax_acc, stream)
 
 
 def _compute_scale(fn, amax, fmt, margin, scale, scale_inv, stream):

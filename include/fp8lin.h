@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 8
+#define FP8LIN_ABI_VERSION 9
 
 /* [MPG] "The precision formats", "FP8 E4M3", "FP8 E5M2": E4M3 = 4 exponent
  * and 3 mantissa bits, range about 2^-9..448; E5M2 = 5 and 2, range about
@@ -106,6 +106,20 @@ const char* fp8_status_string(fp8_status status);
  * ---------------------------------------------------------------------- */
 fp8_status fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, float* amax,
                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_amax_acc -- fp8_amax with the result max-accumulated into *amax_acc
+ * instead of overwriting it: one kernel, no fill ahead of it.
+ * [MPG] "Delayed scaling (the default recipe)": the step's amax goes into
+ * the tensor's history slot, which fp8_amax_history_update_reset clears
+ * after reading it, so the next step accumulates into zero.
+ *   amax_acc  1 float (device), required: on return max(old value, max |x|)
+ *             (as binary32 bit patterns of |value|: a NaN element makes it
+ *             NaN).  Calls that accumulate into one slot may overlap.
+ * Other arguments and errors as fp8_amax.
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_amax_acc(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld,
+                        float* amax_acc, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * fp8_compute_scale -- current scaling: scale = fl32(fmax / amax) * 2^-margin,

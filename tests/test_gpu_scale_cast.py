@@ -55,6 +55,28 @@ def test_amax_specials(O, L):
         assert bits(out.cpu().numpy())[0] == bits(O.amax(x)), hex(special)
 
 
+@pytest.mark.parametrize("shape,ld", [((512, 1024), 1024), ((33, 77), 77), ((64, 300), 512), ((0, 5), 5)])
+@pytest.mark.parametrize("prior", ["below", "above", "zero"])
+def test_amax_acc(O, L, shape, ld, prior):
+    """fp8_amax_acc: max(prior value, max |x|) in the slot, contiguous and
+    strided rows; an empty tensor leaves the slot as it was."""
+    rows, cols = shape
+    say("amax acc", shape, ld, prior)
+    rng = np.random.default_rng(rows * 7 + ld + len(prior))
+    big = datagen.normal(rng, (rows, ld), 2.0)
+    view = np.ascontiguousarray(big[:, :cols])
+    a = np.float32(O.amax(view)) if view.size else np.float32(0)
+    p0 = {"below": a * np.float32(0.5), "above": a * np.float32(2) + np.float32(1),
+          "zero": np.float32(0)}[prior]
+    out = Guarded((1,), torch.float32)
+    out.t.fill_(float(p0))
+    d = dev_bf16(big) if big.size else torch.empty((rows, ld), dtype=torch.bfloat16, device="cuda")
+    L.fp8_amax_acc(d[:, :cols], out.t)
+    torch.cuda.synchronize()
+    out.check()
+    assert bits(out.np())[0] == bits(max(a, p0))
+
+
 @pytest.mark.parametrize("shape,ld,c0", [((64, 300), 512, 8), ((33, 77), 101, 0), ((1000, 8), 16, 0),
                                          ((5, 4096), 4104, 8), ((2, 1), 9, 0), ((3, 5), 11, 0)])
 def test_amax_strided_rows(O, L, shape, ld, c0):
