@@ -300,6 +300,23 @@ void o_cast(const uint16_t* x, int64_t n, float s, int fmt, uint8_t* y) {
   }
 }
 
+/* Saturation and underflow counts of the per-tensor cast, the overflow /
+ * underflow ratios of the diagnostic dashboard ([MPG] "Numerical-failure
+ * taxonomy > A diagnostic dashboard", quantities per layer).  Reading:
+ * with v = fl32(x * s) as in o_cast, an element saturates when |v| is
+ * beyond the format's largest finite value (Inf included, NaN not); it
+ * underflows when x is nonzero and its code is +-0 -- decided by the
+ * encoder itself, not by a threshold.  counts[0] += saturated,
+ * counts[1] += underflowed. */
+void o_cast_stats(const uint16_t* x, int64_t n, float s, int fmt, uint64_t counts[2]) {
+  const double mx = o_fp8_max(fmt);
+  for (int64_t i = 0; i < n; ++i) {
+    const float p = o_bf16_to_f32(x[i]) * s;
+    if (!isnan(p) && fabs((double)p) > mx) counts[0] += 1;
+    if ((x[i] & 0x7FFFu) != 0 && (o_fp8_encode(p, fmt) & 0x7Fu) == 0) counts[1] += 1;
+  }
+}
+
 /* Cast plus transpose: y_t[c][r] = y[r][c] for x laid out [rows][cols].
  * Per-tensor scaling makes the transposed bytes the same bytes. */
 void o_cast_transpose(const uint16_t* x, int64_t rows, int64_t cols, float s,

@@ -85,6 +85,8 @@ def lib():
                                        C.c_int, C.c_int, C.c_void_p, C.c_void_p]
         L.o_cast.restype = None
         L.o_cast.argtypes = [C.c_void_p, C.c_int64, C.c_float, C.c_int, C.c_void_p]
+        L.o_cast_stats.restype = None
+        L.o_cast_stats.argtypes = [C.c_void_p, C.c_int64, C.c_float, C.c_int, C.c_void_p]
         L.o_cast_transpose.restype = None
         L.o_cast_transpose.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_float, C.c_int,
                                        C.c_void_p, C.c_void_p]
@@ -288,6 +290,14 @@ def cast(x_bf16, s: float, fmt: int) -> np.ndarray:
     with ThreadPoolExecutor(max(1, len(chunks))) as ex:
         list(ex.map(one, chunks))
     return y
+
+
+def cast_stats(x_bf16, s: float, fmt: int) -> tuple:
+    """(saturated, underflowed) element counts of the per-tensor cast."""
+    x = _c(x_bf16, np.uint16).reshape(-1)
+    out = np.zeros(2, np.uint64)
+    lib().o_cast_stats(_p(x), x.size, float(np.float32(s)), fmt, _p(out))
+    return int(out[0]), int(out[1])
 
 
 def cast_transpose(x_bf16, s: float, fmt: int):

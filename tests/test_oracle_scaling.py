@@ -173,6 +173,44 @@ def test_cast_all_bf16_patterns_vs_library(O, fmt):
         assert np.all((ours[~keep] & 0x7F) == 0x7F)
 
 
+# the largest magnitude that encodes to +-0 (half the smallest subnormal,
+# which ties to the even code 0)
+UNDER = {0: 2.0 ** -10, 1: 2.0 ** -17}
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_cast_stats_all_bf16_patterns(O, fmt):
+    """Saturation / underflow counts over every bf16 pattern and a set of
+    scales, against thresholds on numpy's float32 product (the oracle counts
+    underflow with its encoder, so this pins the encoder's zero region and
+    the |v| > max rule independently)."""
+    x = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    xf = datagen.bf16_to_f32(x)
+    for s in [1.0, 2.0 ** -12, 2.0 ** 9, np.float32(3.0), np.float32(0.7), np.float32(1e-30),
+              np.float32(FMAX[fmt] / 7.5)]:
+        with np.errstate(over="ignore", invalid="ignore", under="ignore"):
+            v = xf * np.float32(s)
+        a = np.abs(v.astype(np.float64))
+        sat = int(np.sum(~np.isnan(v) & (a > FMAX[fmt])))
+        und = int(np.sum(((x & 0x7FFF) != 0) & ~np.isnan(xf) & (a <= UNDER[fmt])))
+        assert O.cast_stats(x, s, fmt) == (sat, und), s
+
+
+def test_cast_stats_hand_cases(O):
+    one = np.array([0x3F80], np.uint16)            # 1.0
+    nxt = np.float32(2.0 ** -10) * np.float32(1 + 2.0 ** -23)
+    assert O.cast_stats(one, 2.0 ** -10, 0) == (0, 1)      # the tie goes to 0
+    assert O.cast_stats(one, nxt, 0) == (0, 0)             # just above: code 1
+    assert O.cast_stats(one, 2.0 ** -17, 1) == (0, 1)
+    assert O.cast_stats(one, 448.0, 0) == (0, 0)           # the max itself is representable
+    assert O.cast_stats(one, np.float32(448.0) * np.float32(1 + 2.0 ** -23), 0) == (1, 0)
+    assert O.cast_stats(one, 57344.0, 1) == (0, 0)
+    specials = np.array([0x7F80, 0xFF80, 0x7FC0, 0x0000, 0x8000, 0x0001], np.uint16)
+    # +-Inf saturate; NaN and +-0 count nowhere; the smallest bf16 subnormal underflows
+    assert O.cast_stats(specials, 1.0, 0) == (2, 1)
+    assert O.cast_stats(one, 0.0, 0) == (0, 1)             # a nonzero input flushed by s = 0
+
+
 def test_cast_transpose_is_transpose(O):
     rng = np.random.default_rng(2)
     x = datagen.normal(rng, (67, 131), 3.0)
