@@ -557,8 +557,60 @@ def bench_extras(args, torch, L, datagen, dev, stream):
     del data
     blockwise = bench_blockwise(torch, L, datagen, dev, d_bf16, time_launch, time_cold, R)
     del flush
-    return {"delayed4096": delayed4096, "kernels": kernels, "kernels_cold": kernels_cold,
+    c1 = bench_config1(torch, L, datagen, dev, d_bf16, stream)
+    return {"config1": c1, "delayed4096": delayed4096, "kernels": kernels, "kernels_cold": kernels_cold,
             "rowwise": rowwise, "blockwise": blockwise}
+
+
+def bench_config1(torch, L, datagen, dev, d_bf16, stream):
+    """Latency of the per-tensor current-scaling forward at X 256x512,
+    W 512x512: amax of X and W (max-accumulated into a zeroed pair), both
+    scales in one call, the cast of X, the transposed cast of W, the GEMM
+    with BF16 output -- 7 kernels, timed as a replayed HIP graph and as
+    eager calls through the binding."""
+    c = datagen.config1()
+    x, w = d_bf16(c["x"]), d_bf16(c["w"])
+    u8 = dict(dtype=torch.uint8, device=dev)
+    amax = torch.zeros(2, dtype=torch.float32, device=dev)
+    s, si = torch.ones(2, dtype=torch.float32, device=dev), torch.ones(2, dtype=torch.float32, device=dev)
+    xq, wtq = torch.empty((256, 512), **u8), torch.empty((512, 512), **u8)
+    y = torch.empty((256, 512), dtype=torch.bfloat16, device=dev)
+
+    def fwd():
+        amax.zero_()
+        L.fp8_amax_acc(x, amax[0:1])
+        L.fp8_amax_acc(w, amax[1:2])
+        L.fp8_compute_scale(amax, 0, 0, s, si)
+        L.fp8_cast_e4m3(x, s[0:1], y=xq)
+        L.fp8_cast_e4m3(w, s[1:2], y_t=wtq)
+        L.fp8_scaled_gemm(xq, 0, 0, si[0:1], wtq, 0, 0, si[1:2], y)
+
+    n = 100
+    g = capture(torch, lambda: [fwd() for _ in range(n)])
+    g.replay()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) / n)
+    del g
+    for _ in range(5):
+        fwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fwd()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / n
+    return {"workload": "per-tensor current-scaling forward, X 256x512 (4 outlier columns x50), "
+                        "W 512x512: amax x2, scales, cast, cast-transpose, GEMM (7 kernels)",
+            "us_per_forward_graph": round(best * 1e3, 2),
+            "us_per_forward_eager": round(eager * 1e6, 2),
+            "gflop": round(2.0 * 256 * 512 * 512 / 1e9, 3)}
 
 
 def bench_blockwise(torch, L, datagen, dev, d_bf16, time_launch, time_cold, R):

@@ -64,6 +64,18 @@ fp8_status amax_common(const void* x_bf16, int64_t rows, int64_t cols, int64_t l
 }
 }  // namespace
 
+fp8_status fp8_cast_stats(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                          const float* scale, uint64_t* counts, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
+  if (!fmt_ok(fmt)) return FP8_ERR_ARG;
+  if (counts == nullptr) return FP8_ERR_NULL;
+  if (rows > 0 && cols > 0 && (x_bf16 == nullptr || scale == nullptr)) return FP8_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned4(scale) || (reinterpret_cast<uintptr_t>(counts) & 7u) != 0)
+    return FP8_ERR_ALIGN;
+  return launched(launch_cast_stats(static_cast<const uint16_t*>(x_bf16), rows * cols, scale, fmt,
+                                    counts, stream));
+}
+
 fp8_status fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, float* amax,
                     hipStream_t stream) {
   return amax_common(x_bf16, rows, cols, ld, amax, 0, stream);

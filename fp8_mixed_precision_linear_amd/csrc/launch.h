@@ -21,6 +21,11 @@ hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, int acc, hipSt
 hipError_t launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
                             int acc, hipStream_t s);
 
+// Saturated / underflowed element counts of the per-tensor cast of n bf16
+// values (x 16-byte aligned), added to counts[0] / counts[1].
+hipError_t launch_cast_stats(const uint16_t* x, int64_t n, const float* scale, int fmt,
+                             uint64_t* counts, hipStream_t s);
+
 // pow2 != 0: power-of-two (exponent-bias) scales instead of fmax / amax.
 hipError_t launch_compute_scale(const float* amax, int64_t n, int fmt, int margin, int pow2,
                                 float* scale, float* scale_inv, hipStream_t s);

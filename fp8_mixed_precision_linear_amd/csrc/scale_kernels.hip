@@ -71,6 +71,61 @@ __global__ void __launch_bounds__(kAmaxThreads) k_amax(const uint16_t* __restric
   block_max_to(amax, m);
 }
 
+// Saturation and underflow counts of the per-tensor cast, the overflow /
+// underflow ratios of the diagnostic dashboard ([MPG] "Numerical-failure
+// taxonomy > A diagnostic dashboard").  With v = fl32(x * s) as the cast
+// computes it, an element saturates when |v| > the format's largest finite
+// value (Inf included, NaN not) and underflows when x != 0 and |v| <= half
+// the smallest subnormal step (2^-10 for E4M3, 2^-17 for E5M2): the RNE
+// encode of such a value is +-0, the tie at exactly half a step going to
+// the even code 0.  Both tests on the binary32 bit pattern of |v|.  Counts
+// per thread, a block sum, and two 64-bit atomics per block into counts[].
+template <int FMT>
+__global__ void __launch_bounds__(kAmaxThreads) k_cast_stats(const uint16_t* __restrict__ x, int64_t n,
+                                                             const float* __restrict__ scale,
+                                                             unsigned long long* __restrict__ counts) {
+  constexpr uint32_t kMaxBits = FMT == 0 ? 0x43E00000u : 0x47600000u;    // 448, 57344
+  constexpr uint32_t kUnderBits = FMT == 0 ? 0x3A800000u : 0x37000000u;  // 2^-10, 2^-17
+  const float s = *scale;
+  uint32_t sat = 0, und = 0;
+  auto one = [&](uint32_t h) {
+    const uint32_t a = __float_as_uint(__uint_as_float(h << 16) * s) & 0x7FFFFFFFu;
+    sat += (uint32_t)((a > kMaxBits) & (a <= 0x7F800000u));
+    und += (uint32_t)(((h & 0x7FFFu) != 0u) & (a <= kUnderBits));
+  };
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int64_t nv = n >> 3;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nv; i += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = i + u * stride < nv ? ld_nt16(xv + i + u * stride) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { one(w[k] & 0xFFFFu); one(w[k] >> 16); }
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) one(x[(nv << 3) + threadIdx.x]);
+  // block sums (zero inputs -- padded loads and +0 -- count nowhere)
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    sat += __shfl_xor(sat, off, 64);
+    und += __shfl_xor(und, off, 64);
+  }
+  __shared__ uint32_t part[2][kAmaxThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { part[0][wave] = sat; part[1][wave] = und; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long a = 0, b = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) { a += part[0][w]; b += part[1][w]; }
+    if (a) atomicAdd(&counts[0], a);
+    if (b) atomicAdd(&counts[1], b);
+  }
+}
+
 // Current scaling: one thread per tensor.
 __global__ void k_compute_scale(const float* __restrict__ amax, int64_t n, float fmax, int margin,
                                 int pow2, float* __restrict__ scale,
@@ -243,6 +298,21 @@ hipError_t launch_amax(const uint16_t* x, int64_t n, float* amax, int acc, hipSt
   if (blocks < 1) blocks = 1;
   if (blocks > device_cu_count()) blocks = device_cu_count();
   hipLaunchKernelGGL(k_amax, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, s, x, n, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_stats(const uint16_t* x, int64_t n, const float* scale, int fmt,
+                             uint64_t* counts, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t nv = n >> 3;
+  int64_t blocks = (nv + 4 * kAmaxThreads - 1) / (4 * kAmaxThreads);
+  if (blocks < 1) blocks = 1;
+  if (blocks > device_cu_count()) blocks = device_cu_count();
+  auto c = reinterpret_cast<unsigned long long*>(counts);
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_cast_stats<0>, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, s, x, n, scale, c);
+  else
+    hipLaunchKernelGGL(k_cast_stats<1>, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, s, x, n, scale, c);
   return hipGetLastError();
 }
 

@@ -57,6 +57,7 @@ def _load():
         "fp8_status_string": (C.c_char_p, [i32]),
         "fp8_amax": (i32, [vp, i64, i64, i64, vp, vp]),
         "fp8_amax_acc": (i32, [vp, i64, i64, i64, vp, vp]),
+        "fp8_cast_stats": (i32, [vp, i64, i64, i32, vp, vp, vp]),
         "fp8_compute_scale": (i32, [vp, i64, i32, i32, vp, vp, vp]),
         "fp8_compute_scale_pow2": (i32, [vp, i64, i32, i32, vp, vp, vp]),
         "fp8_amax_history_update": (i32, [vp, i64, i64, vp, i32, i32, i32, vp, vp, vp]),
@@ -161,6 +162,18 @@ def fp8_amax(x, amax, stream=None):
     """amax of x: a contiguous tensor, or a 2-D view whose rows are strided
     (row stride >= number of columns, unit column stride)."""
     _amax(_L.fp8_amax, x, amax, stream)
+
+
+def fp8_cast_stats(x, fmt, scale, counts, stream=None):
+    """Adds the cast's saturated / underflowed element counts of x (scale
+    scale[0], format fmt) to counts[0] / counts[1] (an int64 tensor of 2)."""
+    rows, cols = _rc(x)
+    _need(scale, 1, "scale")
+    if counts is None or counts.dtype != torch.int64 or counts.numel() < 2 or not counts.is_cuda:
+        raise ValueError("counts must be a GPU int64 tensor of 2")
+    _check("fp8_cast_stats",
+           _L.fp8_cast_stats(_ptr(x, _BF16, "x"), rows, cols, fmt, _ptr(scale, _F32, "scale"),
+                             counts.data_ptr(), _stream(stream)))
 
 
 def fp8_amax_acc(x, amax_acc, stream=None):

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FP8LIN_ABI_VERSION 9
+#define FP8LIN_ABI_VERSION 10
 
 /* [MPG] "The precision formats", "FP8 E4M3", "FP8 E5M2": E4M3 = 4 exponent
  * and 3 mantissa bits, range about 2^-9..448; E5M2 = 5 and 2, range about
@@ -106,6 +106,26 @@ const char* fp8_status_string(fp8_status status);
  * ---------------------------------------------------------------------- */
 fp8_status fp8_amax(const void* x_bf16, int64_t rows, int64_t cols, int64_t ld, float* amax,
                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_cast_stats -- saturation and underflow counts of the per-tensor cast
+ * (fp8_cast_e4m3 / e5m2 with the same scale), for the diagnostic
+ * dashboard's overflow and underflow ratios per layer.
+ * [MPG] "Numerical-failure taxonomy > A diagnostic dashboard".
+ * With v = fl32(x * scale[0]) as the cast computes it:
+ *   counts[0] += number of elements with |v| beyond the format's largest
+ *                finite value (448 / 57344; +-Inf included, NaN not);
+ *   counts[1] += number of nonzero elements x whose code is +-0 (|v| at
+ *                most half the smallest subnormal step: 2^-10 / 2^-17).
+ *   x_bf16  [rows][cols] bf16, contiguous, 16-byte aligned.
+ *   scale   1 float (device).
+ *   counts  2 uint64 (device), 8-byte aligned; added to, never cleared.
+ * Reads x once (2 B/elem); writes nothing else.
+ * Errors: FP8_ERR_NULL (counts; x or scale with rows*cols > 0),
+ * FP8_ERR_SHAPE, FP8_ERR_ALIGN, FP8_ERR_ARG (fmt).
+ * ---------------------------------------------------------------------- */
+fp8_status fp8_cast_stats(const void* x_bf16, int64_t rows, int64_t cols, fp8_format fmt,
+                          const float* scale, uint64_t* counts, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * fp8_amax_acc -- fp8_amax with the result max-accumulated into *amax_acc

@@ -29,7 +29,7 @@ def test_header_declares_the_layer_calls():
               "fp8_cast_e5m2", "fp8_cast_block", "fp8_scaled_gemm", "fp8_abi_version",
               "fp8_status_string", "fp8_compute_scale_pow2", "fp8_amax_history_update_pow2",
               "fp8_cast_block_pow2", "fp8_cast_rowwise", "fp8_cast_sr", "fp8_amax_ewma_update",
-              "fp8_cast_sr_state", "fp8_amax_acc"]:
+              "fp8_cast_sr_state", "fp8_amax_acc", "fp8_cast_stats"]:
         assert f in fns
 
 
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.abi_version() == 9
+    assert L.abi_version() == 10
     for s in range(7):
         assert isinstance(L.status_string(s), str) and L.status_string(s)
     assert L.status_string(99) == "unknown status"
@@ -58,6 +58,15 @@ def test_host_validation_before_launch(L):
     assert f.fp8_amax_acc(C.c_void_p(0x1000), 4, 4, 4, None, None) == 1
     assert f.fp8_amax_acc(C.c_void_p(0x1000), 4, 8, 7, C.c_void_p(0x2000), None) == 2
     assert f.fp8_amax_acc(C.c_void_p(0x1002), 4, 4, 4, C.c_void_p(0x2000), None) == 3
+    x, s, c = C.c_void_p(0x1000), C.c_void_p(0x2000), C.c_void_p(0x3000)
+    assert f.fp8_cast_stats(x, 4, 8, 0, s, None, None) == 1          # counts
+    assert f.fp8_cast_stats(None, 4, 8, 0, s, c, None) == 1          # x
+    assert f.fp8_cast_stats(x, 4, 8, 0, None, c, None) == 1          # scale
+    assert f.fp8_cast_stats(x, -1, 8, 0, s, c, None) == 2
+    assert f.fp8_cast_stats(x, 4, 8, 2, s, c, None) == 6
+    assert f.fp8_cast_stats(C.c_void_p(0x1008), 4, 8, 0, s, c, None) == 3
+    assert f.fp8_cast_stats(x, 4, 8, 0, s, C.c_void_p(0x3004), None) == 3
+    assert f.fp8_cast_stats(None, 0, 8, 0, None, c, None) == 0       # empty: nothing to do
     # scale: bad format / margin / n
     assert f.fp8_compute_scale(None, 1, 7, 0, None, None, None) == 6
     assert f.fp8_compute_scale(None, 1, 0, 99, None, None, None) == 6

@@ -55,6 +55,56 @@ def test_amax_specials(O, L):
         assert bits(out.cpu().numpy())[0] == bits(O.amax(x)), hex(special)
 
 
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_cast_stats_all_bf16_patterns(O, L, fmt):
+    """Saturation / underflow counts over all 65,536 bf16 patterns (NaNs
+    included) and a set of scales, equal to the oracle's (which decides
+    underflow with its encoder)."""
+    x = dev_bf16(ALL_BF16.reshape(256, 256))
+    fmax = 448.0 if fmt == 0 else 57344.0
+    for s in [1.0, 2.0 ** -12, 2.0 ** 9, 3.0, 0.7, 1e-30, fmax / 7.5, 0.0]:
+        say("cast stats all-bf16", fmt, s)
+        counts = torch.zeros(2, dtype=torch.int64, device="cuda")
+        L.fp8_cast_stats(x, fmt, torch.tensor([s], dtype=torch.float32, device="cuda"), counts)
+        torch.cuda.synchronize()
+        assert tuple(counts.cpu().tolist()) == O.cast_stats(ALL_BF16, np.float32(s), fmt), s
+
+
+@pytest.mark.parametrize("shape", [(33, 77), (1, 1), (257, 129), (1024, 1024), (0, 7)])
+def test_cast_stats_shapes_accumulate(O, L, shape):
+    """Ragged sizes (tails of n % 8 values), counts added to what the slots
+    hold (two calls give twice the counts)."""
+    say("cast stats", shape)
+    rng = np.random.default_rng(shape[0] * 3 + shape[1])
+    x = datagen.student_t3(rng, shape, 1.0) if shape[0] else np.zeros(shape, np.uint16)
+    s = np.float32(60.0)
+    want = O.cast_stats(x, s, 0)
+    counts = torch.zeros(2, dtype=torch.int64, device="cuda")
+    d = dev_bf16(x) if x.size else torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    sc = torch.tensor([s], dtype=torch.float32, device="cuda")
+    L.fp8_cast_stats(d, 0, sc, counts)
+    L.fp8_cast_stats(d, 0, sc, counts)
+    torch.cuda.synchronize()
+    assert tuple(counts.cpu().tolist()) == (2 * want[0], 2 * want[1])
+    if shape == (1024, 1024):
+        assert want[0] > 0 and want[1] > 0   # both rules exercised
+
+
+def test_cast_stats_config1(O, L):
+    """The per-tensor current-scaling forward's activation (outlier columns)
+    at its own scale (448 / amax: at most the amax element itself can land
+    an ulp above the max)."""
+    c = datagen.config1()
+    x = c["x"]
+    s, _, _ = O.compute_scale(O.amax(x), 0)
+    counts = torch.zeros(2, dtype=torch.int64, device="cuda")
+    L.fp8_cast_stats(dev_bf16(x), 0, torch.tensor([s], dtype=torch.float32, device="cuda"), counts)
+    torch.cuda.synchronize()
+    got = tuple(counts.cpu().tolist())
+    assert got == O.cast_stats(x, s, 0)
+    assert got[0] <= 1
+
+
 @pytest.mark.parametrize("shape,ld", [((512, 1024), 1024), ((33, 77), 77), ((64, 300), 512), ((0, 5), 5)])
 @pytest.mark.parametrize("prior", ["below", "above", "zero"])
 def test_amax_acc(O, L, shape, ld, prior):
