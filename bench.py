@@ -706,7 +706,8 @@ def gemm_traffic(cls):
             t = json.load(f)
         if t.get("sources_sha256") != traffic_sources_sha256():
             return None
-        return round(t["kernels"][cls]["traffic_bytes"])
+        k = t["kernels"][cls]
+        return round(k["traffic_bytes"] / k["launches"])
     except (OSError, KeyError, ValueError):
         return None
 
