@@ -466,11 +466,13 @@ def bench_extras(args, torch, L, datagen, dev, stream):
     # max-accumulated into the slot as in a delayed-scaling step), timed
     # right after the same GEMM with a BF16 output; then with the amax
     # overwritten (a one-word fill launched ahead of the GEMM)
-    k["gemm_fwd_tensor"] = min(k["gemm_fwd_tensor"], time_launch(
-        lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y), R))
-    k["gemm_fwd_tensor_fp8out"] = time_launch(
-        lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y8, d_amax=am8,
-                                  d_scale=scale[0:1], d_fmt=0, D_t=y8t, amax_accumulate=True), R)
+    fp8out = (lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y8, d_amax=am8,
+                                        d_scale=scale[0:1], d_fmt=0, D_t=y8t, amax_accumulate=True))
+    k["gemm_fwd_tensor_fp8out"] = float("inf")
+    for _ in range(2):   # interleaved with the BF16-output GEMM, best of each
+        k["gemm_fwd_tensor"] = min(k["gemm_fwd_tensor"], time_launch(
+            lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y), R))
+        k["gemm_fwd_tensor_fp8out"] = min(k["gemm_fwd_tensor_fp8out"], time_launch(fp8out, R))
     k["gemm_fwd_tensor_fp8out_amax_overwrite"] = time_launch(
         lambda: L.fp8_scaled_gemm(xq, 0, 0, sinv[0:1], wtq, 0, 0, sinv[1:2], y8, d_amax=am8,
                                   d_scale=scale[0:1], d_fmt=0, D_t=y8t), R)
@@ -898,7 +900,7 @@ def cpu_baseline(step_flops, step_cast_bytes):
     """The oracle, as it stands, on a bounded sample of the step: the O
     linear (8192 tokens, 8192 -> 8192) in both passes -- the casts of X, W
     and dY at full size (per-tensor with transpose, and block-wise) and the
-    three GEMMs of each pass on 48 of 8192 output rows -- extrapolated to
+    three GEMMs of each pass on 192 of 8192 output rows -- extrapolated to
     the step: GEMM time by FLOPs, cast time by algorithmic bytes."""
     from fp8_mixed_precision_linear_amd import datagen
     from oracle import oracle as O
@@ -917,7 +919,7 @@ def cpu_baseline(step_flops, step_cast_bytes):
     bd = O.cast_block(dy, 1, O.S1x128, want_y=True, want_t=True)
     t_cast = time.perf_counter() - t0
     cast_bytes = 2 * 4.0 * (T * DI + DI * DO + T * DO)   # both passes, both orientations
-    rows = np.arange(48, dtype=np.int64)
+    rows = np.arange(192, dtype=np.int64)
     t1 = time.perf_counter()
     one = lambda v: np.array([v], np.float32)
     xt, dt_, wt = (np.ascontiguousarray(a.T) for a in (xq, dq, wq))
@@ -928,12 +930,12 @@ def cpu_baseline(step_flops, step_cast_bytes):
     O.gemm(bd["y"], 1, 1, bd["sinv"], bw["y"], 0, 2, bw["sinv"], ms=rows)
     O.gemm(bx["y_t"], 0, 1, bx["sinv_t"], bd["y_t"], 1, 1, bd["sinv_t"], ms=rows)
     t_gemm_sample = time.perf_counter() - t1
-    sample_flops = 6 * 2.0 * len(rows) * DO * DI   # each GEMM: 48 rows x 8192 x 8192
+    sample_flops = 6 * 2.0 * len(rows) * DO * DI   # each GEMM: 192 rows x 8192 x 8192
     t_step = t_gemm_sample * step_flops / sample_flops + t_cast * step_cast_bytes / cast_bytes
     return {"value": round(step_flops / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": O.nthreads(),
             "kind": "oracle", "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": "the O linear (8192 tokens, 8192 -> 8192) in both passes: amax, scales and "
-                      f"casts of X, W, dY at full size ({t_cast:.2f}s), the six GEMMs on 48 of "
+                      f"casts of X, W, dY at full size ({t_cast:.2f}s), the six GEMMs on {len(rows)} of "
                       f"8192 output rows ({t_gemm_sample:.2f}s); extrapolated to the step by FLOPs "
                       "(GEMMs) and algorithmic bytes (casts)",
             "step_s_extrapolated": round(t_step, 1)}
