@@ -110,6 +110,12 @@ __device__ __forceinline__ void dma16(uint32_t m0, uint32_t off, i32x4 rsrc) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(m0), "v"(off), "s"(rsrc) : "memory", "m0");
 }
+// The same with the instruction's scalar offset added (the K offset of a
+// step, so the lane offsets stay loop-invariant).
+__device__ __forceinline__ void dma16s(uint32_t m0, uint32_t off, i32x4 rsrc, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(off), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
 // 4 bytes per lane into LDS at m0 + 4 * lane.
 __device__ __forceinline__ void dma4(uint32_t m0, uint32_t off, i32x4 rsrc) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
@@ -175,15 +181,30 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   auto load_stage = [&](int kb, uint8_t* base) {
     const int k0 = kb * BK;
     const uint32_t lb = lds_addr(base);
+    // Block scales make K a multiple of the step: every chunk of a step is
+    // inside K, and the step's K offset goes in the scalar offset (no
+    // per-step VALU work beside the promotion; measured 1-2% on the
+    // transformer-block shapes, while the per-tensor kernels, which also
+    // take a K tail, gained nothing)
+    if constexpr (BLOCK) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int row = lrow + 8 * it;
-      const int kc = k0 + 16 * ((lane & 7) ^ swz(row));
-      const bool kin = kc < (int)K;
-      const uint32_t oa = kin ? (uint32_t)(row * lda + kc) : kOOB;
-      const uint32_t ob = kin ? (uint32_t)(row * ldb + kc) : kOOB;
-      dma16(lb + (32 * wave + 8 * it) * BK, oa, ra);
-      dma16(lb + A_BYTES + (32 * wave + 8 * it) * BK, ob, rb);
+      for (int it = 0; it < 4; ++it) {
+        const int row = lrow + 8 * it;
+        const int kc = 16 * ((lane & 7) ^ swz(row));
+        dma16s(lb + (32 * wave + 8 * it) * BK, (uint32_t)(row * lda + kc), ra, (uint32_t)k0);
+        dma16s(lb + A_BYTES + (32 * wave + 8 * it) * BK, (uint32_t)(row * ldb + kc), rb, (uint32_t)k0);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = lrow + 8 * it;
+        const int kc = k0 + 16 * ((lane & 7) ^ swz(row));
+        const bool kin = kc < (int)K;
+        const uint32_t oa = kin ? (uint32_t)(row * lda + kc) : kOOB;
+        const uint32_t ob = kin ? (uint32_t)(row * ldb + kc) : kOOB;
+        dma16(lb + (32 * wave + 8 * it) * BK, oa, ra);
+        dma16(lb + A_BYTES + (32 * wave + 8 * it) * BK, ob, rb);
+      }
     }
     if constexpr (BLOCK && SA_ROWS) {
       if (wave == 0) {   // 256 row scales of this K block
