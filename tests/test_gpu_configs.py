@@ -218,6 +218,60 @@ def test_config2_delayed_16_steps(O, L, c2_data, fused):
                                    label=f"config2 step{t} wgrad")
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_delayed_step_graph_replays_vs_oracle(O, L, c2_data, fused):
+    """The delayed-scaling step captured once into a HIP graph and replayed
+    on four steps of inputs (copied into the captured input buffers between
+    replays, eager work and synchronisation in between): after every replay
+    the histories and scales equal the oracle's recurrence bit for bit, every
+    cast byte equals the oracle's cast at the scale in force, and the three
+    GEMMs pass the gate on sampled rows and columns (steps 1 and 3).
+    Operands are the 1024 x 1024 leading blocks of the 4096^3 workload's
+    tensors (four 256 x 256 tiles per side)."""
+    n = 1024
+    run = DelayedRun(L, T=n, DI=n, DO=n, fused=fused)
+    data = [{k: np.ascontiguousarray(d[k][:n, :n]) for k in ("x", "w", "dy")} for d in c2_data[:4]]
+    xb, wb, dyb = (torch.empty((n, n), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.step(xb, wb, dyb)
+    torch.cuda.synchronize()
+    h = np.zeros((3, 16), np.float32)
+    s = np.ones(3, np.float32)
+    si = np.ones(3, np.float32)
+    fmts = [0, 0, 1]
+    for t, d in enumerate(data):
+        say("graph replay vs oracle", fused, t)
+        s_used, si_used = s.copy(), si.copy()
+        xb.copy_(dev_bf16(d["x"])); wb.copy_(dev_bf16(d["w"])); dyb.copy_(dev_bf16(d["dy"]))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        am = np.array([O.amax(d["x"]), O.amax(d["w"]), O.amax(d["dy"])], np.float32)
+        for i, f in enumerate(fmts):
+            hh, ss, sii = h[i:i + 1].copy(), s[i:i + 1].copy(), si[i:i + 1].copy()
+            O.history_update(hh, am[i:i + 1], f, 0, 0, ss, sii)
+            h[i], s[i], si[i] = hh[0], ss[0], sii[0]
+        gh, gs, gsi = run.state()
+        assert np.array_equal(bits(gh), bits(h)) and np.array_equal(bits(gs), bits(s)), t
+        assert np.array_equal(bits(gsi), bits(si)), t
+        xr, wr, dr = O.cast(d["x"], s_used[0], 0), O.cast(d["w"], s_used[1], 0), O.cast(d["dy"], s_used[2], 1)
+        for got, want in ((run.xq, xr), (run.xtq, xr.T), (run.wq, wr), (run.wtq, wr.T),
+                          (run.dyq, dr), (run.dytq, dr.T)):
+            assert np.array_equal(got.cpu().numpy(), want), t
+        if t in (1, 3):
+            sa = lambda i: np.array([si_used[i]], np.float32)
+            check_gemm_sampled(O, run.y, xr, 0, 0, sa(0), np.ascontiguousarray(wr.T), 0, 0, sa(1),
+                               True, 400 + t, label=f"graph step{t} fwd")
+            check_gemm_sampled(O, run.dx, dr, 1, 0, sa(2), wr, 0, 0, sa(1), True, 500 + t,
+                               label=f"graph step{t} dgrad")
+            check_gemm_sampled(O, run.dw, np.ascontiguousarray(xr.T), 0, 0, sa(0),
+                               np.ascontiguousarray(dr.T), 1, 0, sa(2), False, 600 + t,
+                               label=f"graph step{t} wgrad")
+    del g
+
+
 def test_config2_checkpoint_restore_bitexact(O, L, c2_data):
     """Scale state saved after 8 steps and restored into fresh buffers
     continues bit-exactly (histories, scales and every output byte)."""
