@@ -361,8 +361,9 @@ def bench_c5(args, torch, L, datagen, dev, stream):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    del g
     print(f"# C5 step {ms_step:.3f} ms (graph)", file=sys.stderr, flush=True)
+    clock = sample_clock_under(torch, g)
+    del g
     timed = c5.timed_eager_step(stream)
     summ = c5_summary(timed)
     flops = 2 * c5.flops_per_pass()
@@ -377,7 +378,7 @@ def bench_c5(args, torch, L, datagen, dev, stream):
     del c5
     torch.cuda.empty_cache()
     return {"ms_step": ms_step, "flops": flops, "cast_bytes": cast_bytes, "wall": wall,
-            "summary": summ, "roofline": roofline}
+            "summary": summ, "roofline": roofline, "clock": clock}
 
 
 # ----------------------------------------------------------------------------
@@ -885,6 +886,47 @@ def capture(torch, fn):
     return g
 
 
+def amd_smi_gfx_mhz():
+    """Current gfx clock of GPU 0, MHz, averaged over its XCDs, from the
+    amd-smi tool (a child process); None when it is not available."""
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"],
+                             capture_output=True, text=True, timeout=20).stdout
+        clk = json.loads(out)["gpu_data"][0]["clock"]
+        vals = [v["clk"]["value"] for k, v in clk.items() if k.startswith("gfx_")]
+        vals = [float(v) for v in vals if isinstance(v, (int, float))]
+        return sum(vals) / len(vals) if vals else None
+    except Exception:
+        return None
+
+
+def sample_clock_under(torch, g, max_replays=40):
+    """The gfx clock while the step runs: the captured step is replayed back
+    to back while a thread samples amd-smi twice; replays continue until the
+    samples are in (at most max_replays)."""
+    import threading
+    samples = []
+
+    def sampler():
+        for _ in range(2):
+            time.sleep(0.3)
+            v = amd_smi_gfx_mhz()
+            if v is not None:
+                samples.append(v)
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    n = 0
+    while th.is_alive() and n < max_replays:
+        g.replay()
+        torch.cuda.synchronize()
+        n += 1
+    th.join()
+    return {"gfx_mhz_under_load": round(sum(samples) / len(samples), 1) if samples else None,
+            "samples": len(samples), "source": "amd-smi metric --clock (mean over the 8 XCDs)",
+            "step_replays_during_sampling": n}
+
+
 def cpu_model() -> str:
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
@@ -981,8 +1023,15 @@ def main():
         "wall_s_timed": round(h["wall"], 4),
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "roofline": h["roofline"],
+        "clock": h["clock"],
         "c5": summ,
     }
+    mhz = h["clock"].get("gfx_mhz_under_load")
+    if mhz:   # the peaks assume 2.4 GHz; the same fractions at the clock the step ran at
+        result["clock"]["pct_fp8_peak_at_measured_clock"] = round(
+            100 * value / (FP8_PEAK_TFLOPS * mhz / 2400.0), 2)
+        result["clock"]["roofline_frac_at_measured_clock"] = round(
+            h["roofline"]["frac"] * 2400.0 / mhz, 4)
     if not args.no_extras:
         result.update(bench_extras(args, torch, L, datagen, dev, stream))
     if not args.no_cpu:
