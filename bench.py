@@ -252,6 +252,12 @@ class C5Set:
         stream); returns [(label, kind, work, seconds)]."""
         torch = self.torch
         evs = []
+        # keep the GPU busy while the first launches are enqueued, so the
+        # first event pair times the kernel, not the host's submission
+        try:
+            torch.cuda._sleep(4_000_000)
+        except (AttributeError, RuntimeError):
+            pass
         for mode in ("delayed", "block"):
             for lab, kind, work, fn in self.ops[mode]:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
