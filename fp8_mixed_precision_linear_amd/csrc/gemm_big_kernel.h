@@ -132,6 +132,174 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int row, int g) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+// ---- epilogue pieces shared by the GEMM kernels.  A wavefront's tile is
+// TI x TJ MFMA tiles of 16 x 16 from row r0, column c0 of D; lane (g, l16)
+// holds, for each (i, j), D row r0 + 16 i + l16, columns c0 + 16 j + 4 g ..
+// +3.  deq(i, j, q, a) dequantises accumulator entry (i, j, q).
+
+// Tile wholly inside D with 16-byte-aligned rows, BF16 or FP32 output:
+// staged through the wavefront's REGION bytes of LDS (16-byte chunk c of
+// tile row r at chunk c ^ (r & 7)) and written as whole rows, 16 bytes per
+// lane (passes of as many rows as the region holds); FP32 `accumulate` adds
+// the old row in the same pass.  Returns the running |D| maximum (binary32
+// bit pattern; for BF16 the rounded values').
+template <int TI, int TJ, int REGION, typename Deq>
+__device__ __forceinline__ uint32_t store_staged(const GemmParams& p, const v4f (&acc)[TI][TJ],
+                                                 Deq&& deq, bool may_sub, int64_t r0, int64_t c0,
+                                                 int lane, uint8_t* wl) {
+  constexpr int WTM = 16 * TI, WTN = 16 * TJ;
+  const int g = lane >> 4, l16 = lane & 15;
+  uint32_t amax_bits = 0;
+  auto epi = [&](auto f32tag) {
+    constexpr bool F32 = decltype(f32tag)::value;
+    constexpr int ES = F32 ? 4 : 2;
+    constexpr int ROW_BYTES = WTN * ES;
+    constexpr int ROWS_PASS = REGION / ROW_BYTES < WTM ? REGION / ROW_BYTES : WTM;
+    constexpr int LANES_ROW = ROW_BYTES / 16;
+    constexpr int ROWS_INST = 64 / LANES_ROW;
+    static_assert(WTM % ROWS_PASS == 0 && ROWS_PASS % 16 == 0 && ROW_BYTES >= 128, "staging layout");
+#pragma unroll
+    for (int pass = 0; pass < WTM / ROWS_PASS; ++pass) {
+      // BF16: the hardware pair conversion, one row-tile at a time; a
+      // row-tile in which any lane holds a binary32 subnormal (which that
+      // instruction does not round to nearest) is written again with the
+      // integer rounding.  CHK = false: no output can be subnormal, the
+      // per-value check is left out.
+      auto row_tiles = [&](auto chktag) {
+        constexpr bool CHK = decltype(chktag)::value;
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          if ((16 * i) / ROWS_PASS != pass) continue;
+          const int r = 16 * i + l16 - pass * ROWS_PASS;
+          auto put = [&](auto softtag) -> bool {
+            constexpr bool SOFT = decltype(softtag)::value;
+            bool sub = false;
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+              float v[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = deq(i, j, q, acc[i][j][q]);
+              const int byte = (16 * j + 4 * g) * ES;
+              uint8_t* dst = wl + r * ROW_BYTES + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
+              if constexpr (F32) {
+                *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+              } else if constexpr (SOFT) {
+                *reinterpret_cast<uint2*>(dst) = make_uint2(
+                    (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
+                    (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16));
+              } else {
+                if constexpr (CHK) {
+#pragma unroll
+                  for (int q = 0; q < 4; ++q) sub |= __builtin_isfpclass(v[q], 0x90);
+                }
+                *reinterpret_cast<uint2*>(dst) =
+                    make_uint2(bf16x2_hw(v[0], v[1]), bf16x2_hw(v[2], v[3]));
+              }
+            }
+            return sub;
+          };
+          const bool sub = put(std::false_type{});
+          if constexpr (!F32 && CHK)
+            if (__builtin_expect(__any(sub), 0)) put(std::true_type{});
+        }
+      };
+      if (F32 || !may_sub) row_tiles(std::false_type{});
+      else row_tiles(std::true_type{});
+      // read back whole rows (same wavefront: LDS operations stay in order)
+      const int q = lane % LANES_ROW, rr = lane / LANES_ROW;
+#pragma unroll 4
+      for (int t = 0; t < ROWS_PASS / ROWS_INST; ++t) {
+        const int r = t * ROWS_INST + rr;
+        uint4 w = *reinterpret_cast<const uint4*>(wl + r * ROW_BYTES + ((q ^ (r & 7)) << 4));
+        const int64_t gm = r0 + pass * ROWS_PASS + r;
+        uint8_t* gp = reinterpret_cast<uint8_t*>(p.D) + (gm * p.ldd + c0) * ES + q * 16;
+        if constexpr (F32) {
+          if (p.accumulate) {
+            const float4 o = *reinterpret_cast<const float4*>(gp);
+            w.x = __float_as_uint(o.x + __uint_as_float(w.x));
+            w.y = __float_as_uint(o.y + __uint_as_float(w.y));
+            w.z = __float_as_uint(o.z + __uint_as_float(w.z));
+            w.w = __float_as_uint(o.w + __uint_as_float(w.w));
+          }
+          if (p.d_amax) {
+            const uint32_t m4[4] = {w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu, w.z & 0x7FFFFFFFu,
+                                    w.w & 0x7FFFFFFFu};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) amax_bits = m4[e] > amax_bits ? m4[e] : amax_bits;
+          }
+        } else if (p.d_amax) {
+          const uint32_t m = absmax_fold(absmax_pk(absmax_pk(absmax_pk(absmax_pk(0u, w.x), w.y), w.z), w.w));
+          amax_bits = m > amax_bits ? m : amax_bits;
+        }
+        *reinterpret_cast<uint4*>(gp) = w;
+      }
+    }
+  };
+  if (p.d_f32) epi(std::true_type{});
+  else epi(std::false_type{});
+  return amax_bits;
+}
+
+// Any other tile: element by element with bounds checks (BF16, FP32 or,
+// with OUT8, FP8 codes of fl32(v * so) and their transposed copy).
+template <int TI, int TJ, bool OUT8, typename Deq>
+__device__ __forceinline__ uint32_t store_edge(const GemmParams& p, const v4f (&acc)[TI][TJ],
+                                               Deq&& deq, float so, int64_t r0, int64_t c0,
+                                               int lane) {
+  const int g = lane >> 4, l16 = lane & 15;
+  const int64_t M = p.M, N = p.N;
+  const int64_t mr0 = r0 + l16, nc0 = c0 + 4 * g;
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int64_t m = mr0 + 16 * i, n = nc0 + 16 * j;
+      if (m >= M) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (n + r >= N) continue;
+        float x = deq(i, j, r, acc[i][j][r]);
+        if (OUT8) {
+          const float xs = x * so;
+          const uint8_t c = (uint8_t)((p.d_fp8 == 1 ? cvt4<0, true>(xs, 0.f, 0.f, 0.f)
+                                                    : cvt4<1, true>(xs, 0.f, 0.f, 0.f)) & 0xFFu);
+          reinterpret_cast<uint8_t*>(p.D)[m * p.ldd + n + r] = c;
+          if (p.D_t) p.D_t[(n + r) * p.ldt + m] = c;
+          const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;
+          amax_bits = b > amax_bits ? b : amax_bits;
+        } else if (p.d_f32) {
+          float* d = reinterpret_cast<float*>(p.D) + m * p.ldd + n + r;
+          if (p.accumulate) x = *d + x;
+          *d = x;
+          const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;
+          amax_bits = b > amax_bits ? b : amax_bits;
+        } else {
+          const uint16_t h = f32_to_bf16_rne(x);
+          reinterpret_cast<uint16_t*>(p.D)[m * p.ldd + n + r] = h;
+          const uint32_t b = (uint32_t)(h & 0x7FFFu) << 16;
+          amax_bits = b > amax_bits ? b : amax_bits;
+        }
+      }
+    }
+  return amax_bits;
+}
+
+// The workgroup's |D| maximum into *d_amax: one device atomic per workgroup.
+template <int NW>
+__device__ __forceinline__ void workgroup_amax(float* d_amax, uint32_t amax_bits, int lane, int wave) {
+  __shared__ uint32_t wmax[NW];
+  amax_bits = wave_max_u32(amax_bits);
+  if (lane == 0) wmax[wave] = amax_bits;
+  __syncthreads();
+  if (wave == 0 && lane == 0) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = wmax[w] > m ? wmax[w] : m;
+    if (m != 0u) atomic_max_bits(d_amax, m);
+  }
+}
+
 // BLOCK : block-mode promotion per 128-wide K block;
 // SA_ROWS: A has 1x128 scales (one per row and K block), else one per wave;
 // SB_COL : B has 1x128 scales (one per column and K block), else one per wave.
@@ -525,141 +693,12 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     else epi8(std::integral_constant<int, 1>{});
   } else if (staged) {
     __syncthreads();   // every wavefront is done reading both stages
-    uint8_t* wl = &lds[0][0] + wave * 16384;
-    auto epi = [&](auto f32tag) {
-      constexpr bool F32 = decltype(f32tag)::value;
-      constexpr int ES = F32 ? 4 : 2;
-      constexpr int ROWS_PASS = F32 ? 64 : 128;
-      constexpr int ROW_BYTES = WTN * ES;
-      constexpr int LANES_ROW = ROW_BYTES / 16;
-      constexpr int ROWS_INST = 64 / LANES_ROW;
-#pragma unroll
-      for (int pass = 0; pass < WTM / ROWS_PASS; ++pass) {
-        // BF16: the hardware pair conversion, one row-tile at a time; a
-        // row-tile in which any lane holds a binary32 subnormal (which that
-        // instruction does not round to nearest) is written again with the
-        // integer rounding.  CHK = false: no output can be subnormal, the
-        // per-value check is left out.
-        auto row_tiles = [&](auto chktag) {
-          constexpr bool CHK = decltype(chktag)::value;
-#pragma unroll
-          for (int i = 0; i < TI; ++i) {
-            if ((16 * i) / ROWS_PASS != pass) continue;
-            const int r = 16 * i + l16 - pass * ROWS_PASS;
-            auto put = [&](auto softtag) -> bool {
-              constexpr bool SOFT = decltype(softtag)::value;
-              bool sub = false;
-#pragma unroll
-              for (int j = 0; j < TJ; ++j) {
-                float v[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v[q] = deq(i, j, q, acc[i][j][q]);
-                const int byte = (16 * j + 4 * g) * ES;
-                uint8_t* dst = wl + r * ROW_BYTES + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15);
-                if constexpr (F32) {
-                  *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-                } else if constexpr (SOFT) {
-                  *reinterpret_cast<uint2*>(dst) = make_uint2(
-                      (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16),
-                      (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16));
-                } else {
-                  if constexpr (CHK) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) sub |= __builtin_isfpclass(v[q], 0x90);
-                  }
-                  *reinterpret_cast<uint2*>(dst) =
-                      make_uint2(bf16x2_hw(v[0], v[1]), bf16x2_hw(v[2], v[3]));
-                }
-              }
-              return sub;
-            };
-            const bool sub = put(std::false_type{});
-            if constexpr (!F32 && CHK)
-              if (__builtin_expect(__any(sub), 0)) put(std::true_type{});
-          }
-        };
-        if (F32 || !may_sub) row_tiles(std::false_type{});
-        else row_tiles(std::true_type{});
-        // read back whole rows (same wavefront: LDS operations stay in order)
-        const int q = lane % LANES_ROW, rr = lane / LANES_ROW;
-#pragma unroll 4
-        for (int t = 0; t < ROWS_PASS / ROWS_INST; ++t) {
-          const int r = t * ROWS_INST + rr;
-          uint4 w = *reinterpret_cast<const uint4*>(wl + r * ROW_BYTES + ((q ^ (r & 7)) << 4));
-          const int64_t gm = m0 + wm * WTM + pass * ROWS_PASS + r;
-          uint8_t* gp = reinterpret_cast<uint8_t*>(p.D) + (gm * p.ldd + n0 + wn * WTN) * ES + q * 16;
-          if constexpr (F32) {
-            if (p.accumulate) {
-              const float4 o = *reinterpret_cast<const float4*>(gp);
-              w.x = __float_as_uint(o.x + __uint_as_float(w.x));
-              w.y = __float_as_uint(o.y + __uint_as_float(w.y));
-              w.z = __float_as_uint(o.z + __uint_as_float(w.z));
-              w.w = __float_as_uint(o.w + __uint_as_float(w.w));
-            }
-            if (p.d_amax) {
-              const uint32_t m4[4] = {w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu, w.z & 0x7FFFFFFFu,
-                                      w.w & 0x7FFFFFFFu};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) amax_bits = m4[e] > amax_bits ? m4[e] : amax_bits;
-            }
-          } else if (p.d_amax) {
-            const uint32_t m = absmax_fold(absmax_pk(absmax_pk(absmax_pk(absmax_pk(0u, w.x), w.y), w.z), w.w));
-            amax_bits = m > amax_bits ? m : amax_bits;
-          }
-          *reinterpret_cast<uint4*>(gp) = w;
-        }
-      }
-    };
-    if (p.d_f32) epi(std::true_type{});
-    else epi(std::false_type{});
+    amax_bits = store_staged<TI, TJ, 16384>(p, acc, deq, may_sub, m0 + wm * WTM, n0 + wn * WTN, lane,
+                                            &lds[0][0] + wave * 16384);
   } else {
-    const int64_t mr0 = m0 + wm * WTM + l16;
-    const int64_t nc0 = n0 + wn * WTN + 4 * g;
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int64_t m = mr0 + 16 * i, n = nc0 + 16 * j;
-        if (m >= M) continue;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (n + r >= N) continue;
-          float x = deq(i, j, r, acc[i][j][r]);
-          if (OUT8) {
-            const float xs = x * so;
-            const uint8_t c = (uint8_t)((p.d_fp8 == 1 ? cvt4<0, true>(xs, 0.f, 0.f, 0.f)
-                                                      : cvt4<1, true>(xs, 0.f, 0.f, 0.f)) & 0xFFu);
-            reinterpret_cast<uint8_t*>(p.D)[m * p.ldd + n + r] = c;
-            if (p.D_t) p.D_t[(n + r) * p.ldt + m] = c;
-            const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;
-            amax_bits = b > amax_bits ? b : amax_bits;
-          } else if (p.d_f32) {
-            float* d = reinterpret_cast<float*>(p.D) + m * p.ldd + n + r;
-            if (p.accumulate) x = *d + x;
-            *d = x;
-            const uint32_t b = __float_as_uint(x) & 0x7FFFFFFFu;
-            amax_bits = b > amax_bits ? b : amax_bits;
-          } else {
-            const uint16_t h = f32_to_bf16_rne(x);
-            reinterpret_cast<uint16_t*>(p.D)[m * p.ldd + n + r] = h;
-            const uint32_t b = (uint32_t)(h & 0x7FFFu) << 16;
-            amax_bits = b > amax_bits ? b : amax_bits;
-          }
-        }
-      }
+    amax_bits = store_edge<TI, TJ, OUT8>(p, acc, deq, so, m0 + wm * WTM, n0 + wn * WTN, lane);
   }
-  if (p.d_amax) {   // one device atomic per workgroup
-    __shared__ uint32_t wmax[NWAVES];
-    amax_bits = wave_max_u32(amax_bits);
-    if (lane == 0) wmax[wave] = amax_bits;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t m = 0;
-#pragma unroll
-      for (int w = 0; w < NWAVES; ++w) m = wmax[w] > m ? wmax[w] : m;
-      if (m != 0u) atomic_max_bits(p.d_amax, m);
-    }
-  }
+  if (p.d_amax) workgroup_amax<NWAVES>(p.d_amax, amax_bits, lane, wave);
 }
 
 template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL, bool MX, bool OUT8>
