@@ -14,8 +14,9 @@ bool gemm_big_supported(const GemmParams& p) {
 }
 
 hipError_t launch_gemm_big(const GemmParams& p, hipStream_t s) {
+  if (p.a_scaling == 0 && p.b_scaling == 0)
+    return p.d_fp8 ? launch_gemm_w4_fp8out(p, s) : launch_gemm_w4(p, s);
   if (p.d_fp8) return launch_gemm_big_fp8out(p, s);
-  if (gemm_w4_eligible(p)) return launch_gemm_w4(p, s);
   return launch_gemm_big_out<false>(p, s);
 }
 

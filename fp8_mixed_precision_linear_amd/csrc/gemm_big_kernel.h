@@ -240,6 +240,118 @@ __device__ __forceinline__ uint32_t store_staged(const GemmParams& p, const v4f 
   return amax_bits;
 }
 
+// Tile wholly inside D (and D_t) with 16-byte-aligned rows, FP8 output:
+// codes encode(fl32(v * so)) of the dequantised value v, running maximum of
+// |v| (binary32 bit pattern).  The tile goes in PASSES passes of row-tiles;
+// each pass's codes are staged row-major (16 TJ bytes per tile row, 16-byte
+// chunk c at c ^ (r mod chunks per row)) and leave as whole rows, then go
+// into the column-major copy (row stride 144 bytes, 128 rows), which leaves
+// as rows of D_t after the last pass.  One pass reuses one area for both
+// layouts (max(16 TJ * 128, 16 TJ * 144) bytes of region); more passes keep
+// the column-major copy (16 TJ * 144 bytes) beside a row-major area of one
+// pass, fewer codes live at a time.
+template <int TI, int TJ, int PASSES, typename Deq>
+__device__ __forceinline__ uint32_t store_staged8(const GemmParams& p, const v4f (&acc)[TI][TJ],
+                                                  Deq&& deq, float so, int64_t r0, int64_t c0,
+                                                  int lane, uint8_t* wl) {
+  constexpr int WTM = 16 * TI, WTN = 16 * TJ;
+  constexpr int CH = WTN / 16;        // 16-byte chunks per row-major row
+  constexpr int RPI = 64 / CH;        // rows per read-back instruction
+  constexpr int PI = TI / PASSES;     // row-tiles per pass
+  constexpr int RM = PASSES == 1 ? 0 : WTN * 144;   // offset of the row-major area
+  static_assert(WTM == 128 && TI % PASSES == 0 && (16 * PI) % RPI == 0, "staging layout");
+  const int g = lane >> 4, l16 = lane & 15;
+  uint32_t amax_bits = 0;
+  auto epi8 = [&](auto fmttag) {
+    constexpr int F = decltype(fmttag)::value;
+    // quad lane t of the transposed copy and its byte selects
+    const int t = l16 & 3, k4 = l16 >> 2;
+    const uint32_t sel_a = (t & 1) ? (uint32_t)((t + 4) | (t << 8)) : (uint32_t)(t | ((t + 4) << 8));
+    const uint32_t sel_f = t < 2 ? 0x05040100u : 0x01000504u;
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+      uint32_t code[PI][TJ];
+#pragma unroll
+      for (int il = 0; il < PI; ++il)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int i = pass * PI + il;
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = deq(i, j, q, acc[i][j][q]);
+          // The running maximum is taken here, in place: left to itself the
+          // compiler moves it past the NaN-patch branches to the end of the
+          // pass, which keeps all the dequantised values live (and spilled).
+          amax_bits = max3_in_place(max3_in_place(amax_bits, __float_as_uint(v[0]) & 0x7FFFFFFFu,
+                                                  __float_as_uint(v[1]) & 0x7FFFFFFFu),
+                                    __float_as_uint(v[2]) & 0x7FFFFFFFu,
+                                    __float_as_uint(v[3]) & 0x7FFFFFFFu);
+          code[il][j] = cvt4<F, true>(v[0] * so, v[1] * so, v[2] * so, v[3] * so);
+          const int r = 16 * il + l16;
+          *reinterpret_cast<uint32_t*>(wl + RM + r * WTN + ((j ^ (r & (CH - 1))) << 4) + 4 * g) =
+              code[il][j];
+        }
+      {
+        const int q = lane % CH, rr = lane / CH;
+#pragma unroll
+        for (int u = 0; u < 16 * PI / RPI; ++u) {
+          const int r = RPI * u + rr;
+          const uint4 w = *reinterpret_cast<const uint4*>(wl + RM + r * WTN + ((q ^ (r & (CH - 1))) << 4));
+          uint8_t* gp = reinterpret_cast<uint8_t*>(p.D) + (r0 + 16 * PI * pass + r) * p.ldd + c0 + q * 16;
+          *reinterpret_cast<uint4*>(gp) = w;
+        }
+      }
+      if (p.D_t) {
+        // Transposed copy: a 4 x 4 byte transpose across each quad of lanes
+        // (same g, rows 16i + 4k .. +3): quad lane t gathers byte t of the
+        // four lanes' words (DPP quad permutes, then two byte selects), i.e.
+        // column 16j + 4g + t, rows 16i + 4k .. +3, and writes them as one
+        // dword of the column-major tile (row stride 144 bytes: the 64 lanes
+        // hit 64 different banks).  Same wavefront, LDS operations in order:
+        // with one pass the row-major reads above complete before these
+        // writes reuse the area.
+#pragma unroll
+        for (int il = 0; il < PI; ++il)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            const uint32_t a0 = code[il][j];
+            const uint32_t a1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0xB1, 0xF, 0xF, false);
+            const uint32_t a2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0x4E, 0xF, 0xF, false);
+            const uint32_t a3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0x1B, 0xF, 0xF, false);
+            const uint32_t p01 = __builtin_amdgcn_perm(a1, a0, sel_a);
+            const uint32_t p23 = __builtin_amdgcn_perm(a3, a2, sel_a);
+            *reinterpret_cast<uint32_t*>(wl + (16 * j + 4 * g + t) * 144 + 16 * (pass * PI + il) + 4 * k4) =
+                __builtin_amdgcn_perm(p23, p01, sel_f);
+          }
+      }
+    }
+    if (p.D_t) {
+      const int c = lane & 7, rr = lane >> 3;
+#pragma unroll
+      for (int u = 0; u < WTN / 8; ++u) {
+        const int n = 8 * u + rr;
+        const uint4 w = *reinterpret_cast<const uint4*>(wl + n * 144 + 16 * c);
+        uint8_t* gp = p.D_t + (c0 + n) * p.ldt + r0 + 16 * c;
+        *reinterpret_cast<uint4*>(gp) = w;
+      }
+    }
+  };
+  if (p.d_fp8 == 1) epi8(std::integral_constant<int, 0>{});
+  else epi8(std::integral_constant<int, 1>{});
+  return amax_bits;
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1: the index is a constant
+// expression whatever the unroller decides, so an array indexed by it stays
+// in registers.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Any other tile: element by element with bounds checks (BF16, FP32 or,
 // with OUT8, FP8 codes of fl32(v * so) and their transposed copy).
 template <int TI, int TJ, bool OUT8, typename Deq>
@@ -250,12 +362,12 @@ __device__ __forceinline__ uint32_t store_edge(const GemmParams& p, const v4f (&
   const int64_t M = p.M, N = p.N;
   const int64_t mr0 = r0 + l16, nc0 = c0 + 4 * g;
   uint32_t amax_bits = 0;
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
+  static_for<0, TI>([&](auto itag) {
+    constexpr int i = decltype(itag)::value;
+    static_for<0, TJ>([&](auto jtag) {
+      constexpr int j = decltype(jtag)::value;
       const int64_t m = mr0 + 16 * i, n = nc0 + 16 * j;
-      if (m >= M) continue;
+      if (m >= M) return;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (n + r >= N) continue;
@@ -281,7 +393,8 @@ __device__ __forceinline__ uint32_t store_edge(const GemmParams& p, const v4f (&
           amax_bits = b > amax_bits ? b : amax_bits;
         }
       }
-    }
+    });
+  });
   return amax_bits;
 }
 
@@ -616,81 +729,9 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
                                             ((reinterpret_cast<uintptr_t>(p.D_t) & 15u) == 0)));
   uint32_t amax_bits = 0;
   if (OUT8 && staged) {
-    // FP8 output: codes encode(fl32(v * d_scale)) of the dequantised value
-    // v, amax of |v|.  Codes go through the wavefront's LDS region twice:
-    // row-major (64 bytes per tile row, 16-byte chunk c at c ^ (r & 3)),
-    // then, for the transposed copy, column-major (row stride 144 bytes).
-    __syncthreads();
-    uint8_t* wl = &lds[0][0] + wave * 16384;
-    auto epi8 = [&](auto fmttag) {
-      constexpr int F = decltype(fmttag)::value;
-      uint32_t code[TI][TJ];
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          float v[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = deq(i, j, q, acc[i][j][q]);
-          // The running maximum is taken here, in place: left to itself the
-          // compiler moves it past the NaN-patch branches to the end of the
-          // pass, which keeps all 128 dequantised values live (and spilled).
-          amax_bits = max3_in_place(max3_in_place(amax_bits, __float_as_uint(v[0]) & 0x7FFFFFFFu,
-                                                  __float_as_uint(v[1]) & 0x7FFFFFFFu),
-                                    __float_as_uint(v[2]) & 0x7FFFFFFFu,
-                                    __float_as_uint(v[3]) & 0x7FFFFFFFu);
-          code[i][j] = cvt4<F, true>(v[0] * so, v[1] * so, v[2] * so, v[3] * so);
-          const int r = 16 * i + l16;
-          *reinterpret_cast<uint32_t*>(wl + r * 64 + ((j ^ (r & 3)) << 4) + 4 * g) = code[i][j];
-        }
-      {
-        const int q = lane & 3, rr = lane >> 2;
-#pragma unroll
-        for (int t = 0; t < WTM / 16; ++t) {
-          const int r = 16 * t + rr;
-          const uint4 w = *reinterpret_cast<const uint4*>(wl + r * 64 + ((q ^ (r & 3)) << 4));
-          uint8_t* gp = reinterpret_cast<uint8_t*>(p.D) + (m0 + wm * WTM + r) * p.ldd + n0 +
-                        wn * WTN + q * 16;
-          *reinterpret_cast<uint4*>(gp) = w;
-        }
-      }
-      if (p.D_t) {
-        // Transposed copy: a 4 x 4 byte transpose across each quad of lanes
-        // (same g, rows 16i + 4k .. +3): quad lane t gathers byte t of the
-        // four lanes' words (DPP quad permutes, then two byte selects), i.e.
-        // column 16j + 4g + t, rows 16i + 4k .. +3, and writes them as one
-        // dword of the column-major tile (row stride 144 bytes: the 64 lanes
-        // hit 64 different banks).  Same wavefront, LDS operations in order:
-        // the row-major reads above complete before these writes reuse the
-        // region.
-        const int t = l16 & 3, k4 = l16 >> 2;
-        const uint32_t sel_a = (t & 1) ? (uint32_t)((t + 4) | (t << 8)) : (uint32_t)(t | ((t + 4) << 8));
-        const uint32_t sel_f = t < 2 ? 0x05040100u : 0x01000504u;
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) {
-            const uint32_t a0 = code[i][j];
-            const uint32_t a1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0xB1, 0xF, 0xF, false);
-            const uint32_t a2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0x4E, 0xF, 0xF, false);
-            const uint32_t a3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0x1B, 0xF, 0xF, false);
-            const uint32_t p01 = __builtin_amdgcn_perm(a1, a0, sel_a);
-            const uint32_t p23 = __builtin_amdgcn_perm(a3, a2, sel_a);
-            *reinterpret_cast<uint32_t*>(wl + (16 * j + 4 * g + t) * 144 + 16 * i + 4 * k4) =
-                __builtin_amdgcn_perm(p23, p01, sel_f);
-          }
-        const int c = lane & 7, rr = lane >> 3;
-#pragma unroll
-        for (int t = 0; t < WTN / 8; ++t) {
-          const int n = 8 * t + rr;
-          const uint4 w = *reinterpret_cast<const uint4*>(wl + n * 144 + 16 * c);
-          uint8_t* gp = p.D_t + (n0 + wn * WTN + n) * p.ldt + m0 + wm * WTM + 16 * c;
-          *reinterpret_cast<uint4*>(gp) = w;
-        }
-      }
-    };
-    if (p.d_fp8 == 1) epi8(std::integral_constant<int, 0>{});
-    else epi8(std::integral_constant<int, 1>{});
+    __syncthreads();   // every wavefront is done reading both stages
+    amax_bits = store_staged8<TI, TJ, 1>(p, acc, deq, so, m0 + wm * WTM, n0 + wn * WTN, lane,
+                                      &lds[0][0] + wave * 16384);
   } else if (staged) {
     __syncthreads();   // every wavefront is done reading both stages
     amax_bits = store_staged<TI, TJ, 16384>(p, acc, deq, may_sub, m0 + wm * WTM, n0 + wn * WTN, lane,
@@ -729,9 +770,9 @@ template <int AF, int BF, bool OUT8>
 hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
   const bool row_a = p.a_scaling == 5, row_b = p.b_scaling == 5;
   const bool block = !((p.a_scaling == 0 || row_a) && (p.b_scaling == 0 || row_b));
-  if (!block)
-    return row_a || row_b ? launch_one<AF, BF, false, true, true, false, OUT8>(p, s)
-                          : launch_one<AF, BF, false, false, false, false, OUT8>(p, s);
+  // per-tensor scales on both operands go to the four-wavefront kernel
+  // before this point; here at least one operand is per row or blocked
+  if (!block) return launch_one<AF, BF, false, true, true, false, OUT8>(p, s);
   const bool mx = (p.a_scaling == 0 || p.a_scaling >= 3) && (p.b_scaling == 0 || p.b_scaling >= 3);
   return mx ? launch_block<AF, BF, true, OUT8>(p, s) : launch_block<AF, BF, false, OUT8>(p, s);
 }

@@ -84,9 +84,9 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 bool gemm_big_supported(const GemmParams& p);
 hipError_t launch_gemm_big(const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_big_fp8out(const GemmParams& p, hipStream_t s);   // p.d_fp8 != 0
-// Per-tensor scales on both operands and BF16 / FP32 output (gemm_w4.hip):
-// the four-wavefront kernel, under the same size limits as the large-tile one.
-bool gemm_w4_eligible(const GemmParams& p);
+// Per-tensor scales on both operands: the four-wavefront kernel
+// (gemm_w4.hip, gemm_w4_fp8out.hip), under the same size limits.
 hipError_t launch_gemm_w4(const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm_w4_fp8out(const GemmParams& p, hipStream_t s);   // p.d_fp8 != 0
 
 }  // namespace fp8lin
