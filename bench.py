@@ -307,9 +307,9 @@ def c5_plan(T=8192):
 # GEMM kernel (instantiation) of each pass: the dominant-kernel roofline is
 # taken over the launches of one kernel
 C5_KERNEL = {
-    "delayed fwd": "k_gemm_w4<0, 0, false>",
-    "delayed dgrad": "k_gemm_w4<1, 0, false>",
-    "delayed wgrad": "k_gemm_w4<0, 1, false>",
+    "delayed fwd": "k_gemm_w4<0, 0, false, false>",
+    "delayed dgrad": "k_gemm_w4<1, 0, false, false>",
+    "delayed wgrad": "k_gemm_w4<0, 1, false, false>",
     "block fwd": "k_gemm_big<0, 0, true, true, false, false, false>",
     "block dgrad": "k_gemm_big<1, 0, true, true, false, false, false>",
     "block wgrad": "k_gemm_big<0, 1, true, true, true, false, false>",
