@@ -1,11 +1,14 @@
-// gemm_big_kernel.h -- the large-tile FP8 scaled GEMM for gfx950 (the main
-// path): kernel and launch templates, instantiated by gemm_big.hip (BF16 /
-// FP32 output) and gemm_big_fp8out.hip (FP8 output), two translation units
+// gemm_big_kernel.h -- the large-tile FP8 GEMM for gfx950 with block scales
+// (k_gemm_big, eight wavefronts), and the tile helpers and epilogue it shares
+// with the four-wavefront per-tensor / per-row kernel (gemm_w4_kernel.h):
+// kernel and launch templates, instantiated by gemm_big.hip (BF16 / FP32
+// output) and gemm_big_fp8out.hip (FP8 output), two translation units
 // compiled in parallel.
 //
 // Same contract as k_gemm in gemm_kernels.hip (see there and the C ABI):
-// D = A . B^T, K-contiguous FP8 operands, FP32 accumulation; tensor scales
-// in the epilogue, block scales promoted per 128-wide K block.
+// D = A . B^T, K-contiguous FP8 operands, FP32 accumulation; block scales
+// promoted per 128-wide K block (or, power-of-two, applied inside the
+// matrix instruction), a per-tensor operand's scale folded in.
 // [MPG] = "Mixed Precision LLM Training: The Complete Guide",
 //   "Skipping the BAcc accumulator promotion", "DeepSeek FP8 training recipe
 //   in detail > Block-wise scaling at 128 granularity" and "> Mixed-precision
@@ -413,26 +416,17 @@ __device__ __forceinline__ void workgroup_amax(float* d_amax, uint32_t amax_bits
   }
 }
 
-// BLOCK : block-mode promotion per 128-wide K block;
+// The block-scaled GEMM (per-tensor and per-row scales go to k_gemm_w4):
+// BLOCK  : always true here (block scales on at least one operand);
 // SA_ROWS: A has 1x128 scales (one per row and K block), else one per wave;
-// SB_COL : B has 1x128 scales (one per column and K block), else one per wave.
-// Without BLOCK, SA_ROWS && SB_COL selects per-row scales applied in the
-// epilogue: A's inverse scale per row m (a_scaling 5) and B's per row n
-// (b_scaling 5), either of them possibly per tensor.
+// SB_COL : B has 1x128 scales (one per column and K block), else one per wave;
+// MX     : power-of-two scales applied inside the matrix instruction, else
+//          promoted in FP32 per 128-wide K block.
 template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL, bool MX, bool OUT8>
 __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m, int tiles_n) {
+  static_assert(BLOCK, "per-tensor and per-row scales run on k_gemm_w4");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
   __shared__ float su_tab[NWAVES][MAX_KB];
-  constexpr bool ROWS = !BLOCK && SA_ROWS && SB_COL;
-  // The next stage's DMA goes out right after the end-of-step barrier
-  // (a full step of latency before its wait) in the kernels without block
-  // promotion; with promotion the longer-lived DMA addresses push the
-  // kernel past 256 registers (measured: spills), so there it goes out
-  // after the step's first fragment reads.
-  constexpr bool EARLY_DMA = !BLOCK && !OUT8;
-  // per-row scales of the tile's 256 D rows and 256 D columns, staged once
-  // (rows clamped into D for edge tiles); read in the epilogue
-  __shared__ float rs_tab[ROWS ? BM + BN : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -465,36 +459,23 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     // Block scales make K a multiple of the step: every chunk of a step is
     // inside K, and the step's K offset goes in the scalar offset (no
     // per-step VALU work beside the promotion; measured 1-2% on the
-    // transformer-block shapes, while the per-tensor kernels, which also
-    // take a K tail, gained nothing)
-    if constexpr (BLOCK) {
+    // transformer-block shapes).  Rows past the operand's end fail the
+    // buffer range check on the lane offset and read zeros.
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int row = lrow + 8 * it;
-        const int kc = 16 * ((lane & 7) ^ swz(row));
-        dma16s(lb + (32 * wave + 8 * it) * BK, (uint32_t)(row * lda + kc), ra, (uint32_t)k0);
-        dma16s(lb + A_BYTES + (32 * wave + 8 * it) * BK, (uint32_t)(row * ldb + kc), rb, (uint32_t)k0);
-      }
-    } else {
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int row = lrow + 8 * it;
-        const int kc = k0 + 16 * ((lane & 7) ^ swz(row));
-        const bool kin = kc < (int)K;
-        const uint32_t oa = kin ? (uint32_t)(row * lda + kc) : kOOB;
-        const uint32_t ob = kin ? (uint32_t)(row * ldb + kc) : kOOB;
-        dma16(lb + (32 * wave + 8 * it) * BK, oa, ra);
-        dma16(lb + A_BYTES + (32 * wave + 8 * it) * BK, ob, rb);
-      }
+    for (int it = 0; it < 4; ++it) {
+      const int row = lrow + 8 * it;
+      const int kc = 16 * ((lane & 7) ^ swz(row));
+      dma16s(lb + (32 * wave + 8 * it) * BK, (uint32_t)(row * lda + kc), ra, (uint32_t)k0);
+      dma16s(lb + A_BYTES + (32 * wave + 8 * it) * BK, (uint32_t)(row * ldb + kc), rb, (uint32_t)k0);
     }
-    if constexpr (BLOCK && SA_ROWS) {
+    if constexpr (SA_ROWS) {
       if (wave == 0) {   // 256 row scales of this K block
         const i32x4 rs = make_rsrc(p.a_sinv + (int64_t)kb * M + m0, (uint32_t)(rows_a * 4));
 #pragma unroll
         for (int q = 0; q < 4; ++q) dma4(lb + SA_OFF + q * 256, (uint32_t)(q * 256 + lane * 4), rs);
       }
     }
-    if constexpr (BLOCK && SB_COL) {
+    if constexpr (SB_COL) {
       if (wave == 1) {   // 256 column scales of this K block
         const i32x4 rs = make_rsrc(p.b_sinv + (int64_t)kb * N + n0, (uint32_t)(rows_b * 4));
 #pragma unroll
@@ -513,10 +494,6 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   // the wait for stage 0 covers them, and the epilogue does not start with
   // a round trip to memory.
   float sa = 1.0f, sb = 1.0f, so = 1.0f;
-  if constexpr (!BLOCK) {
-    sa = p.a_sinv[0];
-    sb = p.b_sinv[0];
-  }
   if constexpr (MX) {   // a per-tensor operand's scale is applied there
     if (p.a_scaling == 0) sa = p.a_sinv[0];
     if (p.b_scaling == 0) sb = p.b_sinv[0];
@@ -528,17 +505,8 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   load_stage(0, lds[0]);
   if (nk > 1) load_stage(1, lds[1]);
 
-  if constexpr (ROWS) {   // thread t < BM: A's scale of D row m0 + t; else B's of column n0 + t - BM
-    static_assert(THREADS == BM + BN, "one row scale per thread");
-    const bool is_a = tid < BM;
-    const int64_t r = is_a ? m0 + tid : n0 + (tid - BM);
-    const int64_t lim = is_a ? M : N;
-    const int row_mode = is_a ? p.a_scaling == 5 : p.b_scaling == 5;
-    rs_tab[tid] = (is_a ? p.a_sinv : p.b_sinv)[row_mode ? (r < lim ? r : lim - 1) : 0];
-  }
-
   // ---- per-wavefront table of the uniform part of each K block's scale
-  if constexpr (BLOCK && !(SA_ROWS && SB_COL)) {
+  if constexpr (!(SA_ROWS && SB_COL)) {
     const int64_t mb = min((m0 + wm * WTM) / 128, (M + 127) / 128 - 1);
     const int64_t nb = min((n0 + wn * WTN) / 128, (N + 127) / 128 - 1);
     for (int kb = lane; kb < nk; kb += 64) {
@@ -584,8 +552,11 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     v8i bfr[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) bfr[j] = frag(Bs, wn * WTN + 16 * j + l16, g);
-    if constexpr (!EARLY_DMA)
-      if (kb > 0 && kb + 1 < nk) load_stage(kb + 1, lds[stage ^ 1]);
+    // the next stage's DMA: into the stage the previous step read (the
+    // end-of-step barrier freed it); issued earlier, right after that
+    // barrier, its longer-lived addresses push the promotion kernels past
+    // 256 registers (measured: spills)
+    if (kb > 0 && kb + 1 < nk) load_stage(kb + 1, lds[stage ^ 1]);
 
     // The MFMA takes B as its first operand, so each 16x16 result tile is
     // the transpose of the D tile: lane (g, l16) holds D row 16*i + l16,
@@ -617,7 +588,7 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
         for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_mx<BF, AF>(bfr[j], a_cur, acc[i][j], eb[j], ea);
         a_cur = a_nxt;
       }
-    } else if constexpr (BLOCK) {
+    } else {
       float scol[TJ][4];
       if constexpr (SB_COL) {
 #pragma unroll
@@ -674,23 +645,9 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
         __builtin_amdgcn_sched_barrier(0);
       }
       promote(TI - 1, pprev, sprev);
-    } else {
-      v8i a_cur = a_first;
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        v8i a_nxt = a_cur;
-        if (i + 1 < TI) a_nxt = frag(As, wm * WTM + 16 * (i + 1) + l16, g);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma<BF, AF>(bfr[j], a_cur, acc[i][j]);
-        a_cur = a_nxt;
-      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // every wavefront is past its reads of this stage: the step after next
-    // loads into it now, a whole step before it is needed
-    if constexpr (EARLY_DMA)
-      if (kb + 2 < nk) load_stage(kb + 2, lds[stage]);
   }
 
   // ---- epilogue.  Lane (g, l16) holds, for each (i, j), D row 16*i + l16,
@@ -700,26 +657,14 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   // tile row r sits at chunk c ^ (r & 7)) and leave as whole rows, 16 bytes
   // per lane: one 128-byte line per tile row for BF16, two for FP32 (FP32
   // goes in two passes of 64 rows).  Other tiles store element by element
-  // with bounds checks.
-  constexpr bool EPI_SCALE = !BLOCK || MX;
-  // Can a dequantised output be a binary32 subnormal?  With per-tensor
-  // scales every nonzero accumulator is a multiple of 2^-(qa+qb), the
-  // product of the two formats' smallest subnormal steps (2^-9 for E4M3,
-  // 2^-16 for E5M2), so at least that in magnitude; rounding is monotone,
-  // so if that minimum, dequantised by the same two products, is a normal
-  // binary32, every nonzero output is.  Other modes always check.
-  bool may_sub = true;
-  if constexpr (!BLOCK && !ROWS) {
-    constexpr int QAB = (AF == 0 ? 9 : 16) + (BF == 0 ? 9 : 16);
-    const float lo = (__builtin_ldexpf(1.0f, -QAB) * __builtin_fabsf(sa)) * __builtin_fabsf(sb);
-    may_sub = !(lo >= 1.17549435e-38f);   // NaN scales: check
-  }
-  if constexpr (ROWS) __syncthreads();   // the tile's row scales are in rs_tab
-  // dequantised value of accumulator entry (i, j, q)
-  auto deq = [&](int i, int j, int q, float a) -> float {
-    if constexpr (ROWS)
-      return (a * rs_tab[wm * WTM + 16 * i + l16]) * rs_tab[BM + wn * WTN + 16 * j + 4 * g + q];
-    else if constexpr (EPI_SCALE) return (a * sa) * sb;
+  // with bounds checks.  Block scales can make any output a binary32
+  // subnormal, so the BF16 conversion always checks for them.
+  const bool may_sub = true;
+  // dequantised value of accumulator entry (i, j, q): the promoted
+  // accumulators carry their scales; with power-of-two block scales in the
+  // matrix instruction a per-tensor operand's scale is applied here
+  auto deq = [&](int, int, int, float a) -> float {
+    if constexpr (MX) return (a * sa) * sb;
     else return a;
   };
   const int esz = OUT8 ? 1 : (p.d_f32 ? 4 : 2);
@@ -768,11 +713,8 @@ hipError_t launch_block(const GemmParams& p, hipStream_t s) {
 // power of two is a binary32 scale like any other).
 template <int AF, int BF, bool OUT8>
 hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
-  const bool row_a = p.a_scaling == 5, row_b = p.b_scaling == 5;
-  const bool block = !((p.a_scaling == 0 || row_a) && (p.b_scaling == 0 || row_b));
-  // per-tensor scales on both operands go to the four-wavefront kernel
-  // before this point; here at least one operand is per row or blocked
-  if (!block) return launch_one<AF, BF, false, true, true, false, OUT8>(p, s);
+  // per-tensor and per-row scales go to the four-wavefront kernel before
+  // this point: here at least one operand has block scales
   const bool mx = (p.a_scaling == 0 || p.a_scaling >= 3) && (p.b_scaling == 0 || p.b_scaling >= 3);
   return mx ? launch_block<AF, BF, true, OUT8>(p, s) : launch_block<AF, BF, false, OUT8>(p, s);
 }

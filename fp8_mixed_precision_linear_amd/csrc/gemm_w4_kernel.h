@@ -43,11 +43,16 @@ constexpr int W4_OUT8_PASSES = 2;
 // KT: K is not a multiple of the step (chunks past K map to the
 // out-of-range marker, step by step); OUT8: FP8 output quantised in the
 // epilogue (codes, optional transposed copy, amax of the unquantised
-// values), as k_gemm_big's.
-template <int AF, int BF, bool KT, bool OUT8>
+// values); ROWS: one scale per row of A (a_scaling 5) and / or of B
+// (b_scaling 5), the other operand possibly per tensor, applied after the
+// K sum ([MPG] "Per-row vs per-tensor scaling").
+template <int AF, int BF, bool KT, bool OUT8, bool ROWS>
 __global__ void __launch_bounds__(W4_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][W4_STAGE];
+  // per-row scales of the tile's 256 D rows and 256 D columns (rows clamped
+  // into D for edge tiles), read in the epilogue
+  __shared__ float rs_tab[ROWS ? BM + BN : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -72,7 +77,11 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
   const int lda = (int)p.lda, ldb = (int)p.ldb;
 
   // the epilogue's scales, read ahead of the first DMA (its wait covers them)
-  const float sa = p.a_sinv[0], sb = p.b_sinv[0];
+  float sa = 1.0f, sb = 1.0f;
+  if constexpr (!ROWS) {
+    sa = p.a_sinv[0];
+    sb = p.b_sinv[0];
+  }
   float so = 1.0f;
   if constexpr (OUT8) so = p.d_scale[0];
 
@@ -118,10 +127,17 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
   if (nk > 1) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) load(1, lds[1], q);
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
+  if constexpr (ROWS) {   // thread t: A's scale of D row m0 + t, then B's of column n0 + t
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t r = (h == 0 ? m0 : n0) + tid, lim = h == 0 ? M : N;
+      const bool row_mode = (h == 0 ? p.a_scaling : p.b_scaling) == 5;
+      rs_tab[h * BM + tid] = (h == 0 ? p.a_sinv : p.b_sinv)[row_mode ? (r < lim ? r : lim - 1) : 0];
+    }
+  }
+  if (nk > 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   // Lane (g, l16) of the transposed MFMA (B is its first operand) holds D
@@ -184,10 +200,16 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
   // accumulator is a multiple of 2^-(qa + qb) (the two formats' smallest
   // subnormal steps), so if that minimum dequantises to a normal binary32,
   // no output can be subnormal.
+  // With per-row scales every output is checked.
   constexpr int QAB = (AF == 0 ? 9 : 16) + (BF == 0 ? 9 : 16);
   const float lo = (__builtin_ldexpf(1.0f, -QAB) * __builtin_fabsf(sa)) * __builtin_fabsf(sb);
-  const bool may_sub = !(lo >= 1.17549435e-38f);   // NaN scales: check
-  auto deq = [&](int, int, int, float x) -> float { return (x * sa) * sb; };
+  const bool may_sub = ROWS || !(lo >= 1.17549435e-38f);   // NaN scales: check
+  auto deq = [&](int i, int j, int q, float x) -> float {
+    if constexpr (ROWS)
+      return (x * rs_tab[wm * 128 + 16 * i + l16]) * rs_tab[BM + wn * 128 + 16 * j + 4 * g + q];
+    else
+      return (x * sa) * sb;
+  };
   const int esz = OUT8 ? 1 : (p.d_f32 ? 4 : 2);
   const bool staged = (m0 + BM <= M) && (n0 + BN <= N) && ((p.ldd * esz) % 16 == 0) &&
                       ((reinterpret_cast<uintptr_t>(p.D) & 15u) == 0) &&
@@ -208,15 +230,21 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
   if (p.d_amax) workgroup_amax<4>(p.d_amax, amax_bits, lane, wave);
 }
 
-template <int AF, int BF, bool OUT8>
-hipError_t launch_w4(const GemmParams& p, hipStream_t s) {
+template <int AF, int BF, bool OUT8, bool ROWS>
+hipError_t launch_w4_k(const GemmParams& p, hipStream_t s) {
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(W4_THREADS);
   if (p.K % BK == 0)
-    hipLaunchKernelGGL((k_gemm_w4<AF, BF, false, OUT8>), grid, block, 0, s, p, tiles_m, tiles_n);
+    hipLaunchKernelGGL((k_gemm_w4<AF, BF, false, OUT8, ROWS>), grid, block, 0, s, p, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((k_gemm_w4<AF, BF, true, OUT8>), grid, block, 0, s, p, tiles_m, tiles_n);
+    hipLaunchKernelGGL((k_gemm_w4<AF, BF, true, OUT8, ROWS>), grid, block, 0, s, p, tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+template <int AF, int BF, bool OUT8>
+hipError_t launch_w4(const GemmParams& p, hipStream_t s) {
+  return p.a_scaling == 5 || p.b_scaling == 5 ? launch_w4_k<AF, BF, OUT8, true>(p, s)
+                                              : launch_w4_k<AF, BF, OUT8, false>(p, s);
 }
 
 template <bool OUT8>

@@ -84,7 +84,7 @@ hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 bool gemm_big_supported(const GemmParams& p);
 hipError_t launch_gemm_big(const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_big_fp8out(const GemmParams& p, hipStream_t s);   // p.d_fp8 != 0
-// Per-tensor scales on both operands: the four-wavefront kernel
+// Per-tensor or per-row scales on both operands: the four-wavefront kernel
 // (gemm_w4.hip, gemm_w4_fp8out.hip), under the same size limits.
 hipError_t launch_gemm_w4(const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_w4_fp8out(const GemmParams& p, hipStream_t s);   // p.d_fp8 != 0
