@@ -14,10 +14,13 @@ bool gemm_big_supported(const GemmParams& p) {
 }
 
 hipError_t launch_gemm_big(const GemmParams& p, hipStream_t s) {
-  // per-tensor and per-row scales: the four-wavefront kernel; block scales
-  // (promoted or in the matrix instruction): the eight-wavefront one
+  // per-tensor and per-row scales: the four-wavefront kernel
   const bool per_a = p.a_scaling == 0 || p.a_scaling == 5, per_b = p.b_scaling == 0 || p.b_scaling == 5;
   if (per_a && per_b) return p.d_fp8 ? launch_gemm_w4_fp8out(p, s) : launch_gemm_w4(p, s);
+  // power-of-two block scales: the same kernel, scales in the matrix
+  // instruction; other block scales: promoted in FP32 by k_gemm_big
+  const bool mx = (p.a_scaling == 0 || p.a_scaling >= 3) && (p.b_scaling == 0 || p.b_scaling >= 3);
+  if (mx) return p.d_fp8 ? launch_gemm_w4_mx_fp8out(p, s) : launch_gemm_w4_mx(p, s);
   if (p.d_fp8) return launch_gemm_big_fp8out(p, s);
   return launch_gemm_big_out<false>(p, s);
 }

@@ -416,15 +416,16 @@ __device__ __forceinline__ void workgroup_amax(float* d_amax, uint32_t amax_bits
   }
 }
 
-// The block-scaled GEMM (per-tensor and per-row scales go to k_gemm_w4):
+// The block-scaled GEMM with binary32 block scales, promoted in FP32 per
+// 128-wide K block (per-tensor, per-row and power-of-two block scales go to
+// k_gemm_w4):
 // BLOCK  : always true here (block scales on at least one operand);
 // SA_ROWS: A has 1x128 scales (one per row and K block), else one per wave;
 // SB_COL : B has 1x128 scales (one per column and K block), else one per wave;
-// MX     : power-of-two scales applied inside the matrix instruction, else
-//          promoted in FP32 per 128-wide K block.
+// MX     : always false here.
 template <int AF, int BF, bool BLOCK, bool SA_ROWS, bool SB_COL, bool MX, bool OUT8>
 __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m, int tiles_n) {
-  static_assert(BLOCK, "per-tensor and per-row scales run on k_gemm_w4");
+  static_assert(BLOCK && !MX, "per-tensor, per-row and power-of-two scales run on k_gemm_w4");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][STAGE];
   __shared__ float su_tab[NWAVES][MAX_KB];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -490,14 +491,10 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // The epilogue's per-tensor scales are read now, ahead of the first DMA:
-  // the wait for stage 0 covers them, and the epilogue does not start with
-  // a round trip to memory.
-  float sa = 1.0f, sb = 1.0f, so = 1.0f;
-  if constexpr (MX) {   // a per-tensor operand's scale is applied there
-    if (p.a_scaling == 0) sa = p.a_sinv[0];
-    if (p.b_scaling == 0) sb = p.b_sinv[0];
-  }
+  // The FP8 output scale is read now, ahead of the first DMA: the wait for
+  // stage 0 covers it, and the epilogue does not start with a round trip
+  // to memory.
+  float so = 1.0f;
   if constexpr (OUT8) so = p.d_scale[0];
 
   // the first two stages go out together, so the second one's latency
@@ -510,24 +507,12 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     const int64_t mb = min((m0 + wm * WTM) / 128, (M + 127) / 128 - 1);
     const int64_t nb = min((n0 + wn * WTN) / 128, (N + 127) / 128 - 1);
     for (int kb = lane; kb < nk; kb += 64) {
-      if constexpr (MX) {
-        // E8M0 codes of the uniform block scales: A in bits 0-7, B in 8-15
-        // (127 = 1.0 for a per-tensor operand, whose scale goes to the
-        // epilogue)
-        int ea = 127, eb = 127;
-        if constexpr (!SA_ROWS)
-          if (p.a_scaling != 0) ea = e8m0_of(p.a_sinv[kb * ((M + 127) / 128) + mb]);
-        if constexpr (!SB_COL)
-          if (p.b_scaling != 0) eb = e8m0_of(p.b_sinv[kb * ((N + 127) / 128) + nb]);
-        su_tab[wave][kb] = __uint_as_float((uint32_t)ea | ((uint32_t)eb << 8));
-      } else {
-        float s = 1.0f;
-        if constexpr (!SA_ROWS)
-          s = p.a_scaling == 0 ? p.a_sinv[0] : p.a_sinv[kb * ((M + 127) / 128) + mb];
-        if constexpr (!SB_COL)
-          s *= p.b_scaling == 0 ? p.b_sinv[0] : p.b_sinv[kb * ((N + 127) / 128) + nb];
-        su_tab[wave][kb] = s;
-      }
+      float s = 1.0f;
+      if constexpr (!SA_ROWS)
+        s = p.a_scaling == 0 ? p.a_sinv[0] : p.a_sinv[kb * ((M + 127) / 128) + mb];
+      if constexpr (!SB_COL)
+        s *= p.b_scaling == 0 ? p.b_sinv[0] : p.b_sinv[kb * ((N + 127) / 128) + nb];
+      su_tab[wave][kb] = s;
     }
   }
 
@@ -561,34 +546,7 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     // The MFMA takes B as its first operand, so each 16x16 result tile is
     // the transpose of the D tile: lane (g, l16) holds D row 16*i + l16,
     // columns 16*j + 4*g .. +3 -- four consecutive outputs of one row.
-    if constexpr (MX) {
-      // power-of-two block scales applied inside the matrix instruction
-      // (exact): lane l of the B fragment scales its row (a D column), lane
-      // l of the A fragment its row; no FP32 promotion, the accumulator
-      // stays in the instruction's C operand.
-      uint32_t eu = 0;
-      if constexpr (!(SA_ROWS && SB_COL)) eu = __float_as_uint(su_tab[wave][kb]);
-      int eb[TJ];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        if constexpr (SB_COL)
-          eb[j] = e8m0_of(reinterpret_cast<const float*>(As + SB_OFF)[wn * WTN + 16 * j + l16]);
-        else
-          eb[j] = (int)((eu >> 8) & 0xFFu);
-      }
-      v8i a_cur = a_first;
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        v8i a_nxt = a_cur;
-        if (i + 1 < TI) a_nxt = frag(As, wm * WTM + 16 * (i + 1) + l16, g);
-        int ea = (int)(eu & 0xFFu);
-        if constexpr (SA_ROWS)
-          ea = e8m0_of(reinterpret_cast<const float*>(As + SA_OFF)[wm * WTM + 16 * i + l16]);
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_mx<BF, AF>(bfr[j], a_cur, acc[i][j], eb[j], ea);
-        a_cur = a_nxt;
-      }
-    } else {
+    {
       float scol[TJ][4];
       if constexpr (SB_COL) {
 #pragma unroll
@@ -661,12 +619,8 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   // subnormal, so the BF16 conversion always checks for them.
   const bool may_sub = true;
   // dequantised value of accumulator entry (i, j, q): the promoted
-  // accumulators carry their scales; with power-of-two block scales in the
-  // matrix instruction a per-tensor operand's scale is applied here
-  auto deq = [&](int, int, int, float a) -> float {
-    if constexpr (MX) return (a * sa) * sb;
-    else return a;
-  };
+  // accumulators carry their scales
+  auto deq = [&](int, int, int, float a) -> float { return a; };
   const int esz = OUT8 ? 1 : (p.d_f32 ? 4 : 2);
   const bool staged = (m0 + BM <= M) && (n0 + BN <= N) && ((p.ldd * esz) % 16 == 0) &&
                       ((reinterpret_cast<uintptr_t>(p.D) & 15u) == 0) &&
@@ -713,10 +667,10 @@ hipError_t launch_block(const GemmParams& p, hipStream_t s) {
 // power of two is a binary32 scale like any other).
 template <int AF, int BF, bool OUT8>
 hipError_t launch_fmt(const GemmParams& p, hipStream_t s) {
-  // per-tensor and per-row scales go to the four-wavefront kernel before
-  // this point: here at least one operand has block scales
-  const bool mx = (p.a_scaling == 0 || p.a_scaling >= 3) && (p.b_scaling == 0 || p.b_scaling >= 3);
-  return mx ? launch_block<AF, BF, true, OUT8>(p, s) : launch_block<AF, BF, false, OUT8>(p, s);
+  // per-tensor, per-row and power-of-two block scales go to the
+  // four-wavefront kernel before this point: here at least one operand has
+  // block scales with binary32 values, promoted in FP32
+  return launch_block<AF, BF, false, OUT8>(p, s);
 }
 
 // OUT8: FP8 output (its own instantiations, so that the BF16 / FP32 kernels

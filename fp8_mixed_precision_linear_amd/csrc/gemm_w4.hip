@@ -4,6 +4,6 @@
 
 namespace fp8lin {
 
-hipError_t launch_gemm_w4(const GemmParams& p, hipStream_t s) { return launch_w4_out<false>(p, s); }
+hipError_t launch_gemm_w4(const GemmParams& p, hipStream_t s) { return launch_w4_out<false, false>(p, s); }
 
 }  // namespace fp8lin

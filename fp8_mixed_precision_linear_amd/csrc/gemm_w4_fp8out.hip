@@ -5,7 +5,7 @@
 namespace fp8lin {
 
 hipError_t launch_gemm_w4_fp8out(const GemmParams& p, hipStream_t s) {
-  return launch_w4_out<true>(p, s);
+  return launch_w4_out<true, false>(p, s);
 }
 
 }  // namespace fp8lin

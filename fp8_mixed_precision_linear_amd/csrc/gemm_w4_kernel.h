@@ -34,7 +34,8 @@ namespace fp8lin {
 namespace {
 
 constexpr int W4_THREADS = 256;
-constexpr int W4_STAGE = A_BYTES + B_BYTES;   // 64 KB: A then B, no scale rows
+constexpr int W4_STAGE = A_BYTES + B_BYTES;   // 64 KB: A then B (block modes: + scale rows)
+enum : int { W4_TENSOR = 0, W4_ROWS = 1, W4_MX = 2 };
 // FP8 output: the epilogue in two passes of 64 rows (fewer codes live at a
 // time; the column-major copy, 18 KB, and a 64-row row-major area, 8 KB,
 // fit in the wavefront's 32 KB)
@@ -43,16 +44,28 @@ constexpr int W4_OUT8_PASSES = 2;
 // KT: K is not a multiple of the step (chunks past K map to the
 // out-of-range marker, step by step); OUT8: FP8 output quantised in the
 // epilogue (codes, optional transposed copy, amax of the unquantised
-// values); ROWS: one scale per row of A (a_scaling 5) and / or of B
-// (b_scaling 5), the other operand possibly per tensor, applied after the
-// K sum ([MPG] "Per-row vs per-tensor scaling").
-template <int AF, int BF, bool KT, bool OUT8, bool ROWS>
+// values).  MODE: W4_TENSOR, per-tensor scales; W4_ROWS, one scale per row
+// of A (a_scaling 5) and / or of B (b_scaling 5), the other operand
+// possibly per tensor, applied after the K sum ([MPG] "Per-row vs
+// per-tensor scaling"); W4_MX + (A 1x128 ? 1 : 0) + (B 1x128 ? 2 : 0),
+// power-of-two block scales (E8M0 codes) applied inside the matrix
+// instruction, the accumulator staying in its C operand ([MPG] "DeepSeek
+// FP8 training recipe in detail > Block-wise scaling at 128 granularity";
+// a per-tensor operand's scale goes to the epilogue).
+template <int AF, int BF, bool KT, bool OUT8, int MODE>
 __global__ void __launch_bounds__(W4_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][W4_STAGE];
+  constexpr bool ROWS = MODE == W4_ROWS, MX = MODE >= W4_MX;
+  constexpr bool SA_ROWS = MX && ((MODE - W4_MX) & 1), SB_COL = MX && ((MODE - W4_MX) & 2);
+  static_assert(!(MX && KT), "block scales make K a multiple of the step");
+  // a stage: A, B, then (block modes) 256 row scales of A and of B
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][MX ? STAGE : W4_STAGE];
   // per-row scales of the tile's 256 D rows and 256 D columns (rows clamped
   // into D for edge tiles), read in the epilogue
   __shared__ float rs_tab[ROWS ? BM + BN : 1];
+  // block modes: per wavefront and K block, the E8M0 codes of the uniform
+  // (128 x 128 or per-tensor) scales, A in bits 0-7, B in bits 8-15
+  __shared__ float su_tab[MX ? 4 : 1][MX ? MAX_KB : 1];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -78,9 +91,13 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
 
   // the epilogue's scales, read ahead of the first DMA (its wait covers them)
   float sa = 1.0f, sb = 1.0f;
-  if constexpr (!ROWS) {
+  if constexpr (MODE == W4_TENSOR) {
     sa = p.a_sinv[0];
     sb = p.b_sinv[0];
+  }
+  if constexpr (MX) {   // a per-tensor operand's scale
+    if (p.a_scaling == 0) sa = p.a_sinv[0];
+    if (p.b_scaling == 0) sb = p.b_sinv[0];
   }
   float so = 1.0f;
   if constexpr (OUT8) so = p.d_scale[0];
@@ -113,6 +130,20 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
       dma16(dst, kc < (int)K ? ro[o][it] + (uint32_t)kc : kOOB, o ? rb : ra);
     }
   };
+  // block modes: the K block's 256 A row scales and 256 B column scales,
+  // wavefront w fetching rows (columns) 64w .. 64w + 63 of each (rows past
+  // the end read zeros); two instructions per wavefront and stage
+  auto load_scales = [&](int kb, const uint8_t* base) {
+    const uint32_t lb = lds_addr(base);
+    if constexpr (SA_ROWS) {
+      const i32x4 rs = make_rsrc(p.a_sinv + (int64_t)kb * M + m0, (uint32_t)(rows_a * 4));
+      dma4(lb + SA_OFF + wave * 256, (uint32_t)(wave * 256 + lane * 4), rs);
+    }
+    if constexpr (SB_COL) {
+      const i32x4 rs = make_rsrc(p.b_sinv + (int64_t)kb * N + n0, (uint32_t)(rows_b * 4));
+      dma4(lb + SB_OFF + wave * 256, (uint32_t)(wave * 256 + lane * 4), rs);
+    }
+  };
 
   v4f acc[8][8];
 #pragma unroll
@@ -124,9 +155,11 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
   // instructions per stage and wavefront, counted down in issue order)
 #pragma unroll
   for (int q = 0; q < 16; ++q) load(0, lds[0], q);
+  load_scales(0, lds[0]);
   if (nk > 1) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) load(1, lds[1], q);
+    load_scales(1, lds[1]);
   }
   if constexpr (ROWS) {   // thread t: A's scale of D row m0 + t, then B's of column n0 + t
 #pragma unroll
@@ -136,6 +169,22 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
       rs_tab[h * BM + tid] = (h == 0 ? p.a_sinv : p.b_sinv)[row_mode ? (r < lim ? r : lim - 1) : 0];
     }
   }
+  if constexpr (MX && !(SA_ROWS && SB_COL)) {
+    // the uniform parts: the wavefront's 128 rows and 128 columns each sit
+    // in one 128 x 128 block (1.0, code 127, for a per-tensor operand)
+    const int64_t mb = min((m0 + wm * 128) / 128, (M + 127) / 128 - 1);
+    const int64_t nb = min((n0 + wn * 128) / 128, (N + 127) / 128 - 1);
+    for (int k = lane; k < nk; k += 64) {
+      int ea = 127, eb = 127;
+      if constexpr (!SA_ROWS)
+        if (p.a_scaling != 0) ea = e8m0_of(p.a_sinv[k * ((M + 127) / 128) + mb]);
+      if constexpr (!SB_COL)
+        if (p.b_scaling != 0) eb = e8m0_of(p.b_sinv[k * ((N + 127) / 128) + nb]);
+      su_tab[wave][k] = __uint_as_float((uint32_t)ea | ((uint32_t)eb << 8));
+    }
+  }
+  // stage 0 done (in the block modes up to 2 more DMA instructions per
+  // stage: the wait then covers part of stage 1 as well)
   if (nk > 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -147,6 +196,32 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) b[j] = frag(lds[0] + A_BYTES, br + 16 * j, g);
   a[0] = frag(lds[0], ar, g);
+  // block modes: the step's scales of A's row-tiles (lane l16: row
+  // 16 i + l16) and of B's column-tiles (column 16 j + l16), kept as read;
+  // their E8M0 codes are taken at the MFMA, long after the read returned
+  float ea[8], eb[8];
+  auto ea_of = [&](const uint8_t* S, int i) {
+    return reinterpret_cast<const float*>(S + SA_OFF)[wm * 128 + 16 * i + l16];
+  };
+  auto eb_of = [&](const uint8_t* S, int j) {
+    return reinterpret_cast<const float*>(S + SB_OFF)[wn * 128 + 16 * j + l16];
+  };
+  if constexpr (SA_ROWS) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ea[i] = ea_of(lds[0], i);
+  }
+  if constexpr (SB_COL) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) eb[j] = eb_of(lds[0], j);
+  }
+  // one MFMA: plain, or with the block codes of row-tile i and column-tile j
+  auto mm = [&](const v8i& bj, const v8i& ai, const v4f& c, int i, int j, uint32_t eu) -> v4f {
+    if constexpr (MX)
+      return mfma_mx<BF, AF>(bj, ai, c, SB_COL ? e8m0_of(eb[j]) : (int)((eu >> 8) & 0xFFu),
+                             SA_ROWS ? e8m0_of(ea[i]) : (int)(eu & 0xFFu));
+    else
+      return mfma<BF, AF>(bj, ai, c);
+  };
 
   // One K step on stage X, with B's fragments and row-tile 0's A fragment
   // in registers; Y is the next step's stage.  The scheduling barriers keep
@@ -154,6 +229,8 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
   auto step = [&](auto dmatag, auto nexttag, const uint8_t* X, const uint8_t* Y, int kb) {
     constexpr bool DMA = decltype(dmatag)::value;    // issue the DMA of step kb + 2
     constexpr bool NEXT = decltype(nexttag)::value;  // read step kb + 1's fragments
+    uint32_t eu = 0;
+    if constexpr (MX && !(SA_ROWS && SB_COL)) eu = __float_as_uint(su_tab[wave][kb]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -161,7 +238,7 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
       h[i] = frag(X, ar + 16 * (i + 4), g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = mfma<BF, AF>(b[j], a[i & 1], acc[i][j]);
+      for (int j = 0; j < 8; ++j) acc[i][j] = mm(b[j], a[i & 1], acc[i][j], i, j, eu);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (NEXT) {
@@ -171,17 +248,27 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       a[0] = frag(Y, ar, g);
+      if constexpr (SA_ROWS) {   // row-tiles 0..3 are done with theirs
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ea[i] = ea_of(Y, i);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
 #pragma unroll
-      for (int i = 4; i < 8; ++i) acc[i][j] = mfma<BF, AF>(b[j], h[i - 4], acc[i][j]);
+      for (int i = 4; i < 8; ++i) acc[i][j] = mm(b[j], h[i - 4], acc[i][j], i, j, eu);
       if constexpr (NEXT) b[j] = frag(Y + A_BYTES, br + 16 * j, g);
+      if constexpr (SB_COL && NEXT) eb[j] = eb_of(Y, j);
       if constexpr (DMA) {
         load(kb + 2, X, 2 * j);
         load(kb + 2, X, 2 * j + 1);
+        if (j == 7) load_scales(kb + 2, X);
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (SA_ROWS && NEXT) {
+#pragma unroll
+      for (int i = 4; i < 8; ++i) ea[i] = ea_of(Y, i);
     }
   };
 
@@ -200,10 +287,10 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
   // accumulator is a multiple of 2^-(qa + qb) (the two formats' smallest
   // subnormal steps), so if that minimum dequantises to a normal binary32,
   // no output can be subnormal.
-  // With per-row scales every output is checked.
+  // With per-row or block scales every output is checked.
   constexpr int QAB = (AF == 0 ? 9 : 16) + (BF == 0 ? 9 : 16);
   const float lo = (__builtin_ldexpf(1.0f, -QAB) * __builtin_fabsf(sa)) * __builtin_fabsf(sb);
-  const bool may_sub = ROWS || !(lo >= 1.17549435e-38f);   // NaN scales: check
+  const bool may_sub = MODE != W4_TENSOR || !(lo >= 1.17549435e-38f);   // NaN scales: check
   auto deq = [&](int i, int j, int q, float x) -> float {
     if constexpr (ROWS)
       return (x * rs_tab[wm * 128 + 16 * i + l16]) * rs_tab[BM + wn * 128 + 16 * j + 4 * g + q];
@@ -230,29 +317,41 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
   if (p.d_amax) workgroup_amax<4>(p.d_amax, amax_bits, lane, wave);
 }
 
-template <int AF, int BF, bool OUT8, bool ROWS>
+template <int AF, int BF, bool OUT8, int MODE>
 hipError_t launch_w4_k(const GemmParams& p, hipStream_t s) {
   const int tiles_m = (int)((p.M + BM - 1) / BM), tiles_n = (int)((p.N + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(W4_THREADS);
-  if (p.K % BK == 0)
-    hipLaunchKernelGGL((k_gemm_w4<AF, BF, false, OUT8, ROWS>), grid, block, 0, s, p, tiles_m, tiles_n);
+  if constexpr (MODE >= W4_MX)   // block scales: K is a multiple of the step
+    hipLaunchKernelGGL((k_gemm_w4<AF, BF, false, OUT8, MODE>), grid, block, 0, s, p, tiles_m, tiles_n);
+  else if (p.K % BK == 0)
+    hipLaunchKernelGGL((k_gemm_w4<AF, BF, false, OUT8, MODE>), grid, block, 0, s, p, tiles_m, tiles_n);
   else
-    hipLaunchKernelGGL((k_gemm_w4<AF, BF, true, OUT8, ROWS>), grid, block, 0, s, p, tiles_m, tiles_n);
+    hipLaunchKernelGGL((k_gemm_w4<AF, BF, true, OUT8, MODE>), grid, block, 0, s, p, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-template <int AF, int BF, bool OUT8>
+// MX = false: per-tensor or per-row scales; MX = true: power-of-two block
+// scales (codes 3 / 4) or per-tensor on each operand, at least one blocked.
+template <int AF, int BF, bool OUT8, bool MX>
 hipError_t launch_w4(const GemmParams& p, hipStream_t s) {
-  return p.a_scaling == 5 || p.b_scaling == 5 ? launch_w4_k<AF, BF, OUT8, true>(p, s)
-                                              : launch_w4_k<AF, BF, OUT8, false>(p, s);
+  if constexpr (MX) {
+    const bool ra = p.a_scaling == 3, cb = p.b_scaling == 3;   // 1x128 tiles
+    if (ra && cb) return launch_w4_k<AF, BF, OUT8, W4_MX + 3>(p, s);
+    if (ra) return launch_w4_k<AF, BF, OUT8, W4_MX + 1>(p, s);
+    if (cb) return launch_w4_k<AF, BF, OUT8, W4_MX + 2>(p, s);
+    return launch_w4_k<AF, BF, OUT8, W4_MX>(p, s);
+  } else {
+    return p.a_scaling == 5 || p.b_scaling == 5 ? launch_w4_k<AF, BF, OUT8, W4_ROWS>(p, s)
+                                                : launch_w4_k<AF, BF, OUT8, W4_TENSOR>(p, s);
+  }
 }
 
-template <bool OUT8>
+template <bool OUT8, bool MX>
 hipError_t launch_w4_out(const GemmParams& p, hipStream_t s) {
-  if (p.a_fmt == 0 && p.b_fmt == 0) return launch_w4<0, 0, OUT8>(p, s);
-  if (p.a_fmt == 1 && p.b_fmt == 0) return launch_w4<1, 0, OUT8>(p, s);
-  if (p.a_fmt == 0 && p.b_fmt == 1) return launch_w4<0, 1, OUT8>(p, s);
-  return launch_w4<1, 1, OUT8>(p, s);
+  if (p.a_fmt == 0 && p.b_fmt == 0) return launch_w4<0, 0, OUT8, MX>(p, s);
+  if (p.a_fmt == 1 && p.b_fmt == 0) return launch_w4<1, 0, OUT8, MX>(p, s);
+  if (p.a_fmt == 0 && p.b_fmt == 1) return launch_w4<0, 1, OUT8, MX>(p, s);
+  return launch_w4<1, 1, OUT8, MX>(p, s);
 }
 
 }  // namespace

@@ -88,5 +88,10 @@ hipError_t launch_gemm_big_fp8out(const GemmParams& p, hipStream_t s);   // p.d_
 // (gemm_w4.hip, gemm_w4_fp8out.hip), under the same size limits.
 hipError_t launch_gemm_w4(const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_w4_fp8out(const GemmParams& p, hipStream_t s);   // p.d_fp8 != 0
+// Power-of-two block scales (codes 3 / 4, the other operand possibly per
+// tensor): the same kernel with the scales in the matrix instruction
+// (gemm_w4_mx.hip, gemm_w4_mx_fp8out.hip).
+hipError_t launch_gemm_w4_mx(const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm_w4_mx_fp8out(const GemmParams& p, hipStream_t s);   // p.d_fp8 != 0
 
 }  // namespace fp8lin
