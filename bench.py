@@ -70,8 +70,8 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 C5_ORDER = ["qkv", "o", "gate", "up", "down"]
 C5_X = {"qkv": "qkv", "o": "o", "gate": "gate", "up": "gate", "down": "down"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemm_c5_traffic.json")
-TRAFFIC_SOURCES = ("csrc/gemm_big_kernel.h", "csrc/gemm_big.hip", "csrc/gemm_w4.hip",
-                   "csrc/fp8_device.h")
+TRAFFIC_SOURCES = ("csrc/gemm_big_kernel.h", "csrc/gemm_big.hip", "csrc/gemm_w4_kernel.h",
+                   "csrc/gemm_w4.hip", "csrc/fp8_device.h")
 
 
 def parse():
@@ -307,9 +307,9 @@ def c5_plan(T=8192):
 # GEMM kernel (instantiation) of each pass: the dominant-kernel roofline is
 # taken over the launches of one kernel
 C5_KERNEL = {
-    "delayed fwd": "k_gemm_w4<0, 0, false, false>",
-    "delayed dgrad": "k_gemm_w4<1, 0, false, false>",
-    "delayed wgrad": "k_gemm_w4<0, 1, false, false>",
+    "delayed fwd": "k_gemm_w4<0, 0, false, false, 0>",
+    "delayed dgrad": "k_gemm_w4<1, 0, false, false, 0>",
+    "delayed wgrad": "k_gemm_w4<0, 1, false, false, 0>",
     "block fwd": "k_gemm_big<0, 0, true, true, false, false, false>",
     "block dgrad": "k_gemm_big<1, 0, true, true, false, false, false>",
     "block wgrad": "k_gemm_big<0, 1, true, true, true, false, false>",
