@@ -32,7 +32,8 @@
 //   ((r >> 1) & 7) ^ ((r & 1) << 2) the 16-row ds_read_b128 pattern ran
 //   about 1.6x faster than with chunk pairs {2g, 2g+1} (measured on gfx950).
 //   Buffer loads past the end of an operand return zeros, which covers the
-//   M / N / K tails without branches.
+//   M / N tails without branches (block scales make K a multiple of the
+//   step).
 //   The prefetch is issued from inline assembly: the compiler then neither
 //   waits for it before reading the other stage nor keeps it ordered with
 //   anything else; each step ends with an explicit vmcnt(0) and a barrier.

@@ -1,14 +1,17 @@
-// gemm_w4_kernel.h -- the per-tensor-scaled FP8 GEMM on four wavefronts of
-// 128 x 128 (accumulators in the matrix unit's AGPRs); instantiated by
-// gemm_w4.hip (BF16 / FP32 output) and gemm_w4_fp8out.hip (FP8 output).
+// gemm_w4_kernel.h -- the FP8 GEMM on four wavefronts of 128 x 128
+// (accumulators in the matrix unit's AGPRs) for per-tensor, per-row and
+// power-of-two block scales; instantiated by gemm_w4.hip / gemm_w4_fp8out.hip
+// (per-tensor and per-row; BF16 / FP32 and FP8 output) and gemm_w4_mx.hip /
+// gemm_w4_mx_fp8out.hip (power-of-two block scales).
 //
 // Same contract as k_gemm_big (gemm_big_kernel.h, whose helpers and
 // epilogue it shares): D = A . B^T, K-contiguous FP8 operands, FP32
-// accumulation, the two per-tensor scales applied once in the epilogue
+// accumulation, per-tensor and per-row scales applied once in the epilogue
 // ([MPG] "Mixed Precision LLM Training: The Complete Guide", "Transformer
-// Engine internals > Delayed scaling"), the same 256 x 256 output tile, the
-// same two 64 KB LDS stages filled by buffer_load ... lds, the same swizzle
-// and workgroup order.
+// Engine internals > Delayed scaling"), power-of-two block scales inside
+// the matrix instruction; the same 256 x 256 output tile, the same two LDS
+// stages filled by buffer_load ... lds, the same swizzle and workgroup
+// order.
 //
 // What differs is the wavefront layout and the step's schedule.  One
 // wavefront per SIMD with a 128 x 128 tile reads every fragment once per
