@@ -29,7 +29,7 @@ def bits(a):
 
 
 SHAPES = [(256, 512, 384), (512, 256, 256), (200, 136, 384), (129, 257, 256), (1, 1, 128)]
-MODES = [(0, 0), (1, 2), (3, 4), (1, 1)]
+MODES = [(0, 0), (1, 2), (3, 4), (1, 1), (5, 5), (5, 0)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -44,7 +44,7 @@ def test_gemm_fp8_output(O, L, shape, mode, out_fmt, with_t):
     A = rand_codes(rng, (M, K), 0)
     B = rand_codes(rng, (N, K), 1)
     ora = {3: 1, 4: 2}
-    if asc >= 3:
+    if asc in (3, 4):
         sa, sb = pow2_scales(rng, ora[asc], M, K), pow2_scales(rng, ora[bsc], N, K)
     else:
         sa, sb = rand_scales(rng, asc, M, K), rand_scales(rng, bsc, N, K)
