@@ -455,21 +455,25 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
   // instruction; lane p lands in row 8*it + (p >> 3), stored chunk p & 7
   const int lrow = 32 * wave + (lane >> 3);
 
-  auto load_stage = [&](int kb, uint8_t* base) {
-    const int k0 = kb * BK;
+  // DMA instruction q of a stage (0..3: A rows lrow + 8 q, 4..7: B rows
+  // lrow + 8 (q - 4)).  Block scales make K a multiple of the step: every
+  // chunk of a step is inside K, and the step's K offset goes in the scalar
+  // offset (no per-step VALU work beside the promotion; measured 1-2% on
+  // the transformer-block shapes).  Rows past the operand's end fail the
+  // buffer range check on the lane offset and read zeros.
+  auto load_part = [&](int kb, uint8_t* base, int q) {
     const uint32_t lb = lds_addr(base);
-    // Block scales make K a multiple of the step: every chunk of a step is
-    // inside K, and the step's K offset goes in the scalar offset (no
-    // per-step VALU work beside the promotion; measured 1-2% on the
-    // transformer-block shapes).  Rows past the operand's end fail the
-    // buffer range check on the lane offset and read zeros.
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int row = lrow + 8 * it;
-      const int kc = 16 * ((lane & 7) ^ swz(row));
-      dma16s(lb + (32 * wave + 8 * it) * BK, (uint32_t)(row * lda + kc), ra, (uint32_t)k0);
-      dma16s(lb + A_BYTES + (32 * wave + 8 * it) * BK, (uint32_t)(row * ldb + kc), rb, (uint32_t)k0);
-    }
+    const int it = q & 3;
+    const int row = lrow + 8 * it;
+    const int kc = 16 * ((lane & 7) ^ swz(row));
+    if (q < 4)
+      dma16s(lb + (32 * wave + 8 * it) * BK, (uint32_t)(row * lda + kc), ra, (uint32_t)(kb * BK));
+    else
+      dma16s(lb + A_BYTES + (32 * wave + 8 * it) * BK, (uint32_t)(row * ldb + kc), rb,
+             (uint32_t)(kb * BK));
+  };
+  auto load_scales = [&](int kb, uint8_t* base) {
+    const uint32_t lb = lds_addr(base);
     if constexpr (SA_ROWS) {
       if (wave == 0) {   // 256 row scales of this K block
         const i32x4 rs = make_rsrc(p.a_sinv + (int64_t)kb * M + m0, (uint32_t)(rows_a * 4));
@@ -484,6 +488,11 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
         for (int q = 0; q < 4; ++q) dma4(lb + SB_OFF + q * 256, (uint32_t)(q * 256 + lane * 4), rs);
       }
     }
+  };
+  auto load_stage = [&](int kb, uint8_t* base) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) load_part(kb, base, q);
+    load_scales(kb, base);
   };
 
   v4f acc[TI][TJ];
@@ -538,11 +547,13 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
     v8i bfr[TJ];
 #pragma unroll
     for (int j = 0; j < TJ; ++j) bfr[j] = frag(Bs, wn * WTN + 16 * j + l16, g);
-    // the next stage's DMA: into the stage the previous step read (the
-    // end-of-step barrier freed it); issued earlier, right after that
-    // barrier, its longer-lived addresses push the promotion kernels past
-    // 256 registers (measured: spills)
-    if (kb > 0 && kb + 1 < nk) load_stage(kb + 1, lds[stage ^ 1]);
+    // the next stage's DMA goes into the stage the previous step read (the
+    // end-of-step barrier freed it): the scales now, the operands spread
+    // over the first row-tiles below.  Issued right after that barrier,
+    // its longer-lived addresses push the promotion kernels past 256
+    // registers (measured: spills).
+    const bool dma = kb > 0 && kb + 1 < nk;
+    if (dma) load_scales(kb + 1, lds[stage ^ 1]);
 
     // The MFMA takes B as its first operand, so each 16x16 result tile is
     // the transpose of the D tile: lane (g, l16) holds D row 16*i + l16,
@@ -586,6 +597,15 @@ __global__ void __launch_bounds__(THREADS) k_gemm_big(GemmParams p, int tiles_m,
         if constexpr (SA_ROWS) {
           srow = reinterpret_cast<const float*>(As + SA_OFF)[wm * WTM + 16 * i + l16];
           if constexpr (!SB_COL) srow *= suni;
+        }
+        // the next stage's operand DMA, PER instructions with each of the
+        // first 8 / PER row-tiles (3-4% faster than all eight at the step's
+        // start for FWD / DGRAD, 2% for WGRAD; two per row-tile push the
+        // column-scaled kernels past 256 registers)
+        constexpr int PER = SB_COL ? 4 : 2;
+        if (dma && i < 8 / PER) {
+#pragma unroll
+          for (int u = 0; u < PER; ++u) load_part(kb + 1, lds[stage ^ 1], PER * i + u);
         }
         v4f pcur[TJ];
 #pragma unroll
