@@ -7,8 +7,9 @@
 //
 // Same contract as k_gemm in gemm_kernels.hip (see there and the C ABI):
 // D = A . B^T, K-contiguous FP8 operands, FP32 accumulation; block scales
-// promoted per 128-wide K block (or, power-of-two, applied inside the
-// matrix instruction), a per-tensor operand's scale folded in.
+// with binary32 values promoted per 128-wide K block (power-of-two ones are
+// applied inside the matrix instruction by k_gemm_w4), a per-tensor
+// operand's scale folded in.
 // [MPG] = "Mixed Precision LLM Training: The Complete Guide",
 //   "Skipping the BAcc accumulator promotion", "DeepSeek FP8 training recipe
 //   in detail > Block-wise scaling at 128 granularity" and "> Mixed-precision
@@ -36,7 +37,8 @@
 //   step).
 //   The prefetch is issued from inline assembly: the compiler then neither
 //   waits for it before reading the other stage nor keeps it ordered with
-//   anything else; each step ends with an explicit vmcnt(0) and a barrier.
+//   anything else; it is spread over the step's first row-tiles, and each
+//   step ends with an explicit vmcnt(0) and a barrier.
 //   Inside the loop there is no other vector-memory access: per-K-block
 //   scales come from LDS (1x128 rows arrive with the operands; per-tensor and
 //   128x128 scales sit in a per-wavefront table filled before the loop).
