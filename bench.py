@@ -71,7 +71,7 @@ C5_ORDER = ["qkv", "o", "gate", "up", "down"]
 C5_X = {"qkv": "qkv", "o": "o", "gate": "gate", "up": "gate", "down": "down"}
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "gemm_c5_traffic.json")
 TRAFFIC_SOURCES = ("csrc/gemm_big_kernel.h", "csrc/gemm_big.hip", "csrc/gemm_w4_kernel.h",
-                   "csrc/gemm_w4.hip", "csrc/fp8_device.h")
+                   "csrc/gemm_w4.hip", "csrc/fp8_device.h", "build.py")
 
 
 def parse():

@@ -36,6 +36,13 @@ def device_flags():
             "-Wall", "-Wno-unused-function", "-Wno-inline-asm", "-I", os.path.join(ROOT, "include")]
 
 
+# Per-file code-generation options.  The FP32-promoted block GEMMs
+# (gemm_big.hip) schedule with the compiler's max-ILP strategy: block WGRAD
+# 2% faster at 8192x28672x8192, FWD / DGRAD unchanged, results identical,
+# same registers and no scratch.
+EXTRA_FLAGS = {"gemm_big.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -48,7 +55,7 @@ def build(verbose: bool = False, jobs: int = None) -> str:
 
     def one(src):
         obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-        cmd = [cc, *device_flags(), "-c", src, "-o", obj]
+        cmd = [cc, *device_flags(), *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
