@@ -238,6 +238,8 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
     uint32_t eu = 0;
     if constexpr (MX && !(SA_ROWS && SB_COL)) eu = __float_as_uint(su_tab[wave][kb]);
     __builtin_amdgcn_sched_barrier(0);
+    // row-tiles 0..3, row by row: the next row-tile's A fragment is read
+    // after this row's first MFMA, row-tile i + 4's after its fifth
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -262,6 +264,9 @@ k_gemm_w4(GemmParams p, int tiles_m, int tiles_n) {
         for (int i = 0; i < 4; ++i) ea[i] = ea_of(Y, i);
       }
     }
+    // row-tiles 4..7, column by column: two DMA instructions of step kb + 2
+    // after the column's first and third MFMA, then B column-tile j, free
+    // after its fourth, refilled from the next stage
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
 #pragma unroll
